@@ -1,0 +1,300 @@
+"""float64 CPU oracle for one BasisKV decode step -- TEST INFRASTRUCTURE ONLY.
+
+Source: "BasisKV: Value Latents for Communication and Key Routing"
+(arXiv 2611.02583).  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module; the product path never does.
+
+What is cached per token and per physical KV head (appendix Table 4):
+  z  Value latent, width rV   (the full Value is not cached)
+  r  Key residual code, width rq
+  k  exact Key, width dh
+Routing reads rb <= rV leading latent dims plus the rq residual dims of every
+context token; selected attention reads all rV latent dims and the dh Key dims
+of the selected tokens only (Table 4's two read columns).
+
+Array conventions (all "logical", i.e. contiguous per sequence, no pages):
+  q   [B, Hq, dh]            queries of the step
+  z   [B, Hkv, T, rV]        latent cache
+  r   [B, Hkv, T, rq]        residual cache
+  kc  [B, Hkv, T, dh]        exact-Key cache
+  A   [Hkv, dh, rV]          Value encoder  (z = v A)
+  Bf  [Hkv, rV, dh]          Value decoder  (v_hat = z Bf)
+  P   [Hkv, rb, dh]          latent -> Key predictor
+  Q   [Hkv, rq, dh]          residual -> Key decoder
+  E   [Hkv, dh, rq]          residual encoder
+  W_O [Hq*dh, D]             output projection, y = concat_h(v_h) W_O
+Query head h belongs to KV head h // G with G = Hq / Hkv.
+
+Every value is float64.  Stored inputs are decoded exactly
+(storage_to_f64); the only roundings are the ones the method itself performs
+when it writes the cache (compress) and, optionally, the final output store.
+
+Readings of points the pages leave open (each used below):
+  R1 token -> page score: the maximum predicted logit over the page's valid
+     tokens;  R2 the KV head's page score is also the maximum over its G query
+     heads;  R3 query head h uses KV head h // G;  R4 routing logits are
+     unscaled (top-k is invariant to a positive scale);  R5 attention scale is
+     1/sqrt(dh) unless the caller passes another;  R6 the routing base is the
+     leading rb latent dims;  R7 residual code r = (k - z_s[:rb] P) E with the
+     stored (rounded) latent z_s;  R8 the softmax is normalised over the valid
+     tokens of the selected pages only;  R9 ties in page score go to the lower
+     page index, the selection is reported in ascending page order and padded
+     with -1 when k exceeds the number of pages;  R10 a sequence with no valid
+     token yields u = 0 and y = 0.
+"""
+
+import math
+
+import numpy as np
+
+_STORAGES = ("f32", "bf16", "f64")
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+def storage_to_f64(a, storage):
+    """Decode stored values to float64, exactly.
+
+    ``storage`` is "f32" (float32 array), "bf16" (uint16 bit patterns: the
+    upper half of an IEEE float32) or "f64" (no storage rounding; used by the
+    exactness pins).
+    """
+    if storage == "f64":
+        return np.asarray(a, dtype=np.float64)
+    if storage == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if storage == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown storage {storage!r}")
+
+
+def round_to_storage(x, storage):
+    """Round float64 values to the storage format, round-to-nearest-even.
+
+    Returns the rounded values as float64.  For bf16 (8 significant bits) the
+    quantum of a value with frexp exponent e is 2**(e-8); dividing by it is
+    exact, numpy's round() is round-half-even, and the smallest normal's
+    quantum (2**-133) is kept below it (subnormals).  Values past the bf16
+    range become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if storage == "f64":
+        return x.copy()
+    if storage == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if storage != "bf16":
+        raise ValueError(f"unknown storage {storage!r}")
+    out = np.zeros_like(x)
+    nz = x != 0
+    xs = x[nz]
+    _, e = np.frexp(xs)
+    e = np.maximum(e, -125)
+    quantum = np.ldexp(1.0, e - 8)
+    rounded = np.round(xs / quantum) * quantum
+    bf16_max = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    rounded = np.where(np.abs(rounded) > bf16_max, np.copysign(np.inf, rounded), rounded)
+    out[nz] = rounded
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (a0) compression of new tokens into the cache
+# ---------------------------------------------------------------------------
+
+def compress_tokens(k_new, v_new, A, P, E, rb, storage):
+    """Compress tokens' Keys and Values into the three cached states.
+
+    BasisKV abstract: Values are stored only as a low-rank latent, and a
+    Key-specific residual keeps the part of the Key that the latent cannot
+    predict; appendix Table 4 lists the three per-token states (latent rV,
+    residual rq, exact Key dh).
+
+    k_new, v_new: [n, Hkv, dh] float64.  Returns (z_s, r_s, k_s), each
+    [n, Hkv, width], already rounded to ``storage`` (z_s: rV, r_s: rq,
+    k_s: dh).  Steps: z = v A_g; z_s = round(z); r = (k - z_s[:, :rb] P_g) E_g
+    (reading R7); r_s = round(r); the exact Key is stored as given.
+    """
+    n, hkv, dh = k_new.shape
+    z_s = np.empty((n, hkv, A.shape[2]))
+    r_s = np.empty((n, hkv, E.shape[2]))
+    for g in range(hkv):
+        z = v_new[:, g, :] @ A[g]
+        z_s[:, g, :] = round_to_storage(z, storage)
+        residual_key = k_new[:, g, :] - z_s[:, g, :rb] @ P[g]
+        r_s[:, g, :] = round_to_storage(residual_key @ E[g], storage)
+    k_s = round_to_storage(k_new, storage)
+    return z_s, r_s, k_s
+
+
+# ---------------------------------------------------------------------------
+# (a1, a2) routing: predicted keys and page scores
+# ---------------------------------------------------------------------------
+
+def predicted_keys(z, r, P_g, Q_g, rb):
+    """Predicted Keys of a token range for one KV head.
+
+    BasisKV abstract and Figure 1 caption: the cached Value latent predicts
+    part of the Key used for routing and the Key residual supplies the rest.
+    k_hat_t = z_t[:rb] P_g + r_t Q_g, as an explicit dh-vector (reading R6).
+    z: [T, rV], r: [T, rq]  ->  [T, dh].
+    """
+    return z[:, :rb] @ P_g + r @ Q_g
+
+
+def route_page_scores(q_group, z, r, P_g, Q_g, rb, seq_len, page_size, n_pages_out):
+    """Page scores of one (sequence, KV head).
+
+    BasisKV abstract: the predicted Key information decides which Key pages
+    are read; Table 9's caption fixes the routing unit as a page of tokens.
+    For every valid token t and query head h of the group, the routing logit
+    is q_h . k_hat_t (unscaled, R4); a page's score is the maximum over its
+    valid tokens and the group's heads (R1, R2).  Pages at or beyond
+    ceil(seq_len / page_size) get -inf.  Returns [n_pages_out] float64.
+    """
+    scores = np.full(n_pages_out, -np.inf)
+    if seq_len <= 0:
+        return scores
+    khat = predicted_keys(z[:seq_len], r[:seq_len], P_g, Q_g, rb)
+    logits = q_group @ khat.T  # [G, seq_len]
+    n_pages = -(-seq_len // page_size)
+    for p in range(min(n_pages, n_pages_out)):
+        lo, hi = p * page_size, min((p + 1) * page_size, seq_len)
+        scores[p] = logits[:, lo:hi].max()
+    return scores
+
+
+# ---------------------------------------------------------------------------
+# (a3) page selection
+# ---------------------------------------------------------------------------
+
+def select_pages(scores, n_pages, k):
+    """The k highest-scoring pages among the first n_pages, ascending.
+
+    BasisKV abstract: only the selected pages' original Keys are fetched.
+    Ties go to the lower page index and the result is padded with -1 when
+    k > n_pages (reading R9).  Pure-Python ordering by (-score, index).
+    """
+    n_pages = max(0, int(n_pages))
+    order = sorted(range(n_pages), key=lambda p: (-float(scores[p]), p))
+    chosen = sorted(order[:k])
+    return np.array(chosen + [-1] * (k - len(chosen)), dtype=np.int64)
+
+
+def selected_tokens(sel, seq_len, page_size):
+    """Token positions covered by the selected pages (valid ones only)."""
+    toks = []
+    for p in sel:
+        if p < 0:
+            continue
+        lo = p * page_size
+        toks.extend(range(lo, min(lo + page_size, seq_len)))
+    return np.array(toks, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# (a4) exact attention over the selected pages, summed in latent space
+# ---------------------------------------------------------------------------
+
+def attend_group(q_group, kc, z, sel, seq_len, page_size, scale):
+    """Latent attention output of one KV head's query group.
+
+    BasisKV abstract: exact QK scores are computed from the original Keys of
+    the selected pages; Figure 1 caption: the attention output is formed as a
+    Value latent (the weighted sum runs over the cached latents, all rV
+    dims, appendix Table 4 "selected attention").  For each head h:
+    s_t = scale * q_h . k_t over the valid tokens of the selected pages,
+    p = softmax(s) over those tokens only (R8), u_h = sum_t p_t z_t.
+    q_group [G, dh], kc [T, dh], z [T, rV]  ->  [G, rV].
+    """
+    toks = selected_tokens(sel, seq_len, page_size)
+    if toks.size == 0:
+        return np.zeros((q_group.shape[0], z.shape[1]))
+    s = scale * (q_group @ kc[toks].T)  # [G, n]
+    s = s - s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    w = w / w.sum(axis=1, keepdims=True)
+    return w @ z[toks]
+
+
+# ---------------------------------------------------------------------------
+# (a5) reconstruction through the Value decoder and the output projection
+# ---------------------------------------------------------------------------
+
+def reconstruct(u, Bf, W_O, group):
+    """Output of one sequence from the per-head latents.
+
+    BasisKV abstract: Value compression is tied to the output projection;
+    Figure 1 caption: the full output is rebuilt from the latents after they
+    are exchanged.  Definition (unfused): v_h = u_h Bf_{h // G}, then
+    y = concat_h(v_h) W_O.  u [Hq, rV], Bf [Hkv, rV, dh], W_O [Hq*dh, D].
+    """
+    hq = u.shape[0]
+    v = np.stack([u[h] @ Bf[h // group] for h in range(hq)])  # [Hq, dh]
+    return v.reshape(-1) @ W_O
+
+
+# ---------------------------------------------------------------------------
+# one decode step
+# ---------------------------------------------------------------------------
+
+def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
+                top_k, n_pages_out, storage, scale=None, k_new=None, v_new=None,
+                store_output=True):
+    """One decode step of one layer for a batch.
+
+    Inputs are float64 (decode stored values with storage_to_f64 first);
+    ``storage`` names the format the cache is written in ("f32", "bf16",
+    "f64").  If k_new / v_new ([B, Hkv, dh]) are given, the step first
+    compresses that token into position seq_lens[b] - 1 of each sequence
+    (a0); then it routes (a1, a2), selects (a3), attends (a4) and
+    reconstructs (a5).  Arrays z, r, kc are copied, not modified.
+
+    Returns a dict: scores [B, Hkv, n_pages_out], sel [B, Hkv, top_k],
+    u [B, Hq, rV], y [B, D] (float64, unrounded), y_stored (y rounded to
+    ``storage`` when store_output), and z, r, kc (the caches after the
+    append).
+    """
+    bsz, hq, dh = q.shape
+    hkv = z.shape[1]
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    z = np.array(z, dtype=np.float64, copy=True)
+    r = np.array(r, dtype=np.float64, copy=True)
+    kc = np.array(kc, dtype=np.float64, copy=True)
+    if k_new is not None:
+        for b in range(bsz):
+            pos = int(seq_lens[b]) - 1
+            if pos < 0 or pos >= z.shape[2]:
+                continue
+            zs, rs, ks = compress_tokens(k_new[b:b + 1], v_new[b:b + 1], A, P, E, rb, storage)
+            z[b, :, pos, :] = zs[0]
+            r[b, :, pos, :] = rs[0]
+            kc[b, :, pos, :] = ks[0]
+
+    rv = z.shape[3]
+    scores = np.full((bsz, hkv, n_pages_out), -np.inf)
+    sel = np.full((bsz, hkv, top_k), -1, dtype=np.int64)
+    u = np.zeros((bsz, hq, rv))
+    y = np.zeros((bsz, W_O.shape[1]))
+    for b in range(bsz):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        n_pages = -(-L // page_size)
+        for g in range(hkv):
+            qg = q[b, g * group:(g + 1) * group]
+            scores[b, g] = route_page_scores(qg, z[b, g], r[b, g], P[g], Q[g], rb, L,
+                                             page_size, n_pages_out)
+            sel[b, g] = select_pages(scores[b, g], n_pages, top_k)
+            u[b, g * group:(g + 1) * group] = attend_group(qg, kc[b, g], z[b, g], sel[b, g],
+                                                           L, page_size, scale)
+        y[b] = reconstruct(u[b], Bf, W_O, group)
+    out = dict(scores=scores, sel=sel, u=u, y=y, z=z, r=r, kc=kc)
+    if store_output:
+        out["y_stored"] = round_to_storage(y, storage)
+    return out

@@ -1,0 +1,82 @@
+"""The five synthetic workloads the decode path is tested and measured on.
+
+Shapes follow the models the BasisKV pages evaluate (Llama-3.1-8B:
+32 query / 8 KV heads, head dim 128, hidden 4096; Qwen3-32B: 64 / 8, hidden
+5120; page sizes of Table 10; latent widths V64 / V96 of Figure 3).  Values
+are seeded and synthetic; no model weights or datasets are involved.
+"""
+
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    storage: str            # "f32" or "bf16": q, caches, factors, output
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    hidden: int
+    ctx: int                # tokens per sequence at the (last) decode step
+    page_size: int
+    r_v: int                # Value-latent width
+    r_b: int                # routing base width (leading latent dims)
+    r_q: int                # Key-residual rank
+    top_k: int              # pages kept per KV head
+    n_planted: int = 0      # planted pages per sequence
+    planted: str = "none"   # "even", "random" or "none"
+    latent_norm_sigma: float = 0.0  # >0: per-token latent norms ~ LogNormal(0, sigma)
+    noise: float = 0.05
+    seed: int = 1000
+    # prefill + decode workload only
+    prefill_batch: int = 0
+    prefill_tokens: int = 0
+    decode_steps: int = 0
+
+    @property
+    def group(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def max_pages(self):
+        return -(-self.ctx // self.page_size)
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+WORKLOADS = (
+    # 0: tiny fp32 single decode step
+    Workload("tiny-fp32", "f32", batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, hidden=1024,
+             ctx=2048, page_size=16, r_v=64, r_b=64, r_q=32, top_k=16,
+             n_planted=4, planted="even", seed=1000),
+    # 1: Llama-3.1-8B-shaped layer, 4K context, top-k = 1/8 of the pages
+    Workload("llama8b-ctx4k", "bf16", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128,
+             hidden=4096, ctx=4096, page_size=32, r_v=96, r_b=96, r_q=48, top_k=16,
+             n_planted=8, planted="even", seed=1001),
+    # 2: Llama-3.1-8B-shaped layer, 32K context (the headline decode step)
+    Workload("llama8b-ctx32k", "bf16", batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
+             hidden=4096, ctx=32768, page_size=32, r_v=64, r_b=64, r_q=32, top_k=128,
+             n_planted=8, planted="random", latent_norm_sigma=0.5, seed=1002),
+    # 3: Qwen3-32B-shaped layer, 32K context, top-k = 1/16 of the pages
+    Workload("qwen32b-ctx32k", "bf16", batch=4, n_q_heads=64, n_kv_heads=8, head_dim=128,
+             hidden=5120, ctx=32768, page_size=32, r_v=96, r_b=96, r_q=48, top_k=64,
+             n_planted=8, planted="random", latent_norm_sigma=0.5, seed=1003),
+    # 4: Llama-3.1-8B-shaped prefill (4 x 4096 tokens) then 128 decode steps of
+    #    batch 2 ending at 131072 tokens, top-k = 1/32 of the pages
+    Workload("llama8b-prefill-decode-128k", "bf16", batch=2, n_q_heads=32, n_kv_heads=8,
+             head_dim=128, hidden=4096, ctx=131072, page_size=32, r_v=64, r_b=64, r_q=32,
+             top_k=128, seed=1004, prefill_batch=4, prefill_tokens=4096, decode_steps=128),
+)
+
+HEADLINE = 2
+
+
+def workload(index_or_name):
+    if isinstance(index_or_name, int):
+        return WORKLOADS[index_or_name]
+    for w in WORKLOADS:
+        if w.name == index_or_name:
+            return w
+    raise KeyError(index_or_name)

@@ -1,0 +1,380 @@
+"""Pins of the float64 oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to brute force, a closed form, an
+invariant or a library routine, so that a plausible slip (dropped term,
+transposed factor, wrong head / page index, wrong softmax set, wrong tie
+rule) fails at least one of them.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import basiskv_ref as ref
+from oracle import brute
+from sparse_decode_attention_latent_amd import synth
+from sparse_decode_attention_latent_amd.configs import workload, Workload
+
+
+def tiny_workload(**kw):
+    base = dict(name="tiny-brute", storage="f64", batch=2, n_q_heads=4, n_kv_heads=2, head_dim=8,
+                hidden=6, ctx=11, page_size=2, r_v=4, r_b=3, r_q=2, top_k=3, n_planted=0,
+                planted="none", seed=77)
+    base.update(kw)
+    return Workload(**base)
+
+
+def as64(inp, key):
+    return ref.storage_to_f64(inp[key], inp["storage"])
+
+
+def unpack(inp):
+    names = ("q", "z", "r", "kc", "k_new", "v_new", "A", "Bf", "P", "Q", "E", "W_O")
+    return {n: as64(inp, n) for n in names}
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_and_closed_forms():
+    rng = np.random.default_rng(1)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    x32[:4] = [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130]
+    mine = ref.round_to_storage(x32.astype(np.float64), "bf16")
+    lib = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, lib)
+    # halfway cases go to the even neighbour
+    assert mine[0] == 1.0 and mine[1] == 1 + 2 ** -6 and mine[2] == -1.0
+
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits.astype(np.uint32) >> 7) & 0xFF) != 0xFF
+    bits = bits[finite]
+    mine = ref.storage_to_f64(bits, "bf16")
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, lib)
+
+
+# ---------------------------------------------------------------------------
+# compression
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage", ["f64", "bf16"])
+def test_compress_matches_brute(storage):
+    wl = tiny_workload(storage=storage)
+    fac = synth.factors(wl)
+    A, P, E = (ref.storage_to_f64(fac[k], storage) for k in ("A", "P", "E"))
+    rng = np.random.default_rng(5)
+    k_new = ref.round_to_storage(rng.standard_normal((3, wl.n_kv_heads, wl.head_dim)), storage)
+    v_new = ref.round_to_storage(rng.standard_normal((3, wl.n_kv_heads, wl.head_dim)), storage)
+    z_s, r_s, k_s = ref.compress_tokens(k_new, v_new, A, P, E, wl.r_b, storage)
+    np.testing.assert_array_equal(k_s, k_new)
+
+    def rnd(x):
+        return float(ref.round_to_storage(np.array([x]), storage)[0])
+
+    for n in range(3):
+        for g in range(wl.n_kv_heads):
+            zb, rb_ = brute.compress_token(k_new[n, g], v_new[n, g], A[g].tolist(), P[g].tolist(),
+                                           E[g].tolist(), wl.r_b, rnd)
+            if storage == "f64":
+                np.testing.assert_allclose(z_s[n, g], zb, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(r_s[n, g], rb_, rtol=0, atol=1e-12)
+            else:
+                # both orders agree to ~1e-16 before the bf16 store, so the stored
+                # values are identical unless a value sits on a rounding tie
+                # (none does for these seeded inputs)
+                np.testing.assert_array_equal(z_s[n, g], zb)
+                np.testing.assert_array_equal(r_s[n, g], rb_)
+
+
+def test_compress_recovers_exact_codes():
+    """With noise-free K, V and A = pinv(B), E = pinv(Q), the encoders give back
+    the generating codes exactly (the latent/residual split of the abstract)."""
+    wl = workload(0).with_(storage="f64", ctx=64, n_planted=0, planted="none")
+    fac = synth.factors(wl)
+    A, P, Q, E, Bf = (ref.storage_to_f64(fac[k], "f64") for k in ("A", "P", "Q", "E", "Bf"))
+    rng = np.random.default_rng(3)
+    n = 40
+    z = rng.standard_normal((n, wl.n_kv_heads, wl.r_v))
+    r = rng.standard_normal((n, wl.n_kv_heads, wl.r_q))
+    k = np.einsum("ngi,gid->ngd", z[:, :, :wl.r_b], P) + np.einsum("ngj,gjd->ngd", r, Q)
+    v = np.einsum("ngi,gid->ngd", z, Bf)
+    z_s, r_s, _ = ref.compress_tokens(k, v, A, P, E, wl.r_b, "f64")
+    np.testing.assert_allclose(z_s, z, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(r_s, r, rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seq_len", [11, 10, 1])
+def test_route_matches_projected_query_brute(seq_len):
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    G = wl.group
+    n_out = wl.max_pages + 1
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            qg = d["q"][b, g * G:(g + 1) * G]
+            mine = ref.route_page_scores(qg, d["z"][b, g], d["r"][b, g], d["P"][g], d["Q"][g],
+                                         wl.r_b, seq_len, wl.page_size, n_out)
+            other = brute.route_page_scores(qg.tolist(), d["z"][b, g].tolist(), d["r"][b, g].tolist(),
+                                            d["P"][g].tolist(), d["Q"][g].tolist(), wl.r_b, seq_len,
+                                            wl.page_size, n_out)
+            np.testing.assert_allclose(mine, other, rtol=1e-12, atol=1e-12)
+            n_pages = -(-seq_len // wl.page_size)
+            assert np.all(np.isneginf(mine[n_pages:])) and np.all(np.isfinite(mine[:n_pages]))
+
+
+def test_route_equals_exact_logits_when_keys_are_exact():
+    """Noise-free keys are exactly z[:rb] P + r Q, so the predicted-key logit
+    equals the true q.k logit; the page score is then the page's largest
+    exact logit over the group (closed form)."""
+    wl = workload(0).with_(storage="f64", ctx=300, batch=1)
+    inp = synth.decode_inputs(wl, exact=True)
+    d = unpack(inp)
+    G, S = wl.group, wl.page_size
+    L = 300
+    for g in range(wl.n_kv_heads):
+        qg = d["q"][0, g * G:(g + 1) * G]
+        mine = ref.route_page_scores(qg, d["z"][0, g], d["r"][0, g], d["P"][g], d["Q"][g], wl.r_b,
+                                     L, S, wl.max_pages)
+        exact = torch.from_numpy(qg) @ torch.from_numpy(d["kc"][0, g, :L]).T
+        n_pages = -(-L // S)
+        want = [exact[:, p * S:min((p + 1) * S, L)].max().item() for p in range(n_pages)]
+        np.testing.assert_allclose(mine[:n_pages], want, rtol=1e-10, atol=1e-9)
+
+
+def test_route_uses_only_leading_rb_latent_dims():
+    wl = tiny_workload(r_v=6, r_b=2)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    qg = d["q"][0, :wl.group]
+    base = ref.route_page_scores(qg, d["z"][0, 0], d["r"][0, 0], d["P"][0], d["Q"][0], wl.r_b, 11, 2, 6)
+    z2 = d["z"][0, 0].copy()
+    z2[:, wl.r_b:] += 100.0
+    moved = ref.route_page_scores(qg, z2, d["r"][0, 0], d["P"][0], d["Q"][0], wl.r_b, 11, 2, 6)
+    np.testing.assert_array_equal(base, moved)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def test_select_matches_exhaustive_search_with_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 11))
+        scores = rng.integers(-3, 4, size=n).astype(np.float64)  # many exact ties
+        mine = ref.select_pages(scores, n, k)
+        other = brute.select_pages(scores.tolist(), n, k)
+        assert mine.tolist() == other, (scores, k)
+
+
+def test_select_matches_stable_argsort():
+    rng = np.random.default_rng(12)
+    for n, k in [(128, 16), (1024, 128), (4096, 128), (100, 100), (37, 50)]:
+        scores = rng.standard_normal(n)
+        scores[::7] = scores[3]  # ties
+        want = np.sort(np.argsort(-scores, kind="stable")[:k])
+        want = np.concatenate([want, -np.ones(k - len(want), dtype=np.int64)])
+        np.testing.assert_array_equal(ref.select_pages(scores, n, k), want)
+
+
+def test_select_ignores_pages_past_n_pages():
+    scores = np.array([1.0, 5.0, 3.0, 9.0, 8.0])
+    np.testing.assert_array_equal(ref.select_pages(scores, 3, 2), [1, 2])
+    np.testing.assert_array_equal(ref.select_pages(scores, 0, 2), [-1, -1])
+
+
+# ---------------------------------------------------------------------------
+# attention over the selected pages
+# ---------------------------------------------------------------------------
+
+def _sdpa(q, k, v, mask=None):
+    """torch's CPU scaled_dot_product_attention in float64 (scale 1/sqrt(dh)).
+    q [G, dh] (the G heads act as a batch), k [n, dh], v [n, w], mask [n] bool."""
+    G = q.shape[0]
+    qt = torch.from_numpy(np.ascontiguousarray(q)).reshape(G, 1, 1, -1)
+    kt = torch.from_numpy(np.ascontiguousarray(k)).reshape(1, 1, *k.shape).expand(G, 1, -1, -1).contiguous()
+    vt = torch.from_numpy(np.ascontiguousarray(v)).reshape(1, 1, *v.shape).expand(G, 1, -1, -1).contiguous()
+    m = None
+    if mask is not None:
+        m = torch.from_numpy(mask).reshape(1, 1, 1, -1).expand(G, 1, 1, -1).contiguous()
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)
+    return out[:, 0, 0, :].numpy()
+
+
+@pytest.mark.parametrize("L", [2048, 2041])
+def test_attend_all_pages_equals_sdpa(L):
+    """k >= number of pages: attention over every valid token (library routine),
+    including a partial last page."""
+    wl = workload(0).with_(storage="f64", batch=1)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    G, S = wl.group, wl.page_size
+    n_pages = -(-L // S)
+    sel = np.arange(n_pages)
+    for g in range(wl.n_kv_heads):
+        qg = d["q"][0, g * G:(g + 1) * G]
+        mine = ref.attend_group(qg, d["kc"][0, g], d["z"][0, g], sel, L, S, 1 / math.sqrt(wl.head_dim))
+        want = _sdpa(qg, d["kc"][0, g, :L], d["z"][0, g, :L])
+        np.testing.assert_allclose(mine, want, rtol=1e-10, atol=1e-12)
+
+
+def test_attend_subset_matches_masked_sdpa_and_brute():
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    G, S, L = wl.group, wl.page_size, 11
+    sel = np.array([0, 2, 5, -1])  # page 5 is the partial last page (token 10 only)
+    scale = 0.37
+    for g in range(wl.n_kv_heads):
+        qg = d["q"][1, g * G:(g + 1) * G]
+        mine = ref.attend_group(qg, d["kc"][1, g], d["z"][1, g], sel, L, S, scale)
+        other = brute.attend_group(qg.tolist(), d["kc"][1, g].tolist(), d["z"][1, g].tolist(),
+                                   sel.tolist(), L, S, scale)
+        np.testing.assert_allclose(mine, other, rtol=1e-12, atol=1e-13)
+        mask = np.zeros(L, dtype=bool)
+        for p in (0, 2, 5):
+            mask[p * S:min((p + 1) * S, L)] = True
+        want = _sdpa(qg * scale * math.sqrt(wl.head_dim), d["kc"][1, g, :L], d["z"][1, g, :L], mask)
+        np.testing.assert_allclose(mine, want, rtol=1e-10, atol=1e-12)
+
+
+def test_attend_empty_selection_is_zero():
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    out = ref.attend_group(d["q"][0, :2], d["kc"][0, 0], d["z"][0, 0], np.array([-1, -1]), 11, 2, 0.5)
+    np.testing.assert_array_equal(out, 0.0)
+
+
+# ---------------------------------------------------------------------------
+# reconstruction
+# ---------------------------------------------------------------------------
+
+def test_reconstruct_matches_fused_brute():
+    wl = tiny_workload()
+    fac = synth.factors(wl)
+    Bf, W_O = ref.storage_to_f64(fac["Bf"], "f64"), ref.storage_to_f64(fac["W_O"], "f64")
+    u = np.random.default_rng(4).standard_normal((wl.n_q_heads, wl.r_v))
+    mine = ref.reconstruct(u, Bf, W_O, wl.group)
+    other = brute.reconstruct(u.tolist(), Bf.tolist(), W_O.tolist(), wl.group)
+    np.testing.assert_allclose(mine, other, rtol=1e-12, atol=1e-12)
+
+
+def test_full_k_invariant_equals_dense_attention_through_W_O():
+    """Exact factors and k = all pages: the latent path equals dense softmax
+    attention over (K, V = z B) followed by W_O (the pages' Full-K reference
+    with the same compressed Values)."""
+    wl = workload(0).with_(storage="f64", batch=1, ctx=512)
+    inp = synth.decode_inputs(wl, exact=True)
+    d = unpack(inp)
+    n_pages = wl.max_pages
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rb=wl.r_b, page_size=wl.page_size,
+                          top_k=n_pages, n_pages_out=n_pages, storage="f64")
+    G = wl.group
+    heads = []
+    for h in range(wl.n_q_heads):
+        g = h // G
+        v = d["z"][0, g] @ d["Bf"][g]
+        heads.append(_sdpa(d["q"][0, h:h + 1], d["kc"][0, g], v)[0])
+    y_dense = np.concatenate(heads) @ d["W_O"]
+    np.testing.assert_allclose(out["y"][0], y_dense, rtol=1e-9, atol=1e-10)
+
+
+def test_latent_identity_for_any_selection():
+    """(sum_t p_t z_t) B W_O == attention over reconstructed values z B, on the
+    selected tokens only, then W_O."""
+    wl = workload(0).with_(storage="f64", batch=1, ctx=700)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    L, S, G = 700, wl.page_size, wl.group
+    rng = np.random.default_rng(9)
+    sel = np.sort(rng.choice(-(-L // S), size=7, replace=False))
+    u = np.zeros((wl.n_q_heads, wl.r_v))
+    heads = []
+    mask = np.zeros(L, dtype=bool)
+    for p in sel:
+        mask[p * S:min((p + 1) * S, L)] = True
+    for g in range(wl.n_kv_heads):
+        qg = d["q"][0, g * G:(g + 1) * G]
+        u[g * G:(g + 1) * G] = ref.attend_group(qg, d["kc"][0, g], d["z"][0, g], sel, L, S,
+                                                1 / math.sqrt(wl.head_dim))
+    for h in range(wl.n_q_heads):
+        g = h // G
+        heads.append(_sdpa(d["q"][0, h:h + 1], d["kc"][0, g, :L], (d["z"][0, g] @ d["Bf"][g])[:L], mask)[0])
+    np.testing.assert_allclose(ref.reconstruct(u, d["Bf"], d["W_O"], G),
+                               np.concatenate(heads) @ d["W_O"], rtol=1e-10, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# a whole step, end to end against the brute-force statement
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seq_lens", [(11, 7), (0, 3), (1, 11)])
+def test_decode_step_matches_brute_end_to_end(seq_lens):
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl, seq_lens=np.array(seq_lens))
+    d = unpack(inp)
+    G, S, k = wl.group, wl.page_size, wl.top_k
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rb=wl.r_b, page_size=S, top_k=k,
+                          n_pages_out=wl.max_pages, storage="f64", k_new=d["k_new"], v_new=d["v_new"])
+    scale = 1 / math.sqrt(wl.head_dim)
+    for b in range(wl.batch):
+        L = int(seq_lens[b])
+        z, r, kc = d["z"][b].copy(), d["r"][b].copy(), d["kc"][b].copy()
+        u = np.zeros((wl.n_q_heads, wl.r_v))
+        if L > 0:
+            for g in range(wl.n_kv_heads):
+                zz, rr = brute.compress_token(d["k_new"][b, g], d["v_new"][b, g], d["A"][g].tolist(),
+                                              d["P"][g].tolist(), d["E"][g].tolist(), wl.r_b, float)
+                z[g, L - 1], r[g, L - 1], kc[g, L - 1] = zz, rr, d["k_new"][b, g]
+        for g in range(wl.n_kv_heads):
+            qg = d["q"][b, g * G:(g + 1) * G].tolist()
+            sc = brute.route_page_scores(qg, z[g].tolist(), r[g].tolist(), d["P"][g].tolist(),
+                                         d["Q"][g].tolist(), wl.r_b, L, S, wl.max_pages)
+            np.testing.assert_allclose(out["scores"][b, g], sc, rtol=1e-11, atol=1e-11)
+            n_pages = -(-L // S) if L > 0 else 0
+            sel = brute.select_pages(sc, n_pages, k)
+            assert out["sel"][b, g].tolist() == sel
+            u[g * G:(g + 1) * G] = brute.attend_group(qg, kc[g].tolist(), z[g].tolist(), sel, L, S, scale)
+        np.testing.assert_allclose(out["u"][b], u, rtol=1e-11, atol=1e-12)
+        y = brute.reconstruct(u.tolist(), d["Bf"].tolist(), d["W_O"].tolist(), G)
+        np.testing.assert_allclose(out["y"][b], y, rtol=1e-10, atol=1e-11)
+        if L <= 0:
+            np.testing.assert_array_equal(out["y"][b], 0.0)
+
+
+# ---------------------------------------------------------------------------
+# semantics of the synthetic workloads: planted pages are routed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("index,batch", [(0, 1), (1, 2), (2, 1), (3, 1)])
+def test_planted_pages_are_selected(index, batch):
+    wl = workload(index).with_(batch=batch)
+    inp = synth.decode_inputs(wl)
+    st = inp["storage"]
+    q, z, r = (ref.storage_to_f64(inp[k], st) for k in ("q", "z", "r"))
+    P, Q = ref.storage_to_f64(inp["P"], st), ref.storage_to_f64(inp["Q"], st)
+    G = wl.group
+    for b in range(batch):
+        planted = set(inp["planted"][b].tolist())
+        assert len(planted) == wl.n_planted
+        for g in range(wl.n_kv_heads):
+            sc = ref.route_page_scores(q[b, g * G:(g + 1) * G], z[b, g], r[b, g], P[g], Q[g], wl.r_b,
+                                       wl.ctx, wl.page_size, wl.max_pages)
+            sel = set(ref.select_pages(sc, wl.max_pages, wl.top_k).tolist())
+            assert planted <= sel, (b, g, sorted(planted - sel))
