@@ -1,0 +1,191 @@
+/*
+ * basiskv.h -- C ABI of libbasiskv.so: the BasisKV decode-time hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "BasisKV: Value Latents for Communication and Key Routing"
+ * (arXiv 2611.02583).  Per token and per physical KV head the cache holds a
+ * Value latent z (width r_v), a Key residual code r (width r_q) and the exact
+ * Key k (width head_dim) -- appendix Table 4.  A decode step
+ *   (a0) compresses the new token's Key and Value into those three states,
+ *   (a1) projects the queries onto the routing factors,
+ *   (a2) scores every Key page from the latent's leading r_b dims plus the
+ *        residual (the abstract's latent-based Key routing),
+ *   (a3) keeps the top_k pages per KV head,
+ *   (a4) computes exact softmax attention with the original Keys of the kept
+ *        pages only and sums the cached latents with those weights, and
+ *   (a5) maps the per-head latents to the model output through the fused
+ *        latent-to-output matrix M = blockdiag(B) W_O (Figure 1: the output is
+ *        rebuilt from the latents).
+ *
+ * Conventions shared by every entry point
+ *   - Plain C, no exceptions; every call returns a basiskv_status.  Host-side
+ *     validation runs before any launch: on a non-OK status nothing has been
+ *     enqueued and outputs are untouched.
+ *   - All memory is caller-owned and device-resident unless stated; the
+ *     library never allocates, frees or synchronises.  Calls are asynchronous
+ *     on `stream` (a hipStream_t; NULL = the default stream).  Calls on one
+ *     stream are ordered; concurrent calls that share a workspace race.
+ *   - `dims.dtype` is the storage format of queries, caches, factors, K/V
+ *     inputs, M and y: BASISKV_F32 (float32) or BASISKV_BF16 (bfloat16).
+ *     Arithmetic is float32 throughout (float32 accumulation; bf16 values are
+ *     widened exactly; stores to bf16 round to nearest-even).
+ *   - Query head h uses KV head h / (n_q_heads / n_kv_heads).
+ *   - Device-side indices are range-checked by the kernels: a block_table
+ *     entry outside [0, num_phys_pages), a selected page outside the
+ *     sequence, or a position outside [0, max_pages_per_seq * page_size) is
+ *     skipped (treated as absent), never dereferenced.  seq_lens are clamped
+ *     to [0, max_pages_per_seq * page_size].
+ *
+ * Paged cache layout (one pool per state, head-major):
+ *   pool[n_kv_heads][num_phys_pages][width / CE][page_size][CE]
+ * where CE = 16 / sizeof(element) (8 for bf16, 4 for float32) and width is
+ * r_v (z pool), r_q (r pool) or head_dim (k pool).  Token t of a page keeps its
+ * 16-byte chunk c at ((c * page_size) + t) * 16 bytes from the page start, so
+ * one wavefront with a token per lane reads page_size * 16 contiguous bytes per
+ * chunk.  Logical page p of sequence b is physical page block_table[b][p].
+ * Widths must be multiples of CE.
+ */
+#ifndef BASISKV_H
+#define BASISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BASISKV_OK = 0,
+  BASISKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  BASISKV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  BASISKV_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements */
+  BASISKV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  BASISKV_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
+} basiskv_status;
+
+enum { BASISKV_F32 = 0, BASISKV_BF16 = 1 };
+
+/* Sizes of one layer's decode problem (host values). */
+typedef struct {
+  int32_t batch;             /* sequences, >= 1 */
+  int32_t n_q_heads;         /* query heads, multiple of n_kv_heads */
+  int32_t n_kv_heads;        /* physical KV heads */
+  int32_t head_dim;          /* must be 128 */
+  int32_t hidden;            /* output width D of W_O (multiple of 16) */
+  int32_t r_v;               /* Value-latent width */
+  int32_t r_b;               /* routing base width: leading latent dims, <= r_v */
+  int32_t r_q;               /* Key-residual rank */
+  int32_t page_size;         /* tokens per page: 4, 8, 16, 32 or 64 */
+  int32_t max_pages_per_seq; /* columns of block_table, <= 32768 */
+  int32_t num_phys_pages;    /* pages per pool and per KV head */
+  int32_t dtype;             /* BASISKV_F32 or BASISKV_BF16 */
+} basiskv_dims;
+
+/* The paged cache (device pointers, caller-owned). */
+typedef struct {
+  void *z_pages;              /* Value latents  [n_kv][num_phys][r_v/CE][page_size][CE] */
+  void *r_pages;              /* residual codes [n_kv][num_phys][r_q/CE][page_size][CE] */
+  void *k_pages;              /* exact Keys     [n_kv][num_phys][head_dim/CE][page_size][CE] */
+  const int32_t *block_table; /* [batch][max_pages_per_seq] logical -> physical page */
+  const int32_t *seq_lens;    /* [batch] valid tokens of each sequence */
+} basiskv_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char *basiskv_status_string(int32_t status);
+
+/* Bytes of workspace that basiskv_route_pages and basiskv_sparse_attend need
+ * for these dims and top_k (the maximum of the two).  0 if dims are invalid. */
+size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t top_k);
+
+/* (a0) Compress new tokens into the cache -- BasisKV abstract (Value kept
+ * only as a low-rank latent; a Key-specific residual keeps what the latent
+ * cannot predict) and appendix Table 4 (the three cached states).
+ *   k, v      [batch][n_tokens][n_kv_heads][head_dim]  new Keys and Values
+ *   start_pos [batch] (device int32): token i of sequence b is written at
+ *             position start_pos[b] + i
+ *   A [n_kv][head_dim][r_v]   Value encoder:   z = v A            -> z pool
+ *   P [n_kv][r_b][head_dim]   latent -> Key predictor
+ *   E [n_kv][head_dim][r_q]   residual encoder: r = (k - z_s[:r_b] P) E -> r pool
+ *   the Key itself is copied to the k pool.  z_s is the latent as stored
+ *   (rounded to dtype).  GEMMs run on MFMA with float32 accumulation.
+ * seq_lens are not read or changed.  Returns ERR_SHAPE for n_tokens < 1. */
+int32_t basiskv_compress_prefill(const basiskv_dims *dims, const void *k, const void *v,
+                                 const int32_t *start_pos, int32_t n_tokens, const void *A,
+                                 const void *P, const void *E, const basiskv_cache *cache,
+                                 void *stream);
+
+/* (a1) Routing projections of the queries (appendix Table 4: routing reads
+ * r_b latent dims and r_q residual dims, so the query is carried into those
+ * two spaces once per step).
+ *   q [batch][n_q_heads][head_dim];  P [n_kv][r_b][head_dim];  Q [n_kv][r_q][head_dim]
+ *   q_proj [batch][n_q_heads][r_b + r_q] float32 out:
+ *          q_proj[b][h][:r_b] = P_g q_bh,  q_proj[b][h][r_b:] = Q_g q_bh. */
+int32_t basiskv_project_queries(const basiskv_dims *dims, const void *q, const void *P,
+                                const void *Q, float *q_proj, void *stream);
+
+/* (a2) Page scores from the cached latents and residual codes (BasisKV
+ * abstract: the latent predicts the routing part of the Key, the residual the
+ * rest; Table 9 caption: routing is per page).  For every valid token t of
+ * page p and head h of KV head g's group:
+ *   logit = q_proj[b][h][:r_b] . z_t[:r_b] + q_proj[b][h][r_b:] . r_t,
+ * page_scores[b][g][p] = max over the page's valid tokens and the group's
+ * heads; pages at or past ceil(seq_len / page_size) get -inf.
+ *   page_scores [batch][n_kv_heads][max_pages_per_seq] float32 out. */
+int32_t basiskv_score_pages(const basiskv_dims *dims, const float *q_proj,
+                            const basiskv_cache *cache, float *page_scores, void *stream);
+
+/* (a3) Top-k page selection per (sequence, KV head) (BasisKV abstract: only
+ * the selected pages' Keys are fetched).  Exact: the top_k largest scores
+ * among the sequence's ceil(seq_len / page_size) pages; equal scores go to
+ * the lower page index; the list is in ascending page order and padded with
+ * -1 when top_k exceeds the page count (all -1 for an empty sequence).
+ *   seq_lens [batch] device; sel [batch][n_kv_heads][top_k] int32 out. */
+int32_t basiskv_select_pages(const basiskv_dims *dims, const float *page_scores,
+                             const int32_t *seq_lens, int32_t top_k, int32_t *sel,
+                             void *stream);
+
+/* (a1)+(a2)+(a3) in one call; q_proj lives in the workspace. */
+int32_t basiskv_route_pages(const basiskv_dims *dims, const void *q, const void *P,
+                            const void *Q, const basiskv_cache *cache, int32_t top_k,
+                            float *page_scores, int32_t *sel, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* (a4) Exact attention over the selected pages, summed in latent space
+ * (BasisKV abstract: exact QK scores with the original Keys of the selected
+ * pages; Figure 1 and appendix Table 4: the weighted sum runs over the
+ * cached Value latents, all r_v dims).  For each query head h of KV head g:
+ *   s_t = scale * q_h . k_t over the valid tokens of the pages in sel[b][g],
+ *   p = softmax(s) over those tokens, u[b][h] = sum_t p_t z_t.
+ * Entries of sel that are -1 or outside the sequence are skipped; a head with
+ * no valid token gets u = 0.  scale is usually 1/sqrt(head_dim).
+ *   q [batch][n_q_heads][head_dim]; sel [batch][n_kv_heads][top_k];
+ *   u [batch][n_q_heads][r_v] float32 out. */
+int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
+                              const basiskv_cache *cache, const int32_t *sel, int32_t top_k,
+                              float scale, float *u, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* (a5) Output reconstruction y = u M (Figure 1: the complete output is rebuilt
+ * from the latents; abstract: Value compression is tied to the output
+ * projection).  MFMA GEMM with float32 accumulation; for bf16, u is split into
+ * two bf16 terms (hi + lo) so no precision is lost before the product.
+ *   u [batch][n_q_heads * r_v] float32;  M [hidden][n_q_heads * r_v] (row n of
+ *   M holds output feature n);  y [batch][hidden] out, in dtype.
+ * batch must be <= 64. */
+int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void *M, void *y,
+                            void *stream);
+
+/* Set-up: fuse the Value decoder into the output projection,
+ *   M[n][h * r_v + i] = sum_d Bf[h / G][i][d] * W_O[h * head_dim + d][n],
+ * i.e. M = (blockdiag_h(Bf_{h/G}) W_O)^T, float32 accumulation, stored in dtype.
+ *   Bf [n_kv][r_v][head_dim];  W_O [n_q_heads * head_dim][hidden];
+ *   M [hidden][n_q_heads * r_v] out. */
+int32_t basiskv_fuse_output_matrix(const basiskv_dims *dims, const void *Bf, const void *W_O,
+                                   void *M, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASISKV_H */

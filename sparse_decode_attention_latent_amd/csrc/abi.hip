@@ -1,0 +1,186 @@
+// C ABI of libbasiskv: host-side validation, workspace sizing and dispatch.
+// Every entry point validates its arguments before enqueuing anything and
+// returns a basiskv_status; nothing here allocates, frees or synchronises.
+#include <string.h>
+
+#include "common.hpp"
+
+namespace bkv_host {
+size_t compress_lds(const basiskv_dims &d);
+bool score_supported(const basiskv_dims &d);
+bool attend_supported(const basiskv_dims &d);
+}
+
+namespace {
+
+constexpr int kMaxPages = 32768;
+constexpr int kMaxGroup = 16;
+
+int elem_chunk(int dtype) { return dtype == BASISKV_BF16 ? 8 : 4; }
+
+bool pow2_page(int s) { return s == 4 || s == 8 || s == 16 || s == 32 || s == 64; }
+
+// Sizes common to every call.
+int32_t check_dims(const basiskv_dims *d) {
+  if (!d) return BASISKV_ERR_NULL;
+  if (d->dtype != BASISKV_F32 && d->dtype != BASISKV_BF16) return BASISKV_ERR_UNSUPPORTED;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->hidden < 1 || d->r_v < 1 || d->r_b < 1 || d->r_q < 1 || d->page_size < 1 ||
+      d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
+    return BASISKV_ERR_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0 || d->r_b > d->r_v) return BASISKV_ERR_SHAPE;
+  if (d->head_dim != bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
+  if (!pow2_page(d->page_size)) return BASISKV_ERR_UNSUPPORTED;
+  const int ce = elem_chunk(d->dtype);
+  if (d->r_v % ce || d->r_b % ce || d->r_q % ce) return BASISKV_ERR_UNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > kMaxGroup) return BASISKV_ERR_UNSUPPORTED;
+  if (d->max_pages_per_seq > kMaxPages) return BASISKV_ERR_UNSUPPORTED;
+  if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2) return BASISKV_ERR_SHAPE;
+  return BASISKV_OK;
+}
+
+int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_r) {
+  if (!c || !c->block_table || !c->seq_lens) return BASISKV_ERR_NULL;
+  if ((need_k && !c->k_pages) || (need_z && !c->z_pages) || (need_r && !c->r_pages))
+    return BASISKV_ERR_NULL;
+  return BASISKV_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t qproj_bytes(const basiskv_dims &d) {
+  return align_up((size_t)d.batch * d.n_q_heads * (d.r_b + d.r_q) * sizeof(float));
+}
+
+size_t attend_ws_bytes(const basiskv_dims &d, int32_t top_k) {
+  const int ns = bkv_host::attend_splits(d, top_k);
+  return align_up((size_t)d.batch * d.n_q_heads * ns * (d.r_v + 2) * sizeof(float));
+}
+
+int32_t launched(hipError_t e) { return e == hipSuccess ? BASISKV_OK : BASISKV_ERR_LAUNCH; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *basiskv_status_string(int32_t status) {
+  switch (status) {
+    case BASISKV_OK: return "ok";
+    case BASISKV_ERR_NULL: return "null pointer argument";
+    case BASISKV_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case BASISKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BASISKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case BASISKV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t basiskv_workspace_bytes(const basiskv_dims *d, int32_t top_k) {
+  if (check_dims(d) != BASISKV_OK || top_k < 1) return 0;
+  const size_t a = qproj_bytes(*d), b = attend_ws_bytes(*d, top_k);
+  return a > b ? a : b;
+}
+
+int32_t basiskv_compress_prefill(const basiskv_dims *d, const void *k, const void *v,
+                                 const int32_t *start_pos, int32_t n_tokens, const void *A,
+                                 const void *P, const void *E, const basiskv_cache *c,
+                                 void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!k || !v || !start_pos || !A || !P || !E) return BASISKV_ERR_NULL;
+  if ((st = check_cache(c, true, true, true))) return st;
+  if (n_tokens < 1) return BASISKV_ERR_SHAPE;
+  if (d->r_v % 16 || d->r_q % 16) return BASISKV_ERR_UNSUPPORTED;  // 16-wide MFMA output tiles
+  if ((int64_t)d->batch * n_tokens > INT32_MAX / 2) return BASISKV_ERR_SHAPE;
+  if (bkv_host::compress_lds(*d) > 160 * 1024) return BASISKV_ERR_UNSUPPORTED;
+  return launched(bkv_host::launch_compress(*d, k, v, start_pos, n_tokens, A, P, E, *c,
+                                            as_stream(stream)));
+}
+
+int32_t basiskv_project_queries(const basiskv_dims *d, const void *q, const void *P,
+                                const void *Q, float *q_proj, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || !P || !Q || !q_proj) return BASISKV_ERR_NULL;
+  return launched(bkv_host::launch_project(*d, q, P, Q, q_proj, as_stream(stream)));
+}
+
+int32_t basiskv_score_pages(const basiskv_dims *d, const float *q_proj, const basiskv_cache *c,
+                            float *page_scores, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q_proj || !page_scores) return BASISKV_ERR_NULL;
+  if ((st = check_cache(c, false, true, true))) return st;
+  if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  bool unsupported = false;
+  hipError_t e = bkv_host::launch_score(*d, q_proj, *c, page_scores, as_stream(stream), &unsupported);
+  if (unsupported) return BASISKV_ERR_UNSUPPORTED;
+  return launched(e);
+}
+
+int32_t basiskv_select_pages(const basiskv_dims *d, const float *page_scores,
+                             const int32_t *seq_lens, int32_t top_k, int32_t *sel, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!page_scores || !seq_lens || !sel) return BASISKV_ERR_NULL;
+  if (top_k < 1) return BASISKV_ERR_SHAPE;
+  return launched(bkv_host::launch_select(*d, page_scores, seq_lens, top_k, sel, as_stream(stream)));
+}
+
+int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P, const void *Q,
+                            const basiskv_cache *c, int32_t top_k, float *page_scores,
+                            int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || !P || !Q || !page_scores || !sel) return BASISKV_ERR_NULL;
+  if ((st = check_cache(c, false, true, true))) return st;
+  if (top_k < 1) return BASISKV_ERR_SHAPE;
+  if (!ws || ws_bytes < qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
+  if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  float *q_proj = static_cast<float *>(ws);
+  hipStream_t s = as_stream(stream);
+  bool unsupported = false;
+  hipError_t e = bkv_host::launch_project(*d, q, P, Q, q_proj, s);
+  if (e != hipSuccess) return BASISKV_ERR_LAUNCH;
+  e = bkv_host::launch_score(*d, q_proj, *c, page_scores, s, &unsupported);
+  if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
+  return launched(bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s));
+}
+
+int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basiskv_cache *c,
+                              const int32_t *sel, int32_t top_k, float scale, float *u, void *ws,
+                              size_t ws_bytes, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || !sel || !u) return BASISKV_ERR_NULL;
+  if ((st = check_cache(c, true, true, false))) return st;
+  if (top_k < 1) return BASISKV_ERR_SHAPE;
+  if (!bkv_host::attend_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < attend_ws_bytes(*d, top_k)) return BASISKV_ERR_WORKSPACE;
+  bool unsupported = false;
+  hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, static_cast<float *>(ws),
+                                         as_stream(stream), &unsupported);
+  if (unsupported) return BASISKV_ERR_UNSUPPORTED;
+  return launched(e);
+}
+
+int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M, void *y,
+                            void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!u || !M || !y) return BASISKV_ERR_NULL;
+  if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
+  return launched(bkv_host::launch_reconstruct(*d, u, M, y, as_stream(stream)));
+}
+
+int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const void *W_O, void *M,
+                                   void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!Bf || !W_O || !M) return BASISKV_ERR_NULL;
+  return launched(bkv_host::launch_fuse(*d, Bf, W_O, M, as_stream(stream)));
+}
+
+}  // extern "C"

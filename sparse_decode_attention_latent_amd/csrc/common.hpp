@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of libbasiskv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "basiskv.h"
+
+namespace bkv {
+
+constexpr int kHeadDim = 128;   // the only head dim the kernels are built for
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr int kXcds = 8;        // MI355X: 8 accelerator dies, each with its own L2
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Storage element types: float for BASISKV_F32, uint16_t (bf16 bits) for BASISKV_BF16.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int CE = 4;  // elements per 16-byte chunk
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int CE = 8;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+// Widen one 16-byte chunk to float32 (exact for both formats).
+template <typename T> __device__ __forceinline__ void unpack_chunk(const uint4 &c, float *x);
+template <> __device__ __forceinline__ void unpack_chunk<float>(const uint4 &c, float *x) {
+  x[0] = __uint_as_float(c.x);
+  x[1] = __uint_as_float(c.y);
+  x[2] = __uint_as_float(c.z);
+  x[3] = __uint_as_float(c.w);
+}
+template <> __device__ __forceinline__ void unpack_chunk<uint16_t>(const uint4 &c, float *x) {
+  x[0] = __uint_as_float(c.x << 16);
+  x[1] = __uint_as_float(c.x & 0xffff0000u);
+  x[2] = __uint_as_float(c.y << 16);
+  x[3] = __uint_as_float(c.y & 0xffff0000u);
+  x[4] = __uint_as_float(c.z << 16);
+  x[5] = __uint_as_float(c.z & 0xffff0000u);
+  x[6] = __uint_as_float(c.w << 16);
+  x[7] = __uint_as_float(c.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte_off) {
+  return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Work-item index of this workgroup for a 1-D grid of `padded` (multiple of 8)
+// workgroups: consecutive work items land on the same XCD, so workgroups that
+// share per-(sequence, head) data (projected queries, block-table rows) hit
+// the same L2.  Workgroups are dispatched round-robin over the XCDs.
+__device__ __forceinline__ int xcd_work_index(int padded) {
+  const int bid = blockIdx.x;
+  const int per_xcd = padded / kXcds;
+  return (bid % kXcds) * per_xcd + bid / kXcds;
+}
+
+__host__ __device__ __forceinline__ int clamp_len(int L, int cap) {
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+}  // namespace bkv
+
+// Host-side launchers (defined in the .hip files, called by abi.hip after validation).
+namespace bkv_host {
+hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, const void *Q,
+                          float *q_proj, hipStream_t s);
+hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
+                        float *scores, hipStream_t s, bool *unsupported);
+hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
+                         int32_t top_k, int32_t *sel, hipStream_t s);
+int attend_splits(const basiskv_dims &d, int32_t top_k);
+hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
+                         const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
+                         hipStream_t s, bool *unsupported);
+hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const void *M, void *y,
+                              hipStream_t s);
+hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
+                       hipStream_t s);
+hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
+                           const int32_t *start_pos, int32_t n_tokens, const void *A,
+                           const void *P, const void *E, const basiskv_cache &c, hipStream_t s);
+}  // namespace bkv_host

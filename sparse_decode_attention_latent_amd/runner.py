@@ -1,0 +1,126 @@
+"""A decode problem resident on the GPU, driven through the C ABI.
+
+Builds the device state of one layer's decode step from stored host arrays
+(queries, logical caches, factors) -- paged pools, block table, the fused
+latent-to-output matrix (computed by the library), workspace and outputs --
+and runs the step as the sequence of library calls:
+    compress_prefill (one new token per sequence, optional)
+    -> project_queries -> score_pages -> select_pages
+    -> sparse_attend -> reconstruct.
+PyTorch only allocates device memory and provides the stream.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from . import api, layout, synth
+
+
+def to_device(arr, storage, device="cuda"):
+    """Stored numpy array (float32, or uint16 bf16 bits) -> device tensor."""
+    a = np.ascontiguousarray(arr)
+    if storage == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host_storage(t, storage):
+    """Device tensor -> stored numpy array (inverse of to_device)."""
+    if storage == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class DecodeProblem:
+    """Device state for decode steps of one layer.
+
+    inp: dict from synth.decode_inputs (stored arrays).  The pools hold
+    ``max_pages`` pages per sequence, placed through a (by default shuffled)
+    block table.
+    """
+
+    def __init__(self, wl, inp, *, top_k=None, shuffle_seed=12345, device="cuda",
+                 max_pages=None):
+        self.wl = wl
+        self.storage = inp["storage"]
+        st = self.storage
+        q = inp["q"]
+        B, Hq, dh = q.shape
+        Hkv = inp["z"].shape[1]
+        T = inp["z"].shape[2]
+        S = wl.page_size
+        self.top_k = int(top_k or wl.top_k)
+        self.max_pages = int(max_pages or -(-T // S))
+        self.num_phys = B * self.max_pages
+        self.dims = api.make_dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh,
+                                  hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
+                                  page_size=S, max_pages_per_seq=self.max_pages,
+                                  num_phys_pages=self.num_phys,
+                                  dtype=api.BF16 if st == "bf16" else api.F32)
+        self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
+        dev = device
+        self.block_table = torch.from_numpy(self.block_table_host).to(dev)
+        self.seq_lens_host = np.asarray(inp["seq_lens"], dtype=np.int32)
+        self.seq_lens = torch.from_numpy(self.seq_lens_host).to(dev)
+        self.z_pages = to_device(layout.pack_pages(inp["z"], self.block_table_host, S, self.num_phys), st, dev)
+        self.r_pages = to_device(layout.pack_pages(inp["r"], self.block_table_host, S, self.num_phys), st, dev)
+        self.k_pages = to_device(layout.pack_pages(inp["kc"], self.block_table_host, S, self.num_phys), st, dev)
+        self.q = to_device(q, st, dev)
+        self.fac = {k: to_device(inp[k], st, dev) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
+        # appended token of the step: [B, 1, Hkv, dh], written at seq_len - 1
+        self.k_new = to_device(inp["k_new"][:, None], st, dev)
+        self.v_new = to_device(inp["v_new"][:, None], st, dev)
+        self.start_pos = (self.seq_lens - 1).to(torch.int32)
+        self.cache = api.make_cache(self.z_pages, self.r_pages, self.k_pages, self.block_table,
+                                    self.seq_lens)
+        tdt = torch.bfloat16 if st == "bf16" else torch.float32
+        self.M = torch.empty((wl.hidden, Hq * wl.r_v), dtype=tdt, device=dev)
+        api.fuse_output_matrix(self.dims, self.fac["Bf"], self.fac["W_O"], self.M)
+        ws = api.workspace_bytes(self.dims, self.top_k)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.q_proj = torch.empty((B, Hq, wl.r_b + wl.r_q), dtype=torch.float32, device=dev)
+        self.page_scores = torch.empty((B, Hkv, self.max_pages), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, Hkv, self.top_k), dtype=torch.int32, device=dev)
+        self.u = torch.empty((B, Hq, wl.r_v), dtype=torch.float32, device=dev)
+        self.y = torch.empty((B, wl.hidden), dtype=tdt, device=dev)
+        self.scale = 1.0 / math.sqrt(dh)
+
+    # -- the steps of the path, one library call each -------------------------
+    def append(self):
+        api.compress_prefill(self.dims, self.k_new, self.v_new, self.start_pos, 1, self.fac["A"],
+                             self.fac["P"], self.fac["E"], self.cache)
+
+    def project(self):
+        api.project_queries(self.dims, self.q, self.fac["P"], self.fac["Q"], self.q_proj)
+
+    def score(self):
+        api.score_pages(self.dims, self.q_proj, self.cache, self.page_scores)
+
+    def select(self):
+        api.select_pages(self.dims, self.page_scores, self.seq_lens, self.top_k, self.sel)
+
+    def attend(self):
+        api.sparse_attend(self.dims, self.q, self.cache, self.sel, self.top_k, self.scale, self.u,
+                          self.workspace)
+
+    def reconstruct(self):
+        api.reconstruct(self.dims, self.u.view(self.u.shape[0], -1), self.M, self.y)
+
+    def step(self, append=True):
+        if append:
+            self.append()
+        self.project()
+        self.score()
+        self.select()
+        self.attend()
+        self.reconstruct()
+
+    def outputs(self):
+        """Host copies: page_scores, sel, u (float64), y (stored form)."""
+        torch.cuda.synchronize()
+        return dict(scores=self.page_scores.double().cpu().numpy(),
+                    sel=self.sel.cpu().numpy().astype(np.int64),
+                    u=self.u.double().cpu().numpy(),
+                    y=to_host_storage(self.y, self.storage))

@@ -1,0 +1,131 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+its host-side validation answers with the documented status codes before any
+device work (no GPU needed: invalid calls return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_decode_attention_latent_amd import api
+from sparse_decode_attention_latent_amd.configs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "basiskv.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="libbasiskv.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(basiskv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert header_functions() == sorted(api.EXPORTED)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_status_strings():
+    lib = api.lib()
+    for code in range(6):
+        assert lib.basiskv_status_string(code)
+    assert lib.basiskv_status_string(99) == b"unknown status"
+
+
+def dims_of(wl, **over):
+    kw = dict(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+              hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q, page_size=wl.page_size,
+              max_pages_per_seq=wl.max_pages, num_phys_pages=wl.batch * wl.max_pages,
+              dtype=api.BF16 if wl.storage == "bf16" else api.F32)
+    kw.update(over)
+    return api.make_dims(**kw)
+
+
+@needs_lib
+def test_workspace_bytes():
+    for wl in WORKLOADS:
+        d = dims_of(wl)
+        ws = api.workspace_bytes(d, wl.top_k)
+        assert ws > 0 and ws % 256 == 0
+        # covers the routing projections and the attention partials
+        assert ws >= wl.batch * wl.n_q_heads * (wl.r_b + wl.r_q) * 4
+    assert api.workspace_bytes(dims_of(WORKLOADS[2], n_q_heads=30), 8) == 0
+    assert api.workspace_bytes(dims_of(WORKLOADS[2]), 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _cache(**kw):
+    base = dict(z_pages=0x1000, r_pages=0x1000, k_pages=0x1000, block_table=0x1000, seq_lens=0x1000)
+    base.update(kw)
+    return api.Cache(**base)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(n_q_heads=30), 2),          # Hq % Hkv != 0
+    (dict(r_b=128), 2),               # r_b > r_v
+    (dict(batch=0), 2),
+    (dict(head_dim=64), 3),           # only 128 is built
+    (dict(page_size=12), 3),
+    (dict(r_q=36), 3),                # not a multiple of 16 bytes
+    (dict(dtype=7), 3),
+    (dict(max_pages_per_seq=40000), 3),
+])
+def test_dims_validation(over, code):
+    lib = api.lib()
+    d = dims_of(WORKLOADS[2], **over)
+    c = _cache()
+    assert lib.basiskv_project_queries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.basiskv_score_pages(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, None) == code
+    assert lib.basiskv_select_pages(ctypes.byref(d), FAKE, FAKE, 8, FAKE, None) == code
+    assert lib.basiskv_reconstruct(ctypes.byref(d), FAKE, FAKE, FAKE, None) == code
+
+
+@needs_lib
+def test_null_and_shape_and_workspace_errors():
+    lib = api.lib()
+    d = dims_of(WORKLOADS[2])
+    c = _cache()
+    assert lib.basiskv_project_queries(None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.basiskv_project_queries(ctypes.byref(d), None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.basiskv_score_pages(ctypes.byref(d), FAKE, ctypes.byref(_cache(r_pages=None)), FAKE, None) == 1
+    assert lib.basiskv_select_pages(ctypes.byref(d), FAKE, FAKE, 0, FAKE, None) == 2
+    assert lib.basiskv_route_pages(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(c), 128, FAKE, FAKE,
+                                   FAKE, 16, None) == 4
+    assert lib.basiskv_route_pages(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(c), 128, FAKE, FAKE,
+                                   None, 1 << 20, None) == 4
+    assert lib.basiskv_sparse_attend(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, 128, 0.1, FAKE, FAKE,
+                                     64, None) == 4
+    assert lib.basiskv_sparse_attend(ctypes.byref(d), FAKE, ctypes.byref(_cache(k_pages=None)), FAKE, 128,
+                                     0.1, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.basiskv_compress_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE,
+                                        ctypes.byref(c), None) == 2
+    assert lib.basiskv_compress_prefill(ctypes.byref(d), FAKE, FAKE, None, 1, FAKE, FAKE, FAKE,
+                                        ctypes.byref(c), None) == 1
+    assert lib.basiskv_fuse_output_matrix(ctypes.byref(d), FAKE, None, FAKE, None) == 1
+    big = dims_of(WORKLOADS[2], batch=40)
+    assert lib.basiskv_reconstruct(ctypes.byref(big), FAKE, FAKE, FAKE, None) == 3
+
+
+@needs_lib
+def test_unsupported_variant_is_reported_before_launch():
+    lib = api.lib()
+    # group size 3 has no scoring / attention variant
+    d = dims_of(WORKLOADS[2], n_q_heads=24)
+    c = _cache()
+    assert lib.basiskv_score_pages(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, None) == 3
+    assert lib.basiskv_route_pages(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(c), 8, FAKE, FAKE,
+                                   FAKE, 1 << 30, None) == 3
+    assert lib.basiskv_sparse_attend(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, 8, 0.1, FAKE, FAKE,
+                                     1 << 30, None) == 3
