@@ -124,3 +124,64 @@ class DecodeProblem:
                     sel=self.sel.cpu().numpy().astype(np.int64),
                     u=self.u.double().cpu().numpy(),
                     y=to_host_storage(self.y, self.storage))
+
+    def token_codes(self, b, pos):
+        """Stored latent and residual codes of token ``pos`` of sequence b, read
+        back from the pools: (z [Hkv, rV], r [Hkv, rq]) in stored form."""
+        S = self.wl.page_size
+        phys = int(self.block_table_host[b, pos // S])
+        slot = pos % S
+        z = self.z_pages[:, phys, :, slot, :].reshape(self.z_pages.shape[0], -1)
+        r = self.r_pages[:, phys, :, slot, :].reshape(self.r_pages.shape[0], -1)
+        return to_host_storage(z.contiguous(), self.storage), to_host_storage(r.contiguous(), self.storage)
+
+
+class PrefillProblem:
+    """Compression of a batch of prompts into empty paged pools.
+
+    k, v: stored host arrays [B, T, Hkv, dh]; fac: stored factor arrays (A, P,
+    E).  Tokens of sequence b go to positions 0 .. T-1 through a (by default
+    shuffled) block table.
+    """
+
+    def __init__(self, wl, k, v, fac, *, storage, shuffle_seed=54321, device="cuda"):
+        self.wl, self.storage = wl, storage
+        B, T, Hkv, dh = k.shape
+        S = wl.page_size
+        self.T = T
+        self.max_pages = -(-T // S)
+        self.num_phys = B * self.max_pages
+        self.dims = api.make_dims(batch=B, n_q_heads=wl.n_q_heads, n_kv_heads=Hkv, head_dim=dh,
+                                  hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
+                                  page_size=S, max_pages_per_seq=self.max_pages,
+                                  num_phys_pages=self.num_phys,
+                                  dtype=api.BF16 if storage == "bf16" else api.F32)
+        self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
+        self.block_table = torch.from_numpy(self.block_table_host).to(device)
+        self.seq_lens = torch.full((B,), T, dtype=torch.int32, device=device)
+        self.start_pos = torch.zeros((B,), dtype=torch.int32, device=device)
+        self.k = to_device(k, storage, device)
+        self.v = to_device(v, storage, device)
+        self.fac = {n: to_device(fac[n], storage, device) for n in ("A", "P", "E")}
+        tdt = torch.bfloat16 if storage == "bf16" else torch.float32
+        ce = 8 if storage == "bf16" else 4
+
+        def pool(w):
+            return torch.zeros((Hkv, self.num_phys, w // ce, S, ce), dtype=tdt, device=device)
+
+        self.z_pages, self.r_pages, self.k_pages = pool(wl.r_v), pool(wl.r_q), pool(dh)
+        self.cache = api.make_cache(self.z_pages, self.r_pages, self.k_pages, self.block_table,
+                                    self.seq_lens)
+
+    def run(self):
+        api.compress_prefill(self.dims, self.k, self.v, self.start_pos, self.T, self.fac["A"],
+                             self.fac["P"], self.fac["E"], self.cache)
+
+    def logical(self):
+        """Host copies of the pools as logical [B, Hkv, T, w] stored arrays."""
+        torch.cuda.synchronize()
+        out = {}
+        for name, t in (("z", self.z_pages), ("r", self.r_pages), ("k", self.k_pages)):
+            out[name] = layout.unpack_pages(to_host_storage(t, self.storage), self.block_table_host,
+                                            self.wl.page_size, self.T)
+        return out

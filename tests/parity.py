@@ -1,0 +1,141 @@
+"""Helpers of the GPU parity tests: the oracle's answer for chosen sequences of
+a workload, and the comparison rules.
+
+The oracle side calls only oracle/ on the generator's stored arrays (decoded
+exactly to float64).  Nothing computed by the HIP library is ever an oracle
+input, with one sanctioned exception: attention and reconstruction are also
+re-run over the library's own page selection, since several selections are
+correct when two page scores are within rounding of each other.
+
+Tolerances (stated once, used by every GPU test):
+  page scores  |gpu - ref| <= 1e-5 * max(|ref|, rms of the row's valid scores)
+               (float32 accumulation of <= 144 products against float64)
+  selection    bit-exact against the oracle's select applied to the library's
+               own float32 scores (the integer decision taken in the kernel's
+               precision), and the band rule against the oracle's scores: a
+               page more than 1e-3 (relative) above the k-th score is chosen,
+               one more than 1e-3 below it is not
+  u            max |gpu - ref| / max |ref| <= 1e-4 per (sequence, head)
+               (float32 arithmetic in both storage formats)
+  y            max |gpu - ref| / max |ref| <= 1e-4 (float32) or 2e-2 (bf16)
+               per sequence
+  z, r pages   max |gpu - ref| / max |ref| per token row <= 1e-5 (float32)
+               or 2e-2 (bf16), and, for bf16, at most one unit in the last
+               place of the stored value
+"""
+
+import math
+
+import numpy as np
+
+from oracle import basiskv_ref as ref
+
+SCORE_RTOL = 1e-5
+BAND = 1e-3
+U_RTOL = 1e-4
+Y_RTOL = {"f32": 1e-4, "bf16": 2e-2}
+CODE_RTOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def f64(a, storage):
+    return ref.storage_to_f64(a, storage)
+
+
+def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_pages_out=None,
+                    scale=None):
+    """The oracle's decode step for sequence b of a workload's stored inputs.
+
+    Returns scores [Hkv, NPout], sel [Hkv, k], u [Hq, rV], y [D], y_stored,
+    and the appended token's stored codes (z_new, r_new: [Hkv, w]).
+    sel_override [Hkv, k] replaces the oracle's own selection for attention.
+    """
+    st = inp["storage"]
+    G, hkv, S = wl.group, wl.n_kv_heads, wl.page_size
+    T = inp["z"].shape[2]
+    if n_pages_out is None:
+        n_pages_out = -(-T // S)
+    if scale is None:
+        scale = 1.0 / math.sqrt(wl.head_dim)
+    L = int(inp["seq_lens"][b])
+    fac = {k: f64(inp[k], st) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
+    q = f64(inp["q"][b], st)
+    scores = np.full((hkv, n_pages_out), -np.inf)
+    sel = np.full((hkv, top_k), -1, dtype=np.int64)
+    u = np.zeros((wl.n_q_heads, wl.r_v))
+    z_new = np.zeros((hkv, wl.r_v))
+    r_new = np.zeros((hkv, wl.r_q))
+    if L > 0:
+        n_pages = -(-L // S)
+        if append:
+            zs, rs, _ = ref.compress_tokens(f64(inp["k_new"][b:b + 1], st), f64(inp["v_new"][b:b + 1], st),
+                                            fac["A"], fac["P"], fac["E"], wl.r_b, st)
+            z_new, r_new = zs[0], rs[0]
+        for g in range(hkv):
+            z = f64(inp["z"][b, g, :L], st)
+            r = f64(inp["r"][b, g, :L], st)
+            kc = f64(inp["kc"][b, g, :L], st)
+            if append:
+                z[L - 1], r[L - 1], kc[L - 1] = z_new[g], r_new[g], f64(inp["k_new"][b, g], st)
+            qg = q[g * G:(g + 1) * G]
+            scores[g] = ref.route_page_scores(qg, z, r, fac["P"][g], fac["Q"][g], wl.r_b, L, S,
+                                              n_pages_out)
+            sel[g] = ref.select_pages(scores[g], n_pages, top_k)
+            use = sel[g] if sel_override is None else np.asarray(sel_override[g], dtype=np.int64)
+            u[g * G:(g + 1) * G] = ref.attend_group(qg, kc, z, use, L, S, scale)
+    y = ref.reconstruct(u, fac["Bf"], fac["W_O"], G) if L > 0 else np.zeros(wl.hidden)
+    return dict(scores=scores, sel=sel, u=u, y=y, y_stored=ref.round_to_storage(y, st),
+                z_new=z_new, r_new=r_new, n_pages=(-(-L // S) if L > 0 else 0))
+
+
+def check_scores(gpu, want, n_pages, where=""):
+    """Page scores of one (sequence, KV head)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert np.all(np.isneginf(gpu[n_pages:])), f"{where}: pages past the sequence must be -inf"
+    if n_pages == 0:
+        return
+    g, w = gpu[:n_pages], want[:n_pages]
+    rms = math.sqrt(float(np.mean(w * w)))
+    err = np.abs(g - w) / np.maximum(np.abs(w), rms)
+    assert err.max() <= SCORE_RTOL, f"{where}: score rel err {err.max():.3g} at page {int(err.argmax())}"
+
+
+def check_selection(gpu_sel, gpu_scores, want_scores, n_pages, top_k, where=""):
+    """Selection of one (sequence, KV head): exact in the kernel's precision,
+    and inside the band rule against the oracle's float64 scores."""
+    gpu_sel = np.asarray(gpu_sel, dtype=np.int64)
+    # 1. the integer decision over the library's own float32 scores
+    exact = ref.select_pages(np.asarray(gpu_scores, dtype=np.float64), n_pages, top_k)
+    np.testing.assert_array_equal(gpu_sel, exact, err_msg=f"{where}: selection over own scores")
+    if n_pages <= top_k:
+        return
+    # 2. band rule against the oracle's scores
+    w = want_scores[:n_pages]
+    tau = np.sort(w)[::-1][top_k - 1]
+    chosen = np.zeros(n_pages, dtype=bool)
+    chosen[gpu_sel[gpu_sel >= 0]] = True
+    rel = np.abs(w - tau) / np.maximum(np.maximum(np.abs(tau), np.abs(w)), 1e-300)
+    must = (w > tau) & (rel > BAND)
+    must_not = (w < tau) & (rel > BAND)
+    assert np.all(chosen[must]), f"{where}: missed pages {np.nonzero(must & ~chosen)[0]}"
+    assert not np.any(chosen[must_not]), f"{where}: extra pages {np.nonzero(must_not & chosen)[0]}"
+
+
+def rel_rows(gpu, want):
+    """max |gpu - want| / max |want| over the last axis, per leading index."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    num = np.abs(gpu - want).max(axis=-1)
+    den = np.abs(want).max(axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def bf16_ulps(gpu_bits, want_f64):
+    """Distance in bf16 units in the last place between stored bits and the
+    oracle's rounded value (both finite)."""
+    a = np.asarray(gpu_bits, dtype=np.uint16).astype(np.int64)
+    wb = (ref.round_to_storage(want_f64, "bf16").astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+
+    def ordered(x):
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+
+    return np.abs(ordered(a) - ordered(wb))
