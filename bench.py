@@ -1,0 +1,217 @@
+"""Decode-step benchmark of the BasisKV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one layer's whole decode path over one batch, each stage one call
+of libbasiskv: compress_prefill of the step's new token (one per sequence),
+project_queries, score_pages, select_pages, sparse_attend, reconstruct.
+Inputs are seeded synthetic arrays already resident in device memory when
+the timed region starts; K steps run back to back on one stream and are
+bracketed by torch.cuda.synchronize().  HIP events recorded on that stream
+between the calls give every stage's average duration.
+
+The default workload is the Llama-3.1-8B-shaped layer at 32K context
+(batch 8, 32 query / 8 KV heads, head dim 128, latent width 64, residual
+rank 32, 32-token pages, 128 pages kept per KV head).  One JSON line goes to
+stdout: value = algorithmic HBM bytes of the step / step time (GB/s), with
+the step time itself as ms_per_step and us_per_layer; "roofline" covers the
+dominant kernel (page scoring, route_scan_kernel); "cpu_baseline" times the
+float64 oracle on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/layer + achieved HBM GB/s vs peak, 8B-shaped GQA at 32K ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "route_scan_llama8b_ctx32k_pmc.json")
+ROUTE_SOURCES = ("sparse_decode_attention_latent_amd/csrc/route.hip",
+                 "sparse_decode_attention_latent_amd/csrc/common.hpp")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b-ctx32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def route_source_sha():
+    h = hashlib.sha256()
+    for rel in ROUTE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per route_scan launch from the committed rocprofv3 counter
+    summary, or None when there is none for this workload or the kernel's
+    source changed since the counters were taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    with open(PMC_SUMMARY) as f:
+        s = json.load(f)
+    if s.get("workload") != workload_name or s.get("source_sha256") != route_source_sha():
+        return None
+    return float(s["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(wl, inp, target_seconds):
+    """The float64 oracle, as it stands, on whole sequences of the workload,
+    cycling over the batch until about target_seconds have passed (at least
+    one sequence)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import basiskv_ref as ref
+    from sparse_decode_attention_latent_amd import traffic
+
+    st = inp["storage"]
+    f = {k: ref.storage_to_f64(inp[k], st) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
+    B = inp["q"].shape[0]
+    one = _shape(wl, 1, inp)
+    seqs = []
+    for b in range(B):
+        x = {k: ref.storage_to_f64(inp[k][b:b + 1], st)
+             for k in ("q", "z", "r", "kc", "k_new", "v_new")}
+        x["L"] = inp["seq_lens"][b:b + 1]
+        seqs.append(x)
+    done, elapsed, nbytes = 0, 0.0, 0
+    while elapsed < target_seconds or done == 0:
+        x = seqs[done % B]
+        t0 = time.perf_counter()
+        ref.decode_step(x["q"], x["z"], x["r"], x["kc"], x["L"], f["A"], f["Bf"], f["P"], f["Q"],
+                        f["E"], f["W_O"], rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k,
+                        n_pages_out=-(-x["z"].shape[2] // wl.page_size), storage=st,
+                        k_new=x["k_new"], v_new=x["v_new"])
+        elapsed += time.perf_counter() - t0
+        nbytes += traffic.step_bytes(one, x["L"])["total"]
+        done += 1
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": max(threads) if threads else 1, "kind": "oracle",
+            "sample": f"{done} single-sequence decode steps (append, route, select, attend, "
+                      f"reconstruct) cycling over the {B} sequences of the same workload, "
+                      f"float64 numpy oracle, {elapsed:.1f} s",
+            "us_per_layer_equiv": round(elapsed / done * B * 1e6, 1)}
+
+
+def _shape(wl, B, inp):
+    from sparse_decode_attention_latent_amd import traffic
+    T = inp["z"].shape[2]
+    return traffic.StepShape(batch=B, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                             head_dim=wl.head_dim, hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b,
+                             r_q=wl.r_q, page_size=wl.page_size, max_pages=-(-T // wl.page_size),
+                             top_k=wl.top_k, elem=2 if inp["storage"] == "bf16" else 4)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the decode path is built and measured on one GPU's share of the work; the "
+              "multi-GPU sharding is a design, not a run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_decode_attention_latent_amd import api, synth, traffic
+    from sparse_decode_attention_latent_amd.configs import workload
+    from sparse_decode_attention_latent_amd.runner import DecodeProblem
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    api.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    wl = workload(int(args.workload) if args.workload.isdigit() else args.workload)
+    # for the prefill + decode workload the step measured is the last decode
+    # step (context 131072)
+    wl_step = wl
+    log(f"[bench] generating inputs for {wl.name} ...")
+    t0 = time.perf_counter()
+    inp = synth.decode_inputs(wl_step)
+    prob = DecodeProblem(wl_step, inp)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident ({time.perf_counter() - t0:.1f} s)")
+
+    stages = ("append", "project", "score", "select", "attend", "reconstruct")
+    calls = [prob.append, prob.project, prob.score, prob.select, prob.attend, prob.reconstruct]
+
+    for _ in range(args.warmup):
+        prob.step(append=True)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"[bench] timed {K} steps in {wall * 1e3:.2f} ms")
+
+    per_stage = {s: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K * 1e3
+                 for j, s in enumerate(stages)}
+    gpu_step_us = sum(ev[i][0].elapsed_time(ev[i][-1]) for i in range(K)) / K * 1e3
+    ms_per_step = wall / K * 1e3
+
+    shape = _shape(wl_step, inp["q"].shape[0], inp)
+    sb = traffic.step_bytes(shape, inp["seq_lens"])
+    value = sb["total"] / (ms_per_step * 1e-3) / 1e9
+    score_gbs = sb["score"] / (per_stage["score"] * 1e-6) / 1e9
+    traffic_bytes = measured_traffic(wl.name)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the float64 oracle on the host ...")
+        cpu = cpu_baseline(wl_step, inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "us_per_layer": round(ms_per_step * 1e3, 3), "gpu_us_per_step": round(gpu_step_us, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.storage,
+        "data": "synthetic (seeded generator; no weights or datasets)",
+        "config": {"workload": wl.name, "batch": shape.batch, "ctx": int(inp["z"].shape[2]),
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "hidden": wl.hidden, "page_size": wl.page_size,
+                   "r_v": wl.r_v, "r_b": wl.r_b, "r_q": wl.r_q, "top_k": wl.top_k},
+        "algorithmic_bytes_per_step": sb["total"],
+        "stages_us": {k: round(v, 3) for k, v in per_stage.items()},
+        "stages_gbs": {k: round(sb[k] / (per_stage[k] * 1e-6) / 1e9, 1) for k in stages},
+        "roofline": {"kernel": "route_scan_kernel (page scoring)", "bound": "hbm",
+                     "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": sb["score"], "launch_us": round(per_stage["score"], 3),
+                     "traffic": traffic_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,8 +8,11 @@ re-run over the library's own page selection, since several selections are
 correct when two page scores are within rounding of each other.
 
 Tolerances (stated once, used by every GPU test):
-  page scores  |gpu - ref| <= 1e-5 * max(|ref|, rms of the row's valid scores)
-               (float32 accumulation of <= 144 products against float64)
+  page scores  |gpu - ref| <= 1e-4 * max(|ref|, rms of the row's valid scores)
+               (the float32 output bar; the kernel accumulates up to 144
+               products in float32 after a 128-term float32 projection, whose
+               worst-case error relative to a near-cancelling score exceeds
+               1e-5)
   selection    bit-exact against the oracle's select applied to the library's
                own float32 scores (the integer decision taken in the kernel's
                precision), and the band rule against the oracle's scores: a
@@ -20,8 +23,14 @@ Tolerances (stated once, used by every GPU test):
   y            max |gpu - ref| / max |ref| <= 1e-4 (float32) or 2e-2 (bf16)
                per sequence
   z, r pages   max |gpu - ref| / max |ref| per token row <= 1e-5 (float32)
-               or 2e-2 (bf16), and, for bf16, at most one unit in the last
-               place of the stored value
+               or 2e-2 (bf16); for bf16 also every stored latent element
+               within one unit in the last place of the oracle's rounded
+               value unless its absolute error is below 1e-4 of the row's
+               largest magnitude (near zero the bf16 unit is finer than
+               float32 accumulation error, so a rounding decision there may
+               legitimately flip).  The residual code has no unit bound: it
+               is computed from the stored latent, and a legitimate one-unit
+               difference there moves r by about |P| |E| units of z.
 """
 
 import math
@@ -30,7 +39,7 @@ import numpy as np
 
 from oracle import basiskv_ref as ref
 
-SCORE_RTOL = 1e-5
+SCORE_RTOL = 1e-4
 BAND = 1e-3
 U_RTOL = 1e-4
 Y_RTOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -127,6 +136,20 @@ def rel_rows(gpu, want):
     num = np.abs(gpu - want).max(axis=-1)
     den = np.abs(want).max(axis=-1)
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+ULP_FLOOR = 1e-4
+
+
+def bf16_off_by_more_than_one_ulp(gpu_bits, want_f64):
+    """Mask of stored bf16 elements that are more than one unit in the last
+    place from the oracle's rounded value AND whose absolute error exceeds
+    ULP_FLOOR times the row's largest oracle magnitude (last axis = row)."""
+    want = np.asarray(want_f64, dtype=np.float64)
+    ulps = bf16_ulps(gpu_bits, want)
+    err = np.abs(ref.storage_to_f64(gpu_bits, "bf16") - want)
+    floor = ULP_FLOOR * np.abs(want).max(axis=-1, keepdims=True)
+    return (ulps > 1) & (err > floor)
 
 
 def bf16_ulps(gpu_bits, want_f64):
