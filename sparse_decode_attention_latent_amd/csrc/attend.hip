@@ -4,13 +4,36 @@
 // is carried as a Value latent), appendix Table 4 (selected attention reads
 // r_v latent dims and head_dim Key dims per selected token).
 //
-// Split-K over the selected pages, flash-decoding style: each workgroup takes
-// a run of one (sequence, KV head)'s selected pages, keeps a running max /
-// sum / latent accumulator per query head, and writes one partial; a second
-// kernel merges the partials in a fixed order (deterministic, no atomics).
+// Split-K over the selected pages, flash-decoding style.  Each workgroup
+// takes a run of one (sequence, KV head)'s selected pages; each of its
+// wavefronts walks 64-token blocks of that run with one token per lane:
+//   * the lane gathers its token's Key (head_dim * 2 or 4 bytes as 16-byte
+//     chunks: with the chunk-major page layout a wavefront reads page_size *
+//     16 contiguous bytes per chunk) and, in the same breath, the latent
+//     chunks it owns in the weighted-sum phase, so both gathers are in flight
+//     together;
+//   * exact scores against the group's queries, held as float32 in LDS and
+//     read by broadcast;
+//   * an online softmax with a wavefront-uniform running max per head;
+//   * the weighted latent sum: the block's probabilities go through a
+//     wavefront-private LDS row, and lane (tg, vc) accumulates chunk vc of the
+//     tokens tg, tg + TG, ... for every head of the group.
+// The wavefronts and the workgroup's splits are merged in a fixed order
+// (deterministic, no atomics).  A single split writes u directly; otherwise
+// a second kernel merges the per-split partial records.
 #include "common.hpp"
 
 namespace bkv {
+
+constexpr int kAttendWaves = 4;
+#ifndef BKV_ATTEND_WAVES_PER_EU
+#define BKV_ATTEND_WAVES_PER_EU 2
+#endif
+constexpr int kMaxSplits = 64;  // partial records per (sequence, head)
+#ifndef BKV_ATTEND_BLOCKS
+#define BKV_ATTEND_BLOCKS 2
+#endif
+constexpr int kAttendBlocks = BKV_ATTEND_BLOCKS;  // 64-token blocks per wavefront
 
 struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
@@ -18,22 +41,41 @@ struct AttendArgs {
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
 };
 
+// Ordering point for LDS traffic between the lanes of one wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Partial record per (b, h, split): [m, l, u[0..r_v)] with m in base-2 logit
 // units (scale * log2 e already applied), l = sum 2^(s - m), u = sum 2^(s - m) z.
+//
+// Each wavefront owns kAttendBlocks 64-token blocks of the split; their
+// selection entries and block-table rows are requested before the queries are
+// staged, so the chain selection -> block table -> Key gather costs its
+// latency once per wavefront rather than once per block.  With a wide query
+// group (G * latent chunks > 48) the latent chunks are gathered after the
+// scores instead of beside the Key, keeping the live registers within two
+// wavefronts per SIMD.
 template <typename T, int G, int NVC>
-__global__ __launch_bounds__(256) void attend_split_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BKV_ATTEND_WAVES_PER_EU)))
+void attend_split_kernel(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ zpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ sel, float *__restrict__ part, AttendArgs a) {
+    const int32_t *__restrict__ sel, float *__restrict__ part, float *__restrict__ u_out,
+    AttendArgs a) {
   constexpr int CE = Elem<T>::CE;
   constexpr int NKC = kHeadDim / CE;  // Key chunks per token
   constexpr int RV = NVC * CE;        // latent width
   constexpr int TG = kWave / NVC;     // token groups in the latent phase
   constexpr int NJ = (kWave + TG - 1) / TG;
-  constexpr int NW = 4;               // wavefronts per workgroup
+  constexpr int NW = kAttendWaves;
+  constexpr int NB = kAttendBlocks;
+  constexpr bool kZLate = G * NVC > 48 || sizeof(T) == 4;
 
-  __shared__ float p_lds[NW][kWave][G];
-  __shared__ int64_t zoff_lds[NW][kWave];
+  __shared__ __align__(16) float q_lds[G][kHeadDim];
+  __shared__ float p_lds[NW][G][kWave];
   __shared__ float m_lds[NW][G];
   __shared__ float l_lds[NW][G];
   __shared__ float u_lds[NW][G][RV];
@@ -43,8 +85,6 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   const int bg = work / a.n_split;
   const int split = work - bg * a.n_split;
   const int b = bg / a.n_kv, g = bg - b * a.n_kv;
-  const int L = clamp_len(seq_lens[b], a.cap);
-  const int NP = (L + a.page_size - 1) >> a.log2_page;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -53,17 +93,52 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   const int e_begin = split * a.pages_per_split;
   const int e_end = min(a.top_k, e_begin + a.pages_per_split);
   const int n_blocks = (e_end - e_begin + ppi - 1) / ppi;
-  const int n_iter = (n_blocks + NW - 1) / NW;  // same trip count for every wavefront
-
   const int32_t *sel_bg = sel + (int64_t)bg * a.top_k;
   const int32_t *bt = block_table + (int64_t)b * a.max_pages;
-  const uint32_t *q32 = reinterpret_cast<const uint32_t *>(q);
-  const int64_t qrow0 = ((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim;  // element index
+
+  // ---- this wavefront's blocks of round r: selection entries, then physical pages ----
+  const int L = clamp_len(seq_lens[b], a.cap);
+  const int NP = (L + a.page_size - 1) >> a.log2_page;
+  const int n_rounds = (n_blocks + NW * NB - 1) / (NW * NB);
+  int page[NB], phys[NB];
+  auto fetch_pages = [&](int r) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = (r * NB + i) * NW + wave;
+      const int e = e_begin + blk * ppi + (lane >> a.log2_page);
+      page[i] = (blk < n_blocks && e < e_end) ? sel_bg[e] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      phys[i] = -1;
+      if (page[i] >= 0 && page[i] < NP) phys[i] = bt[page[i]];
+    }
+  };
+  fetch_pages(0);
+
+  {  // the group's queries, widened to float32 (G * head_dim / 256 loads per thread, all in flight)
+    constexpr int QL = (G * kHeadDim + 255) / 256;
+    const T *qg = q + ((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim;
+    T qv[QL];
+#pragma unroll
+    for (int u = 0; u < QL; ++u) {
+      const int i = u * 256 + threadIdx.x;
+      if (i < G * kHeadDim) qv[u] = qg[i];
+    }
+#pragma unroll
+    for (int u = 0; u < QL; ++u) {
+      const int i = u * 256 + threadIdx.x;
+      if (i < G * kHeadDim) q_lds[i / kHeadDim][i % kHeadDim] = to_f32(qv[u]);
+    }
+  }
+  __syncthreads();
+
   const int64_t head_page0 = (int64_t)g * a.num_phys;
   const int64_t kpage_bytes = (int64_t)NKC * a.page_size * 16;
   const int64_t zpage_bytes = (int64_t)NVC * a.page_size * 16;
+  const int64_t chunk_stride = (int64_t)a.page_size * 16;
 
-  // latent-phase lane roles: chunk c of tokens t = j * TG + tg
+  // latent-phase lane roles: chunk vc of tokens t = j * TG + tg
   const int vc = lane % NVC;
   const int tg = lane / NVC;
 
@@ -76,27 +151,45 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
     for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
   }
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int blk = it * NW + wave;
-    const int e = e_begin + blk * ppi + (lane >> a.log2_page);
-    int page = -1;
-    if (blk < n_blocks && e < e_end) page = sel_bg[e];
-    int phys = -1;
-    if (page >= 0 && page < NP) phys = bt[page];
-    const int tok = page * a.page_size + slot;
-    const bool valid = page >= 0 && page < NP && tok < L && phys >= 0 && phys < a.num_phys;
+  for (int r = 0; r < n_rounds; ++r) {
+  if (r > 0) fetch_pages(r);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if ((r * NB + i) * NW + wave >= n_blocks) break;  // wavefront-uniform
+    const int tok = page[i] * a.page_size + slot;
+    const bool valid = page[i] >= 0 && page[i] < NP && tok < L && phys[i] >= 0 &&
+                       phys[i] < a.num_phys;
+
+    // ---- gathers: this lane's Key, and the latent chunks it sums ----
+    uint4 kc[NKC];
+    if (valid) {
+      const int64_t koff = (head_page0 + phys[i]) * kpage_bytes + (int64_t)slot * 16;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kc[c] = load_chunk(kpool, koff + c * chunk_stride);
+    }
+    uint4 zc[NJ];
+    bool zv[NJ];
+    auto gather_latents = [&]() {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t = j * TG + tg;
+        const bool role = tg < TG && t < kWave;
+        const int src = role ? t : 0;
+        const int phys_t = __shfl(phys[i], src);
+        const int valid_t = __shfl((int)valid, src);
+        zv[j] = role && valid_t;
+        if (zv[j])
+          zc[j] = load_chunk(zpool, (head_page0 + phys_t) * zpage_bytes + vc * chunk_stride +
+                                        (int64_t)(src & (a.page_size - 1)) * 16);
+      }
+    };
+    if (!kZLate) gather_latents();
 
     // ---- exact scores, one token per lane ----
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-    int64_t zoff = -1;
     if (valid) {
-      const int64_t koff = (head_page0 + phys) * kpage_bytes + (int64_t)slot * 16;
-      zoff = (head_page0 + phys) * zpage_bytes + (int64_t)slot * 16;
-      uint4 kc[NKC];
-#pragma unroll
-      for (int c = 0; c < NKC; ++c) kc[c] = load_chunk(kpool, koff + (int64_t)c * a.page_size * 16);
       float dot[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) dot[h] = 0.f;
@@ -105,26 +198,27 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
         float x[CE];
         unpack_chunk<T>(kc[c], x);
 #pragma unroll
-        for (int ee = 0; ee < CE; ++ee) {
-          const int d = c * CE + ee;
+        for (int h = 0; h < G; ++h) {
+          float qv[CE];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float qv;
-            if constexpr (CE == 8) {
-              const uint32_t w = q32[(qrow0 + (int64_t)h * kHeadDim + d) >> 1];
-              qv = (d & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-            } else {
-              qv = reinterpret_cast<const float *>(q)[qrow0 + (int64_t)h * kHeadDim + d];
-            }
-            dot[h] = fmaf(qv, x[ee], dot[h]);
+          for (int ii = 0; ii < CE; ii += 4) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&q_lds[h][c * CE + ii]);
+            qv[ii] = q4.x;
+            qv[ii + 1] = q4.y;
+            qv[ii + 2] = q4.z;
+            qv[ii + 3] = q4.w;
           }
+#pragma unroll
+          for (int ee = 0; ee < CE; ++ee) dot[h] = fmaf(qv[ee], x[ee], dot[h]);
         }
+        if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted query reads
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = dot[h] * a.scale_log2;
     }
+    if (kZLate) gather_latents();
 
-    // ---- online softmax update (wave-uniform running max per head) ----
+    // ---- online softmax update (wavefront-uniform running max per head) ----
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float bm = wave_max(s[h]);
@@ -138,40 +232,33 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
       l_lane[h] = l_lane[h] * alpha + pr;
 #pragma unroll
       for (int ee = 0; ee < CE; ++ee) acc[h][ee] *= alpha;
-      p_lds[wave][lane][h] = pr;
+      p_lds[wave][h][lane] = pr;
     }
-    zoff_lds[wave][lane] = zoff;
-    __syncthreads();
+    wave_lds_sync();
 
-    // ---- latent weighted sum: lane (tg, vc) takes chunk vc of tokens j*TG + tg ----
-    if (tg < TG) {
-      uint4 zc[NJ];
-      int64_t zo[NJ];
+    // ---- latent weighted sum ----
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < NJ; ++j) {
+      if (zv[j]) {
         const int t = j * TG + tg;
-        zo[j] = (t < kWave) ? zoff_lds[wave][t] : -1;
-        if (zo[j] >= 0) zc[j] = load_chunk(zpool, zo[j] + (int64_t)vc * a.page_size * 16);
-      }
+        float x[CE];
+        unpack_chunk<T>(zc[j], x);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int t = j * TG + tg;
-        if (zo[j] >= 0) {
-          float x[CE];
-          unpack_chunk<T>(zc[j], x);
+        for (int h = 0; h < G; ++h) {
+          const float pr = p_lds[wave][h][t];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pr = p_lds[wave][t][h];
-#pragma unroll
-            for (int ee = 0; ee < CE; ++ee) acc[h][ee] = fmaf(pr, x[ee], acc[h][ee]);
-          }
+          for (int ee = 0; ee < CE; ++ee) acc[h][ee] = fmaf(pr, x[ee], acc[h][ee]);
         }
       }
+      if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted probability reads
     }
-    __syncthreads();
+    wave_lds_sync();
+    // keep the next block's gathers from being hoisted into this one (registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
   }
 
-  // ---- merge: token groups of each wavefront, then the wavefronts ----
+  // ---- merge inside the wavefront: token groups in a fixed order ----
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float lw = wave_sum(l_lane[h]);
@@ -181,7 +268,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
     }
   }
   for (int i = lane; i < G * RV; i += kWave) u_lds[wave][i / RV][i % RV] = 0.f;
-  __syncthreads();
+  wave_lds_sync();
   for (int t = 0; t < TG; ++t) {
     if (tg == t) {
 #pragma unroll
@@ -189,8 +276,11 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
 #pragma unroll
         for (int ee = 0; ee < CE; ++ee) u_lds[wave][h][vc * CE + ee] += acc[h][ee];
     }
-    __syncthreads();
+    wave_lds_sync();
   }
+  __syncthreads();
+
+  // ---- merge the wavefronts; write u (one split) or this split's record ----
   const int rec = RV + 2;
   for (int i = threadIdx.x; i < G * RV; i += blockDim.x) {
     const int h = i / RV, d = i % RV;
@@ -206,32 +296,53 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
         usum = fmaf(u_lds[w][h][d], f, usum);
       }
     }
-    float *rp = part + (((int64_t)b * a.n_q + (int64_t)g * G + h) * a.n_split + split) * rec;
-    rp[2 + d] = usum;
-    if (d == 0) {
-      rp[0] = M;
-      rp[1] = lsum;
+    const int64_t row = (int64_t)b * a.n_q + (int64_t)g * G + h;
+    if (a.n_split == 1) {
+      u_out[row * RV + d] = lsum > 0.f ? usum / lsum : 0.f;
+    } else {
+      float *rp = part + (row * a.n_split + split) * rec;
+      rp[2 + d] = usum;
+      if (d == 0) {
+        rp[0] = M;
+        rp[1] = lsum;
+      }
     }
   }
 }
 
-// Merge of the split partials: u = sum_s u_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// grid (n_q, batch), 128 threads; a head with no valid token gets u = 0.
-__global__ __launch_bounds__(128) void attend_combine_kernel(const float *__restrict__ part,
+// Merge of the split partials of one (sequence, head), staged in LDS:
+//   u = sum_s u_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
+// summed in split order; a head with no valid token gets u = 0.
+// grid (n_q, batch), 256 threads, dynamic LDS n_split * (r_v + 2) floats.
+__global__ __launch_bounds__(256) void attend_combine_kernel(const float *__restrict__ part,
                                                              float *__restrict__ u, int n_q,
                                                              int rv, int n_split) {
+  extern __shared__ float recs[];
   const int h = blockIdx.x, b = blockIdx.y;
   const int rec = rv + 2;
   const float *base = part + ((int64_t)b * n_q + h) * n_split * rec;
+  const int n = n_split * rec;  // <= kMaxSplits * (128 + 2) < 256 * 36
+  float v[36];
+#pragma unroll
+  for (int u = 0; u < 36; ++u) {
+    const int i = u * 256 + threadIdx.x;
+    if (i < n) v[u] = base[i];
+  }
+#pragma unroll
+  for (int u = 0; u < 36; ++u) {
+    const int i = u * 256 + threadIdx.x;
+    if (i < n) recs[i] = v[u];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * rec]);
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, recs[s * rec]);
   for (int d = threadIdx.x; d < rv; d += blockDim.x) {
     float lsum = 0.f, usum = 0.f;
     if (M != -INFINITY) {
       for (int s = 0; s < n_split; ++s) {
-        const float f = exp2f(base[s * rec] - M);
-        lsum = fmaf(base[s * rec + 1], f, lsum);
-        usum = fmaf(base[s * rec + 2 + d], f, usum);
+        const float f = exp2f(recs[s * rec] - M);
+        lsum = fmaf(recs[s * rec + 1], f, lsum);
+        usum = fmaf(recs[s * rec + 2 + d], f, usum);
       }
     }
     u[((int64_t)b * n_q + h) * rv + d] = lsum > 0.f ? usum / lsum : 0.f;
@@ -265,11 +376,28 @@ static int ilog2i(int x) {
   return l;
 }
 
-// Pages per split: 4 wavefronts x one 64-token block each.
-static int pages_per_split(const basiskv_dims &d) { return 4 * (64 / d.page_size); }
+// Pages per split.  Every wavefront takes up to kAttendBlocks 64-token blocks
+// per round; a split is one round when there is work enough for about two
+// workgroups per compute unit at that size, otherwise one block per
+// wavefront (more, smaller workgroups).  A split grows by whole rounds when
+// that would leave more than kMaxSplits splits (the kernel loops over them).
+static int pages_per_split(const basiskv_dims &d, int32_t top_k) {
+  const int ppi = 64 / d.page_size;
+  const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * (((int64_t)top_k + ppi - 1) / ppi);
+  const int per_wave = blocks >= (int64_t)kAttendWaves * kAttendBlocks * 512 ? kAttendBlocks : 1;
+  const int per_round = kAttendWaves * per_wave * ppi;
+  int rounds = 1;
+  const int64_t need = ((int64_t)top_k + kMaxSplits - 1) / kMaxSplits;
+  if (need > per_round) {
+    const int full = kAttendWaves * kAttendBlocks * ppi;  // several rounds: full rounds
+    rounds = (int)((need + full - 1) / full);
+    return full * rounds;
+  }
+  return per_round;
+}
 
 int attend_splits(const basiskv_dims &d, int32_t top_k) {
-  const int pps = pages_per_split(d);
+  const int pps = pages_per_split(d, top_k);
   return (top_k + pps - 1) / pps;
 }
 
@@ -300,17 +428,18 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.log2_page = ilog2i(d.page_size);
   a.cap = d.max_pages_per_seq * d.page_size;
   a.top_k = top_k;
-  a.pages_per_split = pages_per_split(d);
+  a.pages_per_split = pages_per_split(d, top_k);
   a.n_split = attend_splits(d, top_k);
   a.total = d.batch * d.n_kv_heads * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
   a.scale_log2 = scale * kLog2e;
-  void *args[] = {(void *)&q,          (void *)&c.k_pages, (void *)&c.z_pages,
+  void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
-                  (void *)&part,       (void *)&a};
+                  (void *)&part,        (void *)&u,          (void *)&a};
   hipError_t e = hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(d.n_q_heads, d.batch), dim3(128), 0, s, part, u,
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const size_t lds = (size_t)a.n_split * (d.r_v + 2) * sizeof(float);
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(d.n_q_heads, d.batch), dim3(256), lds, s, part, u,
                      d.n_q_heads, d.r_v, a.n_split);
   return hipGetLastError();
 }

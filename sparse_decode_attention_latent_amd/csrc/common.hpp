@@ -64,16 +64,57 @@ __device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte
   return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+// Cross-lane steps through DPP (no LDS round trip).  Control codes of the
+// GFX9 data-parallel-primitives modifier: quad_perm [1,0,3,2] (0xB1) and
+// [2,3,0,1] (0x4E) swap neighbours at distance 1 and 2; row_half_mirror
+// (0x141) reverses each 8-lane half-row; row_mirror (0x140) reverses each
+// 16-lane row.  Applied in that order with an associative op, every lane of a
+// group of 4 / 8 / 16 ends with the group's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Maximum over aligned groups of `width` lanes (1, 2, 4, 8, 16, 32 or 64;
+// wave-uniform); every lane of a group receives the group's maximum.
+__device__ __forceinline__ float group_max(float v, int width) {
+  if (width >= 2) v = fmaxf(v, dpp_move<0xB1>(v));
+  if (width >= 4) v = fmaxf(v, dpp_move<0x4E>(v));
+  if (width >= 8) v = fmaxf(v, dpp_move<0x141>(v));
+  if (width >= 16) v = fmaxf(v, dpp_move<0x140>(v));
+  if (width >= 32) {
+    const float r0 = lane_value(v, 0), r1 = lane_value(v, 16);
+    const float r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+    if (width == 32) {
+      v = (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+    } else {
+      v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    }
+  }
   return v;
 }
 
+// Wave-wide maximum and sum; the result is wavefront-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // Work-item index of this workgroup for a 1-D grid of `padded` (multiple of 8)
@@ -108,6 +149,9 @@ hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const void 
                               hipStream_t s);
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
                        hipStream_t s);
+hipError_t launch_append(const basiskv_dims &d, const void *k, const void *v,
+                         const int32_t *start_pos, int32_t n_tokens, const void *A, const void *P,
+                         const void *E, const basiskv_cache &c, hipStream_t s);
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s);

@@ -83,46 +83,68 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
   for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (kBf) {
-    for (int ks = wave; ks < n_steps; ks += kReconWaves) {
-      const int k = ks * MF::KS + qg * 8;
-      uint4 braw = make_uint4(0, 0, 0, 0);
-      if (n < N && k < K) braw = *reinterpret_cast<const uint4 *>(M + (int64_t)n * K + k);
-      const bf16x8 bfrag = bits_to_frag(braw);
+    // U k-steps per round: every load of the round is issued before the first MFMA
+    constexpr int U = 8 / RT;
+    for (int ks0 = wave; ks0 < n_steps; ks0 += kReconWaves * U) {
+      uint4 braw[U];
+      float4 ux[U][RT][2];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int b = rt * ROWS + (i & 7);
-        float x[8];
-        if (b < batch && k < K) {
-          const float4 *up = reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
-          const float4 x0 = up[0], x1 = up[1];
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        } else {
+      for (int uu = 0; uu < U; ++uu) {
+        const int k = (ks0 + uu * kReconWaves) * MF::KS + qg * 8;
+        braw[uu] = make_uint4(0, 0, 0, 0);
+        if (n < N && k < K) braw[uu] = *reinterpret_cast<const uint4 *>(M + (int64_t)n * K + k);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        for (int rt = 0; rt < RT; ++rt) {
+          const int b = rt * ROWS + (i & 7);
+          ux[uu][rt][0] = ux[uu][rt][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (b < batch && k < K) {
+            const float4 *up = reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
+            ux[uu][rt][0] = up[0];
+            ux[uu][rt][1] = up[1];
+          }
         }
-        bf16x8 hi, lo;
-        split_bf16(x, &hi, &lo);
-        acc[rt] = MF::mma(i < 8 ? hi : lo, bfrag, acc[rt]);
+      }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const bf16x8 bfrag = bits_to_frag(braw[uu]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float4 x0 = ux[uu][rt][0], x1 = ux[uu][rt][1];
+          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          bf16x8 hi, lo;
+          split_bf16(x, &hi, &lo);
+          acc[rt] = MF::mma(i < 8 ? hi : lo, bfrag, acc[rt]);
+        }
       }
     }
   } else {
     // float32: each lane loads 4 consecutive k and feeds 4 MFMAs (k slot (qg, s) -> k0 + 4 qg + s)
+    constexpr int U = 8 / RT;
     const int n_quads = (K + 15) / 16;
-    for (int kq = wave; kq < n_quads; kq += kReconWaves) {
-      const int k = kq * 16 + qg * 4;
-      float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (n < N && k < K) bq = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(M) + (int64_t)n * K + k);
+    for (int kq0 = wave; kq0 < n_quads; kq0 += kReconWaves * U) {
+      float4 bq[U], aq[U][RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int b = rt * ROWS + i;
-        float4 aq = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (b < batch && k < K) aq = *reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
-        acc[rt] = MF::mma(aq.x, bq.x, acc[rt]);
-        acc[rt] = MF::mma(aq.y, bq.y, acc[rt]);
-        acc[rt] = MF::mma(aq.z, bq.z, acc[rt]);
-        acc[rt] = MF::mma(aq.w, bq.w, acc[rt]);
+      for (int uu = 0; uu < U; ++uu) {
+        const int k = (kq0 + uu * kReconWaves) * 16 + qg * 4;
+        bq[uu] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (n < N && k < K)
+          bq[uu] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(M) + (int64_t)n * K + k);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int b = rt * ROWS + i;
+          aq[uu][rt] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (b < batch && k < K) aq[uu][rt] = *reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
+        }
       }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt] = MF::mma(aq[uu][rt].x, bq[uu].x, acc[rt]);
+          acc[rt] = MF::mma(aq[uu][rt].y, bq[uu].y, acc[rt]);
+          acc[rt] = MF::mma(aq[uu][rt].z, bq[uu].z, acc[rt]);
+          acc[rt] = MF::mma(aq[uu][rt].w, bq[uu].w, acc[rt]);
+        }
     }
   }
 #pragma unroll
@@ -425,9 +447,11 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   a.page_size = d.page_size;
   a.cap = d.max_pages_per_seq * d.page_size;
   const size_t lds = compress_lds_bytes<T>(d, a.rb_pad);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compress_kernel<T>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compress_kernel<T>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int rows = d.batch * n_tokens;
   const int n_blocks = (rows + 15) / 16;
   int wgs = (n_blocks + 3) / 4;
@@ -438,9 +462,14 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   return hipGetLastError();
 }
 
+// Few rows per head (the decode append): matrix-vector kernel; otherwise MFMA.
+constexpr int kAppendMaxRows = 64;
+
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s) {
+  if ((int64_t)d.batch * n_tokens <= kAppendMaxRows && d.r_v <= kHeadDim && d.r_q <= kHeadDim)
+    return launch_append(d, k, v, start_pos, n_tokens, A, P, E, c, s);
   return d.dtype == BASISKV_BF16 ? compress_t<uint16_t>(d, k, v, start_pos, n_tokens, A, P, E, c, s)
                                  : compress_t<float>(d, k, v, start_pos, n_tokens, A, P, E, c, s);
 }

@@ -9,37 +9,55 @@ namespace bkv {
 
 // ---------------------------------------------------------------------------
 // (a1) q_proj[b][h] = [P_g q_bh, Q_g q_bh]   (float32, exact widening of inputs)
-// grid (n_kv, batch), 256 threads.
+// grid (ceil(G * (r_b + r_q) / 128), n_kv, batch), 128 threads: one output per
+// thread; its whole factor row (head_dim elements) is requested before the
+// queries are staged, so the two loads overlap.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void project_queries_kernel(
+__global__ __launch_bounds__(128) void project_queries_kernel(
     const T *__restrict__ q, const T *__restrict__ P, const T *__restrict__ Q,
     float *__restrict__ q_proj, int n_q, int n_kv, int rb, int rq) {
   constexpr int CE = Elem<T>::CE;
   constexpr int NC = kHeadDim / CE;
-  __shared__ float qs[16][kHeadDim];
-  const int g = blockIdx.x, b = blockIdx.y;
+  __shared__ __align__(16) float qs[16][kHeadDim];
+  const int g = blockIdx.y, b = blockIdx.z;
   const int G = n_q / n_kv;
   const int w = rb + rq;
-  for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
-    const int h = i / kHeadDim, d = i % kHeadDim;
-    qs[h][d] = to_f32(q[((int64_t)b * n_q + g * G + h) * kHeadDim + d]);
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = o < G * w;
+  const int h = active ? o / w : 0, j = active ? o % w : 0;
+  const T *row = j < rb ? P + ((int64_t)g * rb + j) * kHeadDim
+                        : Q + ((int64_t)g * rq + (j - rb)) * kHeadDim;
+  uint4 c[NC];
+  if (active) {  // the factor row is in flight while the queries are staged
+#pragma unroll
+    for (int i = 0; i < NC; ++i) c[i] = reinterpret_cast<const uint4 *>(row)[i];
+  }
+  {  // the group's queries: G * head_dim elements, 128 threads, one batch of loads
+    const T *qg = q + ((int64_t)b * n_q + g * G) * kHeadDim;
+    T qv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = u * 128 + threadIdx.x;
+      if (i < G * kHeadDim) qv[u] = qg[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = u * 128 + threadIdx.x;
+      if (i < G * kHeadDim) qs[i / kHeadDim][i % kHeadDim] = to_f32(qv[u]);
+    }
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < G * w; o += blockDim.x) {
-    const int h = o / w, j = o % w;
-    const T *row = j < rb ? P + ((int64_t)g * rb + j) * kHeadDim
-                          : Q + ((int64_t)g * rq + (j - rb)) * kHeadDim;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < NC; ++c) {
-      float x[CE];
-      unpack_chunk<T>(reinterpret_cast<const uint4 *>(row)[c], x);
+  if (!active) return;
+  float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < CE; ++e) acc = fmaf(x[e], qs[h][c * CE + e], acc);
-    }
-    q_proj[((int64_t)b * n_q + g * G + h) * w + j] = acc;
+  for (int i = 0; i < NC; ++i) {
+    float x[CE];
+    unpack_chunk<T>(c[i], x);
+#pragma unroll
+    for (int e = 0; e < CE; ++e) acc = fmaf(x[e], qs[h][i * CE + e], acc);
   }
+  q_proj[((int64_t)b * n_q + g * G + h) * w + j] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -53,6 +71,11 @@ __global__ __launch_bounds__(256) void project_queries_kernel(
 // so every FMA takes one scalar and one vector operand.  Page maxima are
 // butterfly reductions over the page's lanes.
 // ---------------------------------------------------------------------------
+#ifndef BKV_ROUTE_STEPS
+#define BKV_ROUTE_STEPS 4
+#endif
+constexpr int kRouteSteps = BKV_ROUTE_STEPS;
+
 struct ScoreArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, zc_total, cap;
   int pages_per_wg, chunks_per_bg, total, padded;
@@ -129,16 +152,18 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h) best = fmaxf(best, acc[h]);
     }
-    for (int off = a.page_size >> 1; off >= 1; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    best = group_max(best, a.page_size);
     if (in_range && slot == 0) out[p] = (p < NP) ? best : -INFINITY;
   }
 }
 
 // ---------------------------------------------------------------------------
-// (a3) exact top-k per (sequence, KV head): radix select on order-preserving
-// 32-bit keys (8-bit digits, 4 passes, LDS histograms, a wavefront suffix
-// scan to find each digit), then an index-ordered compaction that takes every
-// key above the threshold and the lowest-index keys equal to it.
+// (a3) exact top-k per (sequence, KV head).  Scores become order-preserving
+// 32-bit keys in LDS.  The k-th largest key tau is built two bits at a time
+// from the top: of the candidates tau | d << shift, the largest that at least
+// k keys reach is kept (counts by wavefront ballots, one barrier per round,
+// no atomics).  The compaction then takes, in index order, every key above
+// tau and the lowest-index keys equal to it.
 // grid (n_kv, batch), 256 threads, dynamic LDS = max_pages * 4 bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -147,21 +172,23 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the 256 threads of the block; returns the total via *total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total) {
+// Exclusive prefix sum over the 256 threads of the block (unsigned, so two
+// 16-bit counts may share one word); returns the total via *total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  uint32_t incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(incl, off);
+    const uint32_t t = __shfl_up(incl, off);
     if (lane >= off) incl += t;
   }
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  int base = 0, tot = 0;
+  uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const int s = scratch[w];
+    const uint32_t s = scratch[w];
     if (w < wave) base += s;
     tot += s;
   }
@@ -174,9 +201,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k) {
   extern __shared__ uint32_t keys[];
-  __shared__ int hist[256];
-  __shared__ int scan_scratch[4];
-  __shared__ int found[2];
+  __shared__ int counts[2][4][3];
+  __shared__ uint32_t scan_scratch[4];
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int L = clamp_len(seq_lens[b], cap);
@@ -187,64 +213,70 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
     return;
   }
   const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
-  for (int i = tid; i < NP; i += 256) keys[i] = order_key(row[i]);
+  for (int i0 = 0; i0 < NP; i0 += 256 * 16) {  // 16 loads per thread in flight
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * 256 + tid;
+      v[u] = i < NP ? row[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < NP) keys[i] = order_key(v[u]);
+    }
+  }
   __syncthreads();
 
-  uint32_t prefix = 0, mask = 0;
-  int need = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < NP; i += 256) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+  // two bits per round: counts of keys reaching the three candidates
+  // tau | d << shift (d = 1, 2, 3), one ballot per candidate and 64 keys
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t tau = 0;
+  int buf = 0;
+  for (int shift = 30; shift >= 0; shift -= 2, buf ^= 1) {
+    const uint32_t c1 = tau | (1u << shift), c2 = tau | (2u << shift), c3 = tau | (3u << shift);
+    int n1 = 0, n2 = 0, n3 = 0;
+    for (int i0 = wave * 64; i0 < NP; i0 += 256) {  // wavefront-uniform trip count
+      const int i = i0 + lane;
+      const uint32_t key = i < NP ? keys[i] : 0u;  // 0 reaches no candidate (all >= 1)
+      n1 += __popcll(__ballot(key >= c1));
+      n2 += __popcll(__ballot(key >= c2));
+      n3 += __popcll(__ballot(key >= c3));
+    }
+    if (lane == 0) {
+      counts[buf][wave][0] = n1;
+      counts[buf][wave][1] = n2;
+      counts[buf][wave][2] = n3;
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      int c[4], s = 0;
+    int t1 = 0, t2 = 0, t3 = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * tid - j];
-        s += c[j];
-      }
-      int incl = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        int t = __shfl_up(incl, off);
-        if (tid >= off) incl += t;
-      }
-      int run = incl - s;  // keys with a larger digit than this lane's first
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run < need && run + c[j] >= need) {
-          found[0] = 255 - 4 * tid - j;
-          found[1] = run;
-        }
-        run += c[j];
-      }
+    for (int w = 0; w < 4; ++w) {
+      t1 += counts[buf][w][0];
+      t2 += counts[buf][w][1];
+      t3 += counts[buf][w][2];
     }
-    __syncthreads();
-    prefix |= (uint32_t)found[0] << shift;
-    mask |= 255u << shift;
-    need -= found[1];
-    __syncthreads();
+    const uint32_t dg = t3 >= k ? 3u : t2 >= k ? 2u : t1 >= k ? 1u : 0u;
+    tau |= dg << shift;
   }
-  const uint32_t tau = prefix;  // the k-th largest key; `need` keys equal to it are taken
+  // tau is the k-th largest key: at least k keys reach it, fewer than k exceed it
 
   const int per = (NP + 255) / 256;
   const int i0 = min(NP, tid * per), i1 = min(NP, i0 + per);
-  int n_gt = 0, n_eq = 0;
+  uint32_t n_gt = 0, n_eq = 0;
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = keys[i];
     n_gt += key > tau;
     n_eq += key == tau;
   }
-  int total;
-  const int eq_before = block_exclusive_scan(n_eq, scan_scratch, &total);
-  const int take_eq = max(0, min(n_eq, need - eq_before));
-  const int n_sel = n_gt + take_eq;
-  int pos = block_exclusive_scan(n_sel, scan_scratch, &total);
+  // one scan of both counts: each total is < 65536 (NP <= 32768 < k + NP), so
+  // the low half never carries into the high half
+  uint32_t total;
+  const uint32_t packed = block_exclusive_scan(n_gt | (n_eq << 16), scan_scratch, &total);
+  const int need = k - (int)(total & 0xffffu);  // keys equal to tau still to take
+  const int eq_before = (int)(packed >> 16);
+  const int take_eq = max(0, min((int)n_eq, need - eq_before));
+  int pos = (int)(packed & 0xffffu) + min(eq_before, need);
   int taken = 0;
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = keys[i];
@@ -258,7 +290,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
 template <typename T>
 hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                      float *q_proj, hipStream_t s) {
-  hipLaunchKernelGGL(project_queries_kernel<T>, dim3(d.n_kv_heads, d.batch), dim3(256), 0, s,
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int outs = G * (d.r_b + d.r_q);
+  hipLaunchKernelGGL(project_queries_kernel<T>, dim3((outs + 127) / 128, d.n_kv_heads, d.batch),
+                     dim3(128), 0, s,
                      (const T *)q, (const T *)P, (const T *)Q, q_proj, d.n_q_heads, d.n_kv_heads,
                      d.r_b, d.r_q);
   return hipGetLastError();
@@ -330,9 +365,9 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   a.log2_page = ilog2(d.page_size);
   a.zc_total = d.r_v / ce;
   a.cap = d.max_pages_per_seq * d.page_size;
-  // 4 wavefronts per workgroup, each streaming 4 steps of 64 tokens.
+  // 4 wavefronts per workgroup, each streaming kRouteSteps steps of 64 tokens.
   const int ppi = 64 / d.page_size;
-  a.pages_per_wg = ppi * 16;
+  a.pages_per_wg = ppi * 4 * kRouteSteps;
   a.chunks_per_bg = (d.max_pages_per_seq + a.pages_per_wg - 1) / a.pages_per_wg;
   a.total = d.batch * d.n_kv_heads * a.chunks_per_bg;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
