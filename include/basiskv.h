@@ -94,8 +94,14 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char *basiskv_status_string(int32_t status);
 
-/* Bytes of workspace that basiskv_route_pages and basiskv_sparse_attend need
- * for these dims and top_k (the maximum of the two).  0 if dims are invalid. */
+/* Bytes of workspace that basiskv_route_pages, basiskv_sparse_attend and
+ * basiskv_decode_step need for these dims and top_k; one buffer of this size
+ * serves all three.  0 if dims are invalid.
+ * The workspace is device memory owned by the caller.  It must be zero-filled
+ * once after allocation: it holds small integer counters with which the
+ * workgroups of the attention launch elect the one that merges a (sequence,
+ * KV head) row's splits, and every call leaves them at zero again.  Calls
+ * that share one workspace must not run concurrently. */
 size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t top_k);
 
 /* (a0) Compress new tokens into the cache -- BasisKV abstract (Value kept
@@ -145,7 +151,8 @@ int32_t basiskv_select_pages(const basiskv_dims *dims, const float *page_scores,
                              const int32_t *seq_lens, int32_t top_k, int32_t *sel,
                              void *stream);
 
-/* (a1)+(a2)+(a3) in one call; q_proj lives in the workspace. */
+/* (a1)+(a2)+(a3) in one call: projection, scoring and selection launches;
+ * q_proj lives in the workspace. */
 int32_t basiskv_route_pages(const basiskv_dims *dims, const void *q, const void *P,
                             const void *Q, const basiskv_cache *cache, int32_t top_k,
                             float *page_scores, int32_t *sel, void *workspace,
@@ -160,7 +167,9 @@ int32_t basiskv_route_pages(const basiskv_dims *dims, const void *q, const void 
  * Entries of sel that are -1 or outside the sequence are skipped; a head with
  * no valid token gets u = 0.  scale is usually 1/sqrt(head_dim).
  *   q [batch][n_q_heads][head_dim]; sel [batch][n_kv_heads][top_k];
- *   u [batch][n_q_heads][r_v] float32 out. */
+ *   u [batch][n_q_heads][r_v] float32 out.
+ * The workspace (see basiskv_workspace_bytes) holds the per-split partial
+ * results and the counters that elect the workgroup merging them. */
 int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
                               const basiskv_cache *cache, const int32_t *sel, int32_t top_k,
                               float scale, float *u, void *workspace, size_t workspace_bytes,
@@ -172,9 +181,27 @@ int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
  * two bf16 terms (hi + lo) so no precision is lost before the product.
  *   u [batch][n_q_heads * r_v] float32;  M [hidden][n_q_heads * r_v] (row n of
  *   M holds output feature n);  y [batch][hidden] out, in dtype.
- * batch must be <= 64. */
+ * batch must be <= 32 for bf16 and <= 64 for float32 (ERR_UNSUPPORTED). */
 int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void *M, void *y,
                             void *stream);
+
+/* A whole decode step of one layer in one call, with the same results as
+ *   basiskv_compress_prefill(k_new, v_new, start_pos, n_tokens = 1),
+ *   basiskv_route_pages, basiskv_sparse_attend, basiskv_reconstruct
+ * in that order (the compression and the query projection share one launch;
+ * five launches in all, stream-ordered, no host synchronisation).
+ *   k_new, v_new [batch][n_kv_heads][head_dim]: the step's new token of every
+ *     sequence, written at position start_pos[b] (device int32 [batch]);
+ *     seq_lens must already count it.
+ *   q, P, Q, A, E, M, top_k, scale, page_scores, sel, u, y: as in the calls
+ *     above.  Needs r_v, r_q <= 128 and the batch limit of basiskv_reconstruct.
+ *   workspace: see basiskv_workspace_bytes. */
+int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void *k_new,
+                            const void *v_new, const int32_t *start_pos, const void *A,
+                            const void *P, const void *Q, const void *E, const void *M,
+                            const basiskv_cache *cache, int32_t top_k, float scale,
+                            float *page_scores, int32_t *sel, float *u, void *y,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Set-up: fuse the Value decoder into the output projection,
  *   M[n][h * r_v + i] = sum_d Bf[h / G][i][d] * W_O[h * head_dim + d][n],

@@ -21,7 +21,7 @@ EXPORTED = (
     "basiskv_status_string", "basiskv_workspace_bytes", "basiskv_compress_prefill",
     "basiskv_project_queries", "basiskv_score_pages", "basiskv_select_pages",
     "basiskv_route_pages", "basiskv_sparse_attend", "basiskv_reconstruct",
-    "basiskv_fuse_output_matrix",
+    "basiskv_decode_step", "basiskv_fuse_output_matrix",
 )
 
 
@@ -65,6 +65,8 @@ def _lib():
             "basiskv_route_pages": (I32, [DP, P, P, P, CP, I32, P, P, P, SZ, P]),
             "basiskv_sparse_attend": (I32, [DP, P, CP, P, I32, ctypes.c_float, P, P, SZ, P]),
             "basiskv_reconstruct": (I32, [DP, P, P, P, P]),
+            "basiskv_decode_step": (I32, [DP, P, P, P, P, P, P, P, P, P, CP, I32, ctypes.c_float,
+                                          P, P, P, P, P, SZ, P]),
             "basiskv_fuse_output_matrix": (I32, [DP, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -158,6 +160,18 @@ def reconstruct(dims, u, M, y, stream=None):
     _check(_lib().basiskv_reconstruct(ctypes.byref(dims), _ptr(u), _ptr(M), _ptr(y),
                                       _stream(stream)),
            "basiskv_reconstruct")
+
+
+def decode_step(dims, q, k_new, v_new, start_pos, A, P, Q, E, M, cache, top_k, scale,
+                page_scores, sel, u, y, workspace, stream=None):
+    _check(_lib().basiskv_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      _ptr(start_pos), _ptr(A), _ptr(P), _ptr(Q), _ptr(E), _ptr(M),
+                                      ctypes.byref(cache), int(top_k), float(scale),
+                                      _ptr(page_scores), _ptr(sel), _ptr(u), _ptr(y),
+                                      _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)),
+           "basiskv_decode_step")
 
 
 def fuse_output_matrix(dims, Bf, W_O, M, stream=None):

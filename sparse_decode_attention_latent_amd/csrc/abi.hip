@@ -48,13 +48,29 @@ int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_
 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace layout:
+//   [0, C)   per-(sequence, KV head) counters with which the attention
+//            launch elects the workgroup that merges a row's splits; zero
+//            after allocation, and every call leaves them zero
+//   [C, ..)  scratch: the projected queries during routing, then the
+//            attention splits' partial records (stream order keeps the two
+//            uses apart)
+size_t counter_bytes(const basiskv_dims &d) {
+  return align_up((size_t)d.batch * d.n_kv_heads * sizeof(int32_t));
+}
+
 size_t qproj_bytes(const basiskv_dims &d) {
   return align_up((size_t)d.batch * d.n_q_heads * (d.r_b + d.r_q) * sizeof(float));
 }
 
-size_t attend_ws_bytes(const basiskv_dims &d, int32_t top_k) {
+size_t partial_bytes(const basiskv_dims &d, int32_t top_k) {
   const int ns = bkv_host::attend_splits(d, top_k);
   return align_up((size_t)d.batch * d.n_q_heads * ns * (d.r_v + 2) * sizeof(float));
+}
+
+int32_t *attend_counters(void *ws) { return static_cast<int32_t *>(ws); }
+float *scratch(void *ws, const basiskv_dims &d) {
+  return reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes(d));
 }
 
 int32_t launched(hipError_t e) { return e == hipSuccess ? BASISKV_OK : BASISKV_ERR_LAUNCH; }
@@ -79,8 +95,8 @@ const char *basiskv_status_string(int32_t status) {
 
 size_t basiskv_workspace_bytes(const basiskv_dims *d, int32_t top_k) {
   if (check_dims(d) != BASISKV_OK || top_k < 1) return 0;
-  const size_t a = qproj_bytes(*d), b = attend_ws_bytes(*d, top_k);
-  return a > b ? a : b;
+  const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
+  return counter_bytes(*d) + (a > b ? a : b);
 }
 
 int32_t basiskv_compress_prefill(const basiskv_dims *d, const void *k, const void *v,
@@ -115,7 +131,8 @@ int32_t basiskv_score_pages(const basiskv_dims *d, const float *q_proj, const ba
   if ((st = check_cache(c, false, true, true))) return st;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   bool unsupported = false;
-  hipError_t e = bkv_host::launch_score(*d, q_proj, *c, page_scores, as_stream(stream), &unsupported);
+  hipError_t e = bkv_host::launch_score(*d, q_proj, *c, page_scores, as_stream(stream),
+                                        &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
   return launched(e);
 }
@@ -137,9 +154,9 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
   if (!q || !P || !Q || !page_scores || !sel) return BASISKV_ERR_NULL;
   if ((st = check_cache(c, false, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
-  if (!ws || ws_bytes < qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
+  if (!ws || ws_bytes < counter_bytes(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
-  float *q_proj = static_cast<float *>(ws);
+  float *q_proj = scratch(ws, *d);
   hipStream_t s = as_stream(stream);
   bool unsupported = false;
   hipError_t e = bkv_host::launch_project(*d, q, P, Q, q_proj, s);
@@ -158,10 +175,11 @@ int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basisk
   if ((st = check_cache(c, true, true, false))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!bkv_host::attend_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < attend_ws_bytes(*d, top_k)) return BASISKV_ERR_WORKSPACE;
+  if (!ws || ws_bytes < counter_bytes(*d) + partial_bytes(*d, top_k))
+    return BASISKV_ERR_WORKSPACE;
   bool unsupported = false;
-  hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, static_cast<float *>(ws),
-                                         as_stream(stream), &unsupported);
+  hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scratch(ws, *d),
+                                         attend_counters(ws), as_stream(stream), &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
   return launched(e);
 }
@@ -173,6 +191,42 @@ int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M
   if (!u || !M || !y) return BASISKV_ERR_NULL;
   if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
   return launched(bkv_host::launch_reconstruct(*d, u, M, y, as_stream(stream)));
+}
+
+int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
+                            const void *v_new, const int32_t *start_pos, const void *A,
+                            const void *P, const void *Q, const void *E, const void *M,
+                            const basiskv_cache *c, int32_t top_k, float scale,
+                            float *page_scores, int32_t *sel, float *u, void *y, void *ws,
+                            size_t ws_bytes, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || !k_new || !v_new || !start_pos || !A || !P || !Q || !E || !M || !page_scores ||
+      !sel || !u || !y)
+    return BASISKV_ERR_NULL;
+  if ((st = check_cache(c, true, true, true))) return st;
+  if (top_k < 1) return BASISKV_ERR_SHAPE;
+  if (d->r_v > bkv::kHeadDim || d->r_q > bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
+  if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
+    return BASISKV_ERR_UNSUPPORTED;
+  if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
+  const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
+  if (!ws || ws_bytes < counter_bytes(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  float *scr = scratch(ws, *d);
+  bool unsupported = false;
+  // (a0) + (a1) in one launch, then (a2), (a3), (a4), (a5)
+  if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr, s) !=
+      hipSuccess)
+    return BASISKV_ERR_LAUNCH;
+  hipError_t e = bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported);
+  if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
+  if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s) != hipSuccess)
+    return BASISKV_ERR_LAUNCH;
+  e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scr, attend_counters(ws), s,
+                              &unsupported);
+  if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
+  return launched(bkv_host::launch_reconstruct(*d, u, M, y, s));
 }
 
 int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const void *W_O, void *M,

@@ -19,8 +19,10 @@
 //     wavefront-private LDS row, and lane (tg, vc) accumulates chunk vc of the
 //     tokens tg, tg + TG, ... for every head of the group.
 // The wavefronts and the workgroup's splits are merged in a fixed order
-// (deterministic, no atomics).  A single split writes u directly; otherwise
-// a second kernel merges the per-split partial records.
+// (deterministic: no floating-point atomics).  A single split writes u
+// directly; otherwise every split writes a partial record and the last split
+// of the (sequence, KV head) to finish -- elected with an integer counter --
+// merges the records in split order.
 #include "common.hpp"
 
 namespace bkv {
@@ -39,6 +41,7 @@ struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
   int pages_per_split, n_split, total, padded;
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
+  int32_t *counters;  // [batch * n_kv], zero between calls (see the merge)
 };
 
 // Ordering point for LDS traffic between the lanes of one wavefront.
@@ -116,19 +119,24 @@ void attend_split_kernel(
   };
   fetch_pages(0);
 
-  {  // the group's queries, widened to float32 (G * head_dim / 256 loads per thread, all in flight)
-    constexpr int QL = (G * kHeadDim + 255) / 256;
-    const T *qg = q + ((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim;
-    T qv[QL];
+  // The group's queries: bf16 kept as packed pairs (the scores use the
+  // two-term bf16 dot instruction, products exact, float32 sums), float32 as is.
+  {
+    constexpr int QW = G * kHeadDim * (int)sizeof(T) / 4;  // 32-bit words
+    constexpr int QL = (QW + 255) / 256;
+    const uint32_t *qg = reinterpret_cast<const uint32_t *>(
+        q + ((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim);
+    uint32_t *qw = reinterpret_cast<uint32_t *>(&q_lds[0][0]);
+    uint32_t qv[QL];
 #pragma unroll
     for (int u = 0; u < QL; ++u) {
       const int i = u * 256 + threadIdx.x;
-      if (i < G * kHeadDim) qv[u] = qg[i];
+      if (i < QW) qv[u] = qg[i];
     }
 #pragma unroll
     for (int u = 0; u < QL; ++u) {
       const int i = u * 256 + threadIdx.x;
-      if (i < G * kHeadDim) q_lds[i / kHeadDim][i % kHeadDim] = to_f32(qv[u]);
+      if (i < QW) qw[i] = qv[u];
     }
   }
   __syncthreads();
@@ -195,21 +203,27 @@ void attend_split_kernel(
       for (int h = 0; h < G; ++h) dot[h] = 0.f;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
-        float x[CE];
-        unpack_chunk<T>(kc[c], x);
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t *qw = reinterpret_cast<const uint32_t *>(&q_lds[0][0]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float qv[CE];
-#pragma unroll
-          for (int ii = 0; ii < CE; ii += 4) {
-            const float4 q4 = *reinterpret_cast<const float4 *>(&q_lds[h][c * CE + ii]);
-            qv[ii] = q4.x;
-            qv[ii + 1] = q4.y;
-            qv[ii + 2] = q4.z;
-            qv[ii + 3] = q4.w;
+          for (int h = 0; h < G; ++h) {
+            const uint4 q4 = *reinterpret_cast<const uint4 *>(qw + h * (kHeadDim / 2) + c * 4);
+            dot[h] = dot2_bf16(kc[c].x, q4.x, dot[h]);
+            dot[h] = dot2_bf16(kc[c].y, q4.y, dot[h]);
+            dot[h] = dot2_bf16(kc[c].z, q4.z, dot[h]);
+            dot[h] = dot2_bf16(kc[c].w, q4.w, dot[h]);
           }
+        } else {
+          float x[CE];
+          unpack_chunk<T>(kc[c], x);
 #pragma unroll
-          for (int ee = 0; ee < CE; ++ee) dot[h] = fmaf(qv[ee], x[ee], dot[h]);
+          for (int h = 0; h < G; ++h) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&q_lds[h][c * CE]);
+            dot[h] = fmaf(q4.x, x[0], dot[h]);
+            dot[h] = fmaf(q4.y, x[1], dot[h]);
+            dot[h] = fmaf(q4.z, x[2], dot[h]);
+            dot[h] = fmaf(q4.w, x[3], dot[h]);
+          }
         }
         if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted query reads
       }
@@ -301,51 +315,54 @@ void attend_split_kernel(
       u_out[row * RV + d] = lsum > 0.f ? usum / lsum : 0.f;
     } else {
       float *rp = part + (row * a.n_split + split) * rec;
-      rp[2 + d] = usum;
+      store_coherent(rp + 2 + d, usum);
       if (d == 0) {
-        rp[0] = M;
-        rp[1] = lsum;
+        store_coherent(rp, M);
+        store_coherent(rp + 1, lsum);
       }
     }
   }
-}
+  if (a.n_split == 1) return;
 
-// Merge of the split partials of one (sequence, head), staged in LDS:
-//   u = sum_s u_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
-// summed in split order; a head with no valid token gets u = 0.
-// grid (n_q, batch), 256 threads, dynamic LDS n_split * (r_v + 2) floats.
-__global__ __launch_bounds__(256) void attend_combine_kernel(const float *__restrict__ part,
-                                                             float *__restrict__ u, int n_q,
-                                                             int rv, int n_split) {
-  extern __shared__ float recs[];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int rec = rv + 2;
-  const float *base = part + ((int64_t)b * n_q + h) * n_split * rec;
-  const int n = n_split * rec;  // <= kMaxSplits * (128 + 2) < 256 * 36
-  float v[36];
+  // ---- the last split of the (sequence, KV head) to finish merges them all ----
+  //   u = sum_s u_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
+  // in split order; a head with no valid token gets u = 0.
+  if (!last_to_arrive(a.counters + bg, a.n_split)) return;
+  constexpr int U = 8;  // records read per batch of loads
+  for (int i = threadIdx.x; i < G * RV; i += blockDim.x) {
+    const int h = i / RV, d = i % RV;
+    const int64_t row = (int64_t)b * a.n_q + (int64_t)g * G + h;
+    const float *base = part + row * a.n_split * rec;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < a.n_split; s0 += U) {
+      float m[U];
 #pragma unroll
-  for (int u = 0; u < 36; ++u) {
-    const int i = u * 256 + threadIdx.x;
-    if (i < n) v[u] = base[i];
-  }
+      for (int k = 0; k < U; ++k)
+        m[k] = s0 + k < a.n_split ? load_coherent(base + (s0 + k) * rec) : -INFINITY;
 #pragma unroll
-  for (int u = 0; u < 36; ++u) {
-    const int i = u * 256 + threadIdx.x;
-    if (i < n) recs[i] = v[u];
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, recs[s * rec]);
-  for (int d = threadIdx.x; d < rv; d += blockDim.x) {
+      for (int k = 0; k < U; ++k) M = fmaxf(M, m[k]);
+    }
     float lsum = 0.f, usum = 0.f;
     if (M != -INFINITY) {
-      for (int s = 0; s < n_split; ++s) {
-        const float f = exp2f(recs[s * rec] - M);
-        lsum = fmaf(recs[s * rec + 1], f, lsum);
-        usum = fmaf(recs[s * rec + 2 + d], f, usum);
+      for (int s0 = 0; s0 < a.n_split; s0 += U) {
+        float m[U], l[U], uu[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          const bool ok = s0 + k < a.n_split;
+          const float *r = base + (s0 + k) * rec;
+          m[k] = ok ? load_coherent(r) : -INFINITY;
+          l[k] = ok ? load_coherent(r + 1) : 0.f;
+          uu[k] = ok ? load_coherent(r + 2 + d) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          const float f = exp2f(m[k] - M);
+          lsum = fmaf(l[k], f, lsum);
+          usum = fmaf(uu[k], f, usum);
+        }
       }
     }
-    u[((int64_t)b * n_q + h) * rv + d] = lsum > 0.f ? usum / lsum : 0.f;
+    u_out[row * RV + d] = lsum > 0.f ? usum / lsum : 0.f;
   }
 }
 
@@ -412,7 +429,7 @@ bool attend_supported(const basiskv_dims &d) { return find_attend(d) != nullptr;
 
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
-                         hipStream_t s, bool *unsupported) {
+                         int32_t *counters, hipStream_t s, bool *unsupported) {
   const void *fn = find_attend(d);
   if (!fn) {
     *unsupported = true;
@@ -433,15 +450,11 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.total = d.batch * d.n_kv_heads * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
   a.scale_log2 = scale * kLog2e;
+  a.counters = counters;
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};
-  hipError_t e = hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
-  if (e != hipSuccess || a.n_split == 1) return e;
-  const size_t lds = (size_t)a.n_split * (d.r_v + 2) * sizeof(float);
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(d.n_q_heads, d.batch), dim3(256), lds, s, part, u,
-                     d.n_q_heads, d.r_v, a.n_split);
-  return hipGetLastError();
+  return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
 }
 
 }  // namespace bkv_host

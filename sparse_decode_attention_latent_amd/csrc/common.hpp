@@ -60,6 +60,14 @@ template <> __device__ __forceinline__ void unpack_chunk<uint16_t>(const uint4 &
   x[7] = __uint_as_float(c.w & 0xffff0000u);
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16:
+// the products are exact in float32; the result carries float32 rounding).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
 __device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte_off) {
   return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
 }
@@ -117,6 +125,41 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Device-coherent hand-off between the workgroups of one launch.  Results
+// that another workgroup will read are written with relaxed agent-scope
+// atomic stores (they write through to the device coherence point, so every
+// XCD's L2 sees them) and read back with relaxed agent-scope atomic loads.
+// A workgroup counts itself done only after its own stores have completed
+// (s_waitcnt vmcnt(0) in every thread, then a barrier); the workgroup whose
+// increment completes the count handles the row.  No L2 write-back or
+// invalidate is involved, which a device-scope fence would issue for every
+// workgroup.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// True in every thread of the workgroup that completes `counter` to `total`
+// arrivals; that workgroup also resets the counter to zero for the next launch.
+__device__ __forceinline__ bool last_to_arrive(int32_t *counter, int total) {
+  __shared__ int is_last;
+  wait_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == total - 1;
+    if (is_last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return is_last;
+}
+
 // Work-item index of this workgroup for a 1-D grid of `padded` (multiple of 8)
 // workgroups: consecutive work items land on the same XCD, so workgroups that
 // share per-(sequence, head) data (projected queries, block-table rows) hit
@@ -144,7 +187,7 @@ hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32
 int attend_splits(const basiskv_dims &d, int32_t top_k);
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
-                         hipStream_t s, bool *unsupported);
+                         int32_t *counters, hipStream_t s, bool *unsupported);
 hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const void *M, void *y,
                               hipStream_t s);
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
@@ -152,6 +195,10 @@ hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, v
 hipError_t launch_append(const basiskv_dims &d, const void *k, const void *v,
                          const int32_t *start_pos, int32_t n_tokens, const void *A, const void *P,
                          const void *E, const basiskv_cache &c, hipStream_t s);
+hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void *k_new,
+                                const void *v_new, const int32_t *start_pos, const void *A,
+                                const void *P, const void *Q, const void *E,
+                                const basiskv_cache &c, float *q_proj, hipStream_t s);
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s);

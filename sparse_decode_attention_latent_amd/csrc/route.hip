@@ -3,61 +3,195 @@
 // routing with a Key-specific residual; appendix Table 4's routing read widths
 // (r_b latent dims + r_q residual dims per context token); Table 9's caption
 // (routing by page, with a page budget).
-#include "common.hpp"
+#include "decode_bodies.hpp"
 
 namespace bkv {
 
 // ---------------------------------------------------------------------------
-// (a1) q_proj[b][h] = [P_g q_bh, Q_g q_bh]   (float32, exact widening of inputs)
-// grid (ceil(G * (r_b + r_q) / 128), n_kv, batch), 128 threads: one output per
-// thread; its whole factor row (head_dim elements) is requested before the
-// queries are staged, so the two loads overlap.
+// (a1) query projection launch; the body is in decode_bodies.hpp.
+// grid (ceil(G * (r_b + r_q) / 128), n_kv, batch), 128 threads.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(128) void project_queries_kernel(
     const T *__restrict__ q, const T *__restrict__ P, const T *__restrict__ Q,
     float *__restrict__ q_proj, int n_q, int n_kv, int rb, int rq) {
-  constexpr int CE = Elem<T>::CE;
-  constexpr int NC = kHeadDim / CE;
-  __shared__ __align__(16) float qs[16][kHeadDim];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int G = n_q / n_kv;
-  const int w = rb + rq;
-  const int o = blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = o < G * w;
-  const int h = active ? o / w : 0, j = active ? o % w : 0;
-  const T *row = j < rb ? P + ((int64_t)g * rb + j) * kHeadDim
-                        : Q + ((int64_t)g * rq + (j - rb)) * kHeadDim;
-  uint4 c[NC];
-  if (active) {  // the factor row is in flight while the queries are staged
+  project_body<T, 128>(q, P, Q, q_proj, n_q, n_kv, rb, rq, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// ---------------------------------------------------------------------------
+// (a3) exact top-k per (sequence, KV head).
+//
+// Scores become order-preserving 32-bit keys held in registers: lane l of
+// wavefront w owns the KPT consecutive pages starting at (64 w + l) KPT.  The
+// k-th largest key tau is built one bit at a time from the top (a candidate
+// is kept when at least k keys reach it; counts by wavefront ballots, and,
+// with several wavefronts, one LDS exchange and barrier per bit).  Bits that
+// every valid key shares -- above the highest bit in which the largest and
+// smallest keys differ -- are taken as given.  The compaction then writes, in
+// page order, every page whose key exceeds tau and the lowest-index pages
+// equal to it; lane prefix sums come from ballots of the count bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;                      // NaN ranks lowest
+  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wavefront-uniform maximum and minimum of unsigned values.
+__device__ __forceinline__ void wave_max_min_u32(uint32_t &mx, uint32_t &mn) {
+#define BKV_STEP(C)                            \
+  mx = max(mx, dpp_move_u32<C>(mx));           \
+  mn = min(mn, dpp_move_u32<C>(mn));
+  BKV_STEP(0xB1) BKV_STEP(0x4E) BKV_STEP(0x141) BKV_STEP(0x140)
+#undef BKV_STEP
+  uint32_t a = 0, b = ~0u;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) c[i] = reinterpret_cast<const uint4 *>(row)[i];
+  for (int r = 0; r < 4; ++r) {
+    a = max(a, (uint32_t)__builtin_amdgcn_readlane((int)mx, 16 * r));
+    b = min(b, (uint32_t)__builtin_amdgcn_readlane((int)mn, 16 * r));
   }
-  {  // the group's queries: G * head_dim elements, 128 threads, one batch of loads
-    const T *qg = q + ((int64_t)b * n_q + g * G) * kHeadDim;
-    T qv[16];
+  mx = a;
+  mn = b;
+}
+
+// Exclusive prefix over the lanes of v (0 <= v < 2^BITS) and the wave total.
+template <int BITS>
+__device__ __forceinline__ int lane_prefix(int v, int *total) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int pre = 0, tot = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = u * 128 + threadIdx.x;
-      if (i < G * kHeadDim) qv[u] = qg[i];
+  for (int bt = 0; bt < BITS; ++bt) {
+    const uint64_t m = __ballot((v >> bt) & 1);
+    pre += __popcll(m & below) << bt;
+    tot += __popcll(m) << bt;
+  }
+  *total = tot;
+  return pre;
+}
+
+// Top-k of one score row, run by NWV whole wavefronts (threads 0 .. 64 NWV - 1).
+// v[j] holds the score of page (64 w + l) KPT + j (any value past the row).
+// Requires NP <= 64 * NWV * KPT and 1 <= k < NP.
+template <int KPT, int NWV>
+__device__ __forceinline__ void topk_row(const float (&v)[KPT], int NP, int k,
+                                         int32_t *__restrict__ out) {
+  __shared__ int xch[2][NWV > 1 ? NWV : 1][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = (wave * 64 + lane) * KPT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = base + j < NP ? order_key(v[j]) : 0u;
+  // ---- shared leading bits of the valid keys ----
+  uint32_t kmax = 0u, kmin = ~0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (base + j < NP) {
+      kmax = max(kmax, key[j]);
+      kmin = min(kmin, key[j]);
     }
+  }
+  wave_max_min_u32(kmax, kmin);
+  if (NWV > 1) {
+    if (lane == 0) {
+      xch[0][wave][0] = (int)kmax;
+      xch[0][wave][1] = (int)kmin;
+    }
+    __syncthreads();
+    kmax = 0u;
+    kmin = ~0u;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = u * 128 + threadIdx.x;
-      if (i < G * kHeadDim) qs[i / kHeadDim][i % kHeadDim] = to_f32(qv[u]);
+    for (int w = 0; w < NWV; ++w) {
+      kmax = max(kmax, (uint32_t)xch[0][w][0]);
+      kmin = min(kmin, (uint32_t)xch[0][w][1]);
+    }
+    __syncthreads();
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int top = diff ? 31 - __clz(diff) : -1;  // -1: every valid key is equal
+  uint32_t tau = top < 0 ? kmax : top == 31 ? 0u : kmax & ~((2u << top) - 1u);
+  // ---- tau, bit by bit ----
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (NWV > 1) {
+      if (lane == 0) xch[bit & 1][wave][0] = cnt;
+      __syncthreads();
+      cnt = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) cnt += xch[bit & 1][w][0];
+    }
+    if (cnt >= k) tau = cand;
+  }
+  // ---- compaction in page order ----
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    n_gt += key[j] > tau;
+    n_eq += key[j] == tau;
+  }
+  constexpr int CB = KPT >= 64 ? 8 : KPT >= 16 ? 6 : 5;  // bits of a per-lane count
+  int gt_tot, eq_tot;
+  int gt_before = lane_prefix<CB>(n_gt, &gt_tot);
+  int eq_before = lane_prefix<CB>(n_eq, &eq_tot);
+  int total_gt = gt_tot;
+  if (NWV > 1) {
+    __syncthreads();
+    if (lane == 0) {
+      xch[0][wave][0] = gt_tot;
+      xch[0][wave][1] = eq_tot;
+    }
+    __syncthreads();
+    total_gt = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const int g = xch[0][w][0], e = xch[0][w][1];
+      total_gt += g;
+      if (w < wave) {
+        gt_before += g;
+        eq_before += e;
+      }
     }
   }
-  __syncthreads();
-  if (!active) return;
-  float acc = 0.f;
+  const int need = k - total_gt;  // keys equal to tau still to take (>= 1)
+  const int take_eq = max(0, min(n_eq, need - eq_before));
+  int pos = gt_before + min(eq_before, need);
+  int taken = 0;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    float x[CE];
-    unpack_chunk<T>(c[i], x);
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc = fmaf(x[e], qs[h][i * CE + e], acc);
+  for (int j = 0; j < KPT; ++j) {
+    const bool take = key[j] > tau || (key[j] == tau && taken < take_eq);
+    taken += key[j] == tau && take;
+    if (take) out[pos++] = base + j;
   }
-  q_proj[((int64_t)b * n_q + g * G + h) * w + j] = acc;
+}
+
+// Standalone selection: grid (n_kv, batch), 64 * NWV threads.
+template <int KPT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  // the whole row is requested before the sequence length arrives
+  const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
+  const int base = threadIdx.x * KPT;
+  float v[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) v[j] = base + j < max_pages ? row[base + j] : 0.f;
+  const int L = clamp_len(seq_lens[b], cap);
+  const int NP = (L + page_size - 1) / page_size;
+  int32_t *out = sel + ((int64_t)b * n_kv + g) * k;
+  if (k >= NP) {
+    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < NP ? i : -1;
+    return;
+  }
+  topk_row<KPT, NWV>(v, NP, k, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -157,136 +291,6 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// (a3) exact top-k per (sequence, KV head).  Scores become order-preserving
-// 32-bit keys in LDS.  The k-th largest key tau is built two bits at a time
-// from the top: of the candidates tau | d << shift, the largest that at least
-// k keys reach is kept (counts by wavefront ballots, one barrier per round,
-// no atomics).  The compaction then takes, in index order, every key above
-// tau and the lowest-index keys equal to it.
-// grid (n_kv, batch), 256 threads, dynamic LDS = max_pages * 4 bytes.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(float f) {
-  if (f != f) return 0u;                      // NaN ranks lowest
-  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix sum over the 256 threads of the block (unsigned, so two
-// 16-bit counts may share one word); returns the total via *total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
-                                                         uint32_t *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t s = scratch[w];
-    if (w < wave) base += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - v;
-}
-
-__global__ __launch_bounds__(256) void topk_select_kernel(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
-    int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k) {
-  extern __shared__ uint32_t keys[];
-  __shared__ int counts[2][4][3];
-  __shared__ uint32_t scan_scratch[4];
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int L = clamp_len(seq_lens[b], cap);
-  const int NP = (L + page_size - 1) / page_size;
-  int32_t *out = sel + ((int64_t)b * n_kv + g) * k;
-  if (k >= NP) {
-    for (int i = tid; i < k; i += 256) out[i] = i < NP ? i : -1;
-    return;
-  }
-  const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
-  for (int i0 = 0; i0 < NP; i0 += 256 * 16) {  // 16 loads per thread in flight
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = i0 + u * 256 + tid;
-      v[u] = i < NP ? row[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = i0 + u * 256 + tid;
-      if (i < NP) keys[i] = order_key(v[u]);
-    }
-  }
-  __syncthreads();
-
-  // two bits per round: counts of keys reaching the three candidates
-  // tau | d << shift (d = 1, 2, 3), one ballot per candidate and 64 keys
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t tau = 0;
-  int buf = 0;
-  for (int shift = 30; shift >= 0; shift -= 2, buf ^= 1) {
-    const uint32_t c1 = tau | (1u << shift), c2 = tau | (2u << shift), c3 = tau | (3u << shift);
-    int n1 = 0, n2 = 0, n3 = 0;
-    for (int i0 = wave * 64; i0 < NP; i0 += 256) {  // wavefront-uniform trip count
-      const int i = i0 + lane;
-      const uint32_t key = i < NP ? keys[i] : 0u;  // 0 reaches no candidate (all >= 1)
-      n1 += __popcll(__ballot(key >= c1));
-      n2 += __popcll(__ballot(key >= c2));
-      n3 += __popcll(__ballot(key >= c3));
-    }
-    if (lane == 0) {
-      counts[buf][wave][0] = n1;
-      counts[buf][wave][1] = n2;
-      counts[buf][wave][2] = n3;
-    }
-    __syncthreads();
-    int t1 = 0, t2 = 0, t3 = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      t1 += counts[buf][w][0];
-      t2 += counts[buf][w][1];
-      t3 += counts[buf][w][2];
-    }
-    const uint32_t dg = t3 >= k ? 3u : t2 >= k ? 2u : t1 >= k ? 1u : 0u;
-    tau |= dg << shift;
-  }
-  // tau is the k-th largest key: at least k keys reach it, fewer than k exceed it
-
-  const int per = (NP + 255) / 256;
-  const int i0 = min(NP, tid * per), i1 = min(NP, i0 + per);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
-    n_gt += key > tau;
-    n_eq += key == tau;
-  }
-  // one scan of both counts: each total is < 65536 (NP <= 32768 < k + NP), so
-  // the low half never carries into the high half
-  uint32_t total;
-  const uint32_t packed = block_exclusive_scan(n_gt | (n_eq << 16), scan_scratch, &total);
-  const int need = k - (int)(total & 0xffffu);  // keys equal to tau still to take
-  const int eq_before = (int)(packed >> 16);
-  const int take_eq = max(0, min((int)n_eq, need - eq_before));
-  int pos = (int)(packed & 0xffffu) + min(eq_before, need);
-  int taken = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
-    if (key > tau || (key == tau && taken < take_eq)) {
-      taken += key == tau;
-      out[pos++] = i;
-    }
-  }
-}
-
 template <typename T>
 hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                      float *q_proj, hipStream_t s) {
@@ -378,16 +382,20 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
 
 hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s) {
-  const size_t lds = (size_t)d.max_pages_per_seq * sizeof(uint32_t);
-  if (lds > 48 * 1024) {
-    // more than the default dynamic LDS: raise the kernel's limit (gfx950 has 160 KB per CU)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(topk_select_kernel, dim3(d.n_kv_heads, d.batch), dim3(256), lds, s, scores,
-                     seq_lens, sel, d.n_kv_heads, d.max_pages_per_seq, d.page_size,
-                     d.max_pages_per_seq * d.page_size, top_k);
+  const int mp = d.max_pages_per_seq, cap = d.max_pages_per_seq * d.page_size;
+  const dim3 grid(d.n_kv_heads, d.batch);
+  if (mp <= 1024)
+    hipLaunchKernelGGL((topk_select_kernel<16, 1>), grid, dim3(64), 0, s, scores, seq_lens, sel,
+                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+  else if (mp <= 4096)
+    hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
+                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+  else if (mp <= 16384)
+    hipLaunchKernelGGL((topk_select_kernel<16, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
+                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<32, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
+                       d.n_kv_heads, mp, d.page_size, cap, top_k);
   return hipGetLastError();
 }
 

@@ -5,8 +5,8 @@ Builds the device state of one layer's decode step from stored host arrays
 latent-to-output matrix (computed by the library), workspace and outputs --
 and runs the step as the sequence of library calls:
     compress_prefill (one new token per sequence, optional)
-    -> project_queries -> score_pages -> select_pages
-    -> sparse_attend -> reconstruct.
+    -> route_pages (project, score, select) -> sparse_attend -> reconstruct;
+the three routing stages are also callable one by one.
 PyTorch only allocates device memory and provides the stream.
 """
 
@@ -79,7 +79,8 @@ class DecodeProblem:
         self.M = torch.empty((wl.hidden, Hq * wl.r_v), dtype=tdt, device=dev)
         api.fuse_output_matrix(self.dims, self.fac["Bf"], self.fac["W_O"], self.M)
         ws = api.workspace_bytes(self.dims, self.top_k)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        # zero-filled once: the attention call's merge counters live in it
+        self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.q_proj = torch.empty((B, Hq, wl.r_b + wl.r_q), dtype=torch.float32, device=dev)
         self.page_scores = torch.empty((B, Hkv, self.max_pages), dtype=torch.float32, device=dev)
         self.sel = torch.empty((B, Hkv, self.top_k), dtype=torch.int32, device=dev)
@@ -101,6 +102,11 @@ class DecodeProblem:
     def select(self):
         api.select_pages(self.dims, self.page_scores, self.seq_lens, self.top_k, self.sel)
 
+    def route(self):
+        """Projection, scoring and selection in one library call."""
+        api.route_pages(self.dims, self.q, self.fac["P"], self.fac["Q"], self.cache, self.top_k,
+                        self.page_scores, self.sel, self.workspace)
+
     def attend(self):
         api.sparse_attend(self.dims, self.q, self.cache, self.sel, self.top_k, self.scale, self.u,
                           self.workspace)
@@ -108,7 +114,24 @@ class DecodeProblem:
     def reconstruct(self):
         api.reconstruct(self.dims, self.u.view(self.u.shape[0], -1), self.M, self.y)
 
+    def decode_step(self):
+        """The whole step (append, route, attend, reconstruct) in one library call."""
+        api.decode_step(self.dims, self.q, self.k_new, self.v_new, self.start_pos, self.fac["A"],
+                        self.fac["P"], self.fac["Q"], self.fac["E"], self.M, self.cache, self.top_k,
+                        self.scale, self.page_scores, self.sel, self.u,
+                        self.y, self.workspace)
+
     def step(self, append=True):
+        """One decode step: the library's four calls (the new token's append,
+        routing, sparse attention, reconstruction)."""
+        if append:
+            self.append()
+        self.route()
+        self.attend()
+        self.reconstruct()
+
+    def step_unfused(self, append=True):
+        """The same step with routing as its three separate calls."""
         if append:
             self.append()
         self.project()

@@ -99,6 +99,8 @@ def reconstruct_bytes(s: StepShape):
 
 
 def step_bytes(s: StepShape, seq_lens, append=True):
+    """Per-launch algorithmic bytes of one decode step (keys: append, project,
+    score, select, attend, reconstruct, total)."""
     parts = dict(project=project_bytes(s), score=score_bytes(s, seq_lens),
                  select=select_bytes(s, seq_lens), attend=attend_bytes(s, seq_lens),
                  reconstruct=reconstruct_bytes(s))

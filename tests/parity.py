@@ -104,7 +104,8 @@ def check_scores(gpu, want, n_pages, where=""):
         return
     g, w = gpu[:n_pages], want[:n_pages]
     rms = math.sqrt(float(np.mean(w * w)))
-    err = np.abs(g - w) / np.maximum(np.abs(w), rms)
+    den = np.maximum(np.abs(w), rms)
+    err = np.where(den > 0, np.abs(g - w) / np.where(den > 0, den, 1.0), np.abs(g - w))
     assert err.max() <= SCORE_RTOL, f"{where}: score rel err {err.max():.3g} at page {int(err.argmax())}"
 
 

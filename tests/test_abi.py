@@ -114,6 +114,17 @@ def test_null_and_shape_and_workspace_errors():
     assert lib.basiskv_compress_prefill(ctypes.byref(d), FAKE, FAKE, None, 1, FAKE, FAKE, FAKE,
                                         ctypes.byref(c), None) == 1
     assert lib.basiskv_fuse_output_matrix(ctypes.byref(d), FAKE, None, FAKE, None) == 1
+    # the whole-step call: null, shape, workspace and batch checks (all return
+    # before any launch)
+    def step(dd, q=FAKE, top_k=128, ws=FAKE, ws_bytes=1 << 30):
+        return lib.basiskv_decode_step(ctypes.byref(dd), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, ctypes.byref(c), top_k, 0.1, FAKE, FAKE, FAKE,
+                                       FAKE, ws, ws_bytes, None)
+    assert step(d, q=None) == 1
+    assert step(d, top_k=0) == 2
+    assert step(d, ws_bytes=64) == 4
+    assert step(d, ws=None) == 4
+    assert step(dims_of(WORKLOADS[2], batch=40)) == 3
     big = dims_of(WORKLOADS[2], batch=40)
     assert lib.basiskv_reconstruct(ctypes.byref(big), FAKE, FAKE, FAKE, None) == 3
 

@@ -190,16 +190,68 @@ def test_block_table_permutation_and_determinism_bit_exact():
             np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
 
 
-def test_fused_route_call_equals_the_three_step_calls():
-    wl = workload(1)
-    inp = synth.decode_inputs(wl, batch=4, ctx=2048)
-    prob = DecodeProblem(wl, inp)
-    prob.step(append=True)
+@pytest.mark.parametrize("wl_index", [1, 2, 4])
+def test_combined_calls_equal_the_separate_calls(wl_index):
+    """route_pages gives the bits of project + score + select, and the
+    whole-step call (compression and projection sharing one launch) the bits
+    of the four separate calls, also when repeated on one workspace."""
+    wl = workload(wl_index)
+    inp = synth.decode_inputs(wl, batch=4, ctx=8192, seq_lens=[8192, 8000, 33, 4097])
+    prob = DecodeProblem(wl, inp, top_k=16)
+    prob.step_unfused(append=True)
     base = prob.outputs()
-    scores = torch.empty_like(prob.page_scores)
-    sel = torch.empty_like(prob.sel)
-    api.route_pages(prob.dims, prob.q, prob.fac["P"], prob.fac["Q"], prob.cache, prob.top_k, scores,
-                    sel, prob.workspace)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(scores.double().cpu().numpy(), base["scores"])
-    np.testing.assert_array_equal(sel.cpu().numpy(), base["sel"])
+    for call in ("step", "decode_step", "decode_step", "step"):
+        for t in (prob.page_scores, prob.u):
+            t.fill_(float("nan"))
+        prob.sel.fill_(-7)
+        prob.y.fill_(0)
+        getattr(prob, call)()
+        got = prob.outputs()
+        for key in ("scores", "sel", "u", "y"):
+            np.testing.assert_array_equal(got[key], base[key], err_msg=f"{call} {key}")
+    compare_step(wl, inp, prob, got, range(4))
+
+
+def test_repeated_steps_reuse_the_workspace_bit_exact():
+    """Steps that merge several attention splits (the merge counters return to
+    zero after every call) give identical bits call after call."""
+    wl = workload(2)
+    inp = synth.decode_inputs(wl, batch=3, ctx=16384, seq_lens=[16384, 9000, 100])
+    prob = DecodeProblem(wl, inp, top_k=128)
+    outs = []
+    for _ in range(4):
+        prob.u.fill_(float("nan"))
+        prob.step(append=True)
+        outs.append(prob.outputs())
+    for o in outs[1:]:
+        for key in ("scores", "sel", "u", "y"):
+            np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
+    compare_step(wl, inp, prob, outs[-1], range(3))
+
+
+@pytest.mark.parametrize("page_size,ctx", [(8, 100000), (4, 80000)])
+def test_long_rows_selection(page_size, ctx):
+    """Rows of 12500 and 20000 pages: the selection runs as its own launch
+    with 1024 threads per row; every sequence checked against the oracle."""
+    wl = workload(0).with_(page_size=page_size)
+    run_case(wl, batch=1, ctx=ctx, top_k=40)
+
+
+@pytest.mark.parametrize("wl_index,ctx", [(2, 4096), (4, 8192 * 8)])
+def test_all_scores_tied_selects_lowest_pages(wl_index, ctx):
+    """Zero queries make every page score 0: the k lowest page indices are
+    selected (ties go to the lower index), through the fused and the
+    separate selection paths."""
+    wl = workload(wl_index)
+    inp = synth.decode_inputs(wl, batch=2, ctx=ctx, seq_lens=[ctx, ctx - 100])
+    inp["q"] = np.zeros_like(inp["q"])
+    prob = DecodeProblem(wl, inp, top_k=24)
+    prob.step(append=True)
+    out = prob.outputs()
+    S = wl.page_size
+    for b, L in enumerate(inp["seq_lens"]):
+        n_pages = -(-int(L) // S)
+        assert np.all(out["scores"][b][:, :n_pages] == 0.0)
+        for g in range(wl.n_kv_heads):
+            np.testing.assert_array_equal(out["sel"][b, g], np.arange(24))
+    compare_step(wl, inp, prob, out, range(2))
