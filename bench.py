@@ -51,7 +51,70 @@ def parse():
     ap.add_argument("--workload", default="llama8b-ctx32k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a 64 MiB read + 64 MiB write elementwise kernel (torch.neg) "
+                         "five times, the reference for HBM counter scaling")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE; --calibration-copy) into " + PMC_SUMMARY)
     return ap.parse_args()
+
+
+CALIB_BYTES = 64 << 20
+
+
+def calibration_copy():
+    import torch
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def pmc_summary(fetch_dir, write_dir, workload_name):
+    """Per-dispatch HBM bytes of route_scan_kernel from two counter runs,
+    scaled by what the same counters read for the calibration kernel."""
+    import csv
+    import glob
+
+    def per_kernel(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no counter_collection.csv under {d}")
+        vals = {"route": [], "calib": []}
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                name = row["Kernel_Name"]
+                if "route_scan_kernel" in name:
+                    vals["route"].append(float(row["Counter_Value"]))
+                elif "neg_kernel" in name:
+                    vals["calib"].append(float(row["Counter_Value"]))
+        if not vals["route"] or not vals["calib"]:
+            sys.exit(f"{d}: route_scan_kernel or calibration dispatches missing")
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    ref_kib = CALIB_BYTES / 1024
+    fetch_scale = ref_kib / fetch["calib"]
+    write_scale = ref_kib / write["calib"]
+    hbm = (fetch["route"] * fetch_scale + write["route"] * write_scale) * 1024
+    out = {"workload": workload_name, "kernel": "route_scan_kernel",
+           "source_sha256": route_source_sha(),
+           "fetch_size_kib_per_dispatch": round(fetch["route"], 1),
+           "write_size_kib_per_dispatch": round(write["route"], 1),
+           "calibration": {"kernel": "torch.neg over 64 MiB float32 (64 MiB read, 64 MiB written)",
+                           "fetch_size_kib": round(fetch["calib"], 1),
+                           "write_size_kib": round(write["calib"], 1),
+                           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+           "hbm_bytes_per_launch": round(hbm),
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 "
+                        f"bench.py --workload {workload_name} --steps 5 --warmup 2 --cpu-seconds 0 "
+                        f"--calibration-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
+    with open(PMC_SUMMARY, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def route_source_sha():
@@ -125,6 +188,9 @@ def _shape(wl, B, inp):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
@@ -142,6 +208,8 @@ def main():
         sys.exit("bench.py needs a GPU")
     api.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        calibration_copy()
 
     wl = workload(int(args.workload) if args.workload.isdigit() else args.workload)
     # for the prefill + decode workload the step measured is the last decode

@@ -21,15 +21,14 @@ __global__ __launch_bounds__(128) void project_queries_kernel(
 // ---------------------------------------------------------------------------
 // (a3) exact top-k per (sequence, KV head).
 //
-// Scores become order-preserving 32-bit keys held in registers: lane l of
-// wavefront w owns the KPT consecutive pages starting at (64 w + l) KPT.  The
-// k-th largest key tau is built one bit at a time from the top (a candidate
-// is kept when at least k keys reach it; counts by wavefront ballots, and,
-// with several wavefronts, one LDS exchange and barrier per bit).  Bits that
-// every valid key shares -- above the highest bit in which the largest and
-// smallest keys differ -- are taken as given.  The compaction then writes, in
-// page order, every page whose key exceeds tau and the lowest-index pages
-// equal to it; lane prefix sums come from ballots of the count bits.
+// Scores become order-preserving 32-bit keys held in registers, KPT per lane.
+// The k-th largest key tau is built one bit at a time from the top (a
+// candidate is kept when at least k keys reach it; counts by wavefront
+// ballots, and, with several wavefronts, one LDS exchange and barrier per
+// bit).  Bits that every valid key shares -- above the highest bit in which
+// the largest and smallest keys differ -- are taken as given.  The compaction
+// then writes, in page order, every page whose key exceeds tau and the
+// lowest-index pages equal to it; positions come from ballot popcounts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 0u;                      // NaN ranks lowest
@@ -59,43 +58,27 @@ __device__ __forceinline__ void wave_max_min_u32(uint32_t &mx, uint32_t &mn) {
   mn = b;
 }
 
-// Exclusive prefix over the lanes of v (0 <= v < 2^BITS) and the wave total.
-template <int BITS>
-__device__ __forceinline__ int lane_prefix(int v, int *total) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int bt = 0; bt < BITS; ++bt) {
-    const uint64_t m = __ballot((v >> bt) & 1);
-    pre += __popcll(m & below) << bt;
-    tot += __popcll(m) << bt;
-  }
-  *total = tot;
-  return pre;
-}
-
 // Top-k of one score row, run by NWV whole wavefronts (threads 0 .. 64 NWV - 1).
-// v[j] holds the score of page (64 w + l) KPT + j (any value past the row).
-// Requires NP <= 64 * NWV * KPT and 1 <= k < NP.
+// Page i = 64 (KPT w + j) + l is held by lane l of wavefront w as key[j]
+// (a wavefront loads 64 consecutive scores per instruction); v[j] is its
+// score (any value past the row).  Requires NP <= 64 NWV KPT and 1 <= k < NP.
 template <int KPT, int NWV>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int NP, int k,
                                          int32_t *__restrict__ out) {
   __shared__ int xch[2][NWV > 1 ? NWV : 1][2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int base = (wave * 64 + lane) * KPT;
+  const int base = wave * 64 * KPT + lane;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   uint32_t key[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = base + j < NP ? order_key(v[j]) : 0u;
-  // ---- shared leading bits of the valid keys ----
   uint32_t kmax = 0u, kmin = ~0u;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    if (base + j < NP) {
-      kmax = max(kmax, key[j]);
-      kmin = min(kmin, key[j]);
-    }
+    const bool ok = base + 64 * j < NP;
+    key[j] = ok ? order_key(v[j]) : 0u;
+    kmax = ok ? max(kmax, key[j]) : kmax;
+    kmin = ok ? min(kmin, key[j]) : kmin;
   }
+  // ---- leading bits shared by every valid key ----
   wave_max_min_u32(kmax, kmin);
   if (NWV > 1) {
     if (lane == 0) {
@@ -115,7 +98,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int NP, int k,
   const uint32_t diff = kmax ^ kmin;
   const int top = diff ? 31 - __clz(diff) : -1;  // -1: every valid key is equal
   uint32_t tau = top < 0 ? kmax : top == 31 ? 0u : kmax & ~((2u << top) - 1u);
-  // ---- tau, bit by bit ----
+  // ---- tau, bit by bit (padding keys are 0 and reach no candidate) ----
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int cnt = 0;
@@ -130,45 +113,45 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int NP, int k,
     }
     if (cnt >= k) tau = cand;
   }
-  // ---- compaction in page order ----
-  int n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    n_gt += key[j] > tau;
-    n_eq += key[j] == tau;
-  }
-  constexpr int CB = KPT >= 64 ? 8 : KPT >= 16 ? 6 : 5;  // bits of a per-lane count
-  int gt_tot, eq_tot;
-  int gt_before = lane_prefix<CB>(n_gt, &gt_tot);
-  int eq_before = lane_prefix<CB>(n_eq, &eq_tot);
-  int total_gt = gt_tot;
+  // ---- compaction in page order: every key above tau, then the lowest-index
+  // keys equal to tau up to k in all ----
+  int gt_run = 0, eq_run = 0, total_gt = 0;
   if (NWV > 1) {
-    __syncthreads();
-    if (lane == 0) {
-      xch[0][wave][0] = gt_tot;
-      xch[0][wave][1] = eq_tot;
+    int gt_w = 0, eq_w = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      gt_w += __popcll(__ballot(key[j] > tau));
+      eq_w += __popcll(__ballot(key[j] == tau));
     }
     __syncthreads();
-    total_gt = 0;
+    if (lane == 0) {
+      xch[0][wave][0] = gt_w;
+      xch[0][wave][1] = eq_w;
+    }
+    __syncthreads();
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
       const int g = xch[0][w][0], e = xch[0][w][1];
       total_gt += g;
       if (w < wave) {
-        gt_before += g;
-        eq_before += e;
+        gt_run += g;
+        eq_run += e;
       }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) total_gt += __popcll(__ballot(key[j] > tau));
   }
-  const int need = k - total_gt;  // keys equal to tau still to take (>= 1)
-  const int take_eq = max(0, min(n_eq, need - eq_before));
-  int pos = gt_before + min(eq_before, need);
-  int taken = 0;
+  const int need = k - total_gt;  // keys equal to tau to take (>= 1)
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool take = key[j] > tau || (key[j] == tau && taken < take_eq);
-    taken += key[j] == tau && take;
-    if (take) out[pos++] = base + j;
+    const uint64_t m_gt = __ballot(key[j] > tau);
+    const uint64_t m_eq = __ballot(key[j] == tau);
+    const int eq_pos = eq_run + __popcll(m_eq & below);
+    const bool take = key[j] > tau || (key[j] == tau && eq_pos < need);
+    if (take) out[gt_run + __popcll(m_gt & below) + min(eq_pos, need)] = base + 64 * j;
+    gt_run += __popcll(m_gt);
+    eq_run += __popcll(m_eq);
   }
 }
 
@@ -180,10 +163,10 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
   const int g = blockIdx.x, b = blockIdx.y;
   // the whole row is requested before the sequence length arrives
   const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
-  const int base = threadIdx.x * KPT;
+  const int base = (threadIdx.x >> 6) * 64 * KPT + (threadIdx.x & 63);
   float v[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) v[j] = base + j < max_pages ? row[base + j] : 0.f;
+  for (int j = 0; j < KPT; ++j) v[j] = base + 64 * j < max_pages ? row[base + 64 * j] : 0.f;
   const int L = clamp_len(seq_lens[b], cap);
   const int NP = (L + page_size - 1) / page_size;
   int32_t *out = sel + ((int64_t)b * n_kv + g) * k;
@@ -380,13 +363,19 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
 }
 
+#ifndef BKV_SELECT_SMALL_WAVES
+#define BKV_SELECT_SMALL_WAVES 4
+#endif
+constexpr int kSelectSmallWaves = BKV_SELECT_SMALL_WAVES;  // wavefronts per row up to 1024 pages
+
 hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s) {
   const int mp = d.max_pages_per_seq, cap = d.max_pages_per_seq * d.page_size;
   const dim3 grid(d.n_kv_heads, d.batch);
   if (mp <= 1024)
-    hipLaunchKernelGGL((topk_select_kernel<16, 1>), grid, dim3(64), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+    hipLaunchKernelGGL((topk_select_kernel<16 / kSelectSmallWaves, kSelectSmallWaves>), grid,
+                       dim3(64 * kSelectSmallWaves), 0, s, scores, seq_lens, sel, d.n_kv_heads, mp,
+                       d.page_size, cap, top_k);
   else if (mp <= 4096)
     hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
                        d.n_kv_heads, mp, d.page_size, cap, top_k);
