@@ -179,8 +179,10 @@ int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
  * from the latents; abstract: Value compression is tied to the output
  * projection).  MFMA GEMM with float32 accumulation; for bf16, u is split into
  * two bf16 terms (hi + lo) so no precision is lost before the product.
- *   u [batch][n_q_heads * r_v] float32;  M [hidden][n_q_heads * r_v] (row n of
- *   M holds output feature n);  y [batch][hidden] out, in dtype.
+ *   u [batch][n_q_heads * r_v] float32;  M: hidden x K (K = n_q_heads * r_v)
+ *   elements in the tiled layout written by basiskv_fuse_output_matrix;
+ *   y [batch][hidden] out, in dtype.  Needs hidden % 16 == 0 and K % 32 == 0
+ *   (bf16) or K % 16 == 0 (float32), ERR_UNSUPPORTED otherwise.
  * batch must be <= 32 for bf16 and <= 64 for float32 (ERR_UNSUPPORTED). */
 int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void *M, void *y,
                             void *stream);
@@ -205,9 +207,13 @@ int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void 
 
 /* Set-up: fuse the Value decoder into the output projection,
  *   M[n][h * r_v + i] = sum_d Bf[h / G][i][d] * W_O[h * head_dim + d][n],
- * i.e. M = (blockdiag_h(Bf_{h/G}) W_O)^T, float32 accumulation, stored in dtype.
+ * i.e. M = (blockdiag_h(Bf_{h/G}) W_O)^T, float32 accumulation, stored in dtype
+ * in MFMA tiles: element (n, k) at
+ *   ((n / 16 * (K / KS) + k / KS) * 64 + (k % KS) / KL * 16 + n % 16) * KL + k % KL,
+ * KL = 16 / element bytes (8 bf16, 4 float32), KS = 4 * KL, K = n_q_heads * r_v;
+ * each MFMA step's operand (16 features x KS slots) is one contiguous 1 KB run.
  *   Bf [n_kv][r_v][head_dim];  W_O [n_q_heads * head_dim][hidden];
- *   M [hidden][n_q_heads * r_v] out. */
+ *   M: hidden * n_q_heads * r_v elements out (same size as the plain matrix). */
 int32_t basiskv_fuse_output_matrix(const basiskv_dims *dims, const void *Bf, const void *W_O,
                                    void *M, void *stream);
 

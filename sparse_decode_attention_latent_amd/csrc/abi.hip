@@ -39,6 +39,13 @@ int32_t check_dims(const basiskv_dims *d) {
   return BASISKV_OK;
 }
 
+// The fused output matrix is stored in MFMA tiles: 16 output features by 32
+// (bf16) or 16 (float32) contraction slots.
+bool output_tiles_fit(const basiskv_dims &d) {
+  const int kstep = d.dtype == BASISKV_BF16 ? 32 : 16;
+  return d.hidden % 16 == 0 && (d.n_q_heads * d.r_v) % kstep == 0;
+}
+
 int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_r) {
   if (!c || !c->block_table || !c->seq_lens) return BASISKV_ERR_NULL;
   if ((need_k && !c->k_pages) || (need_z && !c->z_pages) || (need_r && !c->r_pages))
@@ -49,14 +56,21 @@ int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout:
-//   [0, C)   per-(sequence, KV head) counters with which the attention
-//            launch elects the workgroup that merges a row's splits; zero
-//            after allocation, and every call leaves them zero
-//   [C, ..)  scratch: the projected queries during routing, then the
-//            attention splits' partial records (stream order keeps the two
-//            uses apart)
+//   [0, C)       per-(sequence, KV head) counters with which the attention
+//                launch elects the workgroup that merges a row's splits;
+//                zero after allocation, and every call leaves them zero
+//   [C, C + U)   (bf16 decode step) u as the reconstruction's A operand
+//   [C + U, ..)  scratch: the projected queries during routing, then the
+//                attention splits' partial records (stream order keeps the
+//                two uses apart)
 size_t counter_bytes(const basiskv_dims &d) {
   return align_up((size_t)d.batch * d.n_kv_heads * sizeof(int32_t));
+}
+
+size_t utile_bytes(const basiskv_dims &d) {
+  if (d.dtype != BASISKV_BF16) return 0;
+  const size_t tiles = (size_t)(d.batch + 7) / 8;
+  return align_up(tiles * ((size_t)d.n_q_heads * d.r_v / 32) * 1024);
 }
 
 size_t qproj_bytes(const basiskv_dims &d) {
@@ -68,9 +82,16 @@ size_t partial_bytes(const basiskv_dims &d, int32_t top_k) {
   return align_up((size_t)d.batch * d.n_q_heads * ns * (d.r_v + 2) * sizeof(float));
 }
 
+size_t scratch_offset(const basiskv_dims &d) { return counter_bytes(d) + utile_bytes(d); }
+
 int32_t *attend_counters(void *ws) { return static_cast<int32_t *>(ws); }
+uint16_t *u_tiles(void *ws, const basiskv_dims &d) {
+  return d.dtype == BASISKV_BF16
+             ? reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + counter_bytes(d))
+             : nullptr;
+}
 float *scratch(void *ws, const basiskv_dims &d) {
-  return reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes(d));
+  return reinterpret_cast<float *>(static_cast<char *>(ws) + scratch_offset(d));
 }
 
 int32_t launched(hipError_t e) { return e == hipSuccess ? BASISKV_OK : BASISKV_ERR_LAUNCH; }
@@ -96,7 +117,7 @@ const char *basiskv_status_string(int32_t status) {
 size_t basiskv_workspace_bytes(const basiskv_dims *d, int32_t top_k) {
   if (check_dims(d) != BASISKV_OK || top_k < 1) return 0;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
-  return counter_bytes(*d) + (a > b ? a : b);
+  return scratch_offset(*d) + (a > b ? a : b);
 }
 
 int32_t basiskv_compress_prefill(const basiskv_dims *d, const void *k, const void *v,
@@ -154,7 +175,7 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
   if (!q || !P || !Q || !page_scores || !sel) return BASISKV_ERR_NULL;
   if ((st = check_cache(c, false, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
-  if (!ws || ws_bytes < counter_bytes(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
+  if (!ws || ws_bytes < scratch_offset(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   float *q_proj = scratch(ws, *d);
   hipStream_t s = as_stream(stream);
@@ -175,11 +196,12 @@ int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basisk
   if ((st = check_cache(c, true, true, false))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!bkv_host::attend_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < counter_bytes(*d) + partial_bytes(*d, top_k))
+  if (!ws || ws_bytes < scratch_offset(*d) + partial_bytes(*d, top_k))
     return BASISKV_ERR_WORKSPACE;
   bool unsupported = false;
   hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scratch(ws, *d),
-                                         attend_counters(ws), as_stream(stream), &unsupported);
+                                         attend_counters(ws), nullptr, as_stream(stream),
+                                         &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
   return launched(e);
 }
@@ -190,7 +212,8 @@ int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M
   if (st) return st;
   if (!u || !M || !y) return BASISKV_ERR_NULL;
   if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
-  return launched(bkv_host::launch_reconstruct(*d, u, M, y, as_stream(stream)));
+  if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
+  return launched(bkv_host::launch_reconstruct(*d, u, nullptr, M, y, as_stream(stream)));
 }
 
 int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
@@ -210,8 +233,9 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
     return BASISKV_ERR_UNSUPPORTED;
   if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
+  if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
-  if (!ws || ws_bytes < counter_bytes(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;
+  if (!ws || ws_bytes < scratch_offset(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   float *scr = scratch(ws, *d);
   bool unsupported = false;
@@ -223,10 +247,11 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
   if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
-  e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scr, attend_counters(ws), s,
+  uint16_t *ut = u_tiles(ws, *d);  // attention also leaves u as the reconstruction's operand
+  e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scr, attend_counters(ws), ut, s,
                               &unsupported);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
-  return launched(bkv_host::launch_reconstruct(*d, u, M, y, s));
+  return launched(bkv_host::launch_reconstruct(*d, u, ut, M, y, s));
 }
 
 int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const void *W_O, void *M,
@@ -234,6 +259,7 @@ int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const 
   int32_t st = check_dims(d);
   if (st) return st;
   if (!Bf || !W_O || !M) return BASISKV_ERR_NULL;
+  if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   return launched(bkv_host::launch_fuse(*d, Bf, W_O, M, as_stream(stream)));
 }
 

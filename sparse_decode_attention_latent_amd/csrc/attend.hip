@@ -42,6 +42,7 @@ struct AttendArgs {
   int pages_per_split, n_split, total, padded;
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
   int32_t *counters;  // [batch * n_kv], zero between calls (see the merge)
+  uint16_t *u_tiles;  // optional: u also written as the reconstruction's A operand (bf16)
 };
 
 // Ordering point for LDS traffic between the lanes of one wavefront.
@@ -312,7 +313,9 @@ void attend_split_kernel(
     }
     const int64_t row = (int64_t)b * a.n_q + (int64_t)g * G + h;
     if (a.n_split == 1) {
-      u_out[row * RV + d] = lsum > 0.f ? usum / lsum : 0.f;
+      const float uv = lsum > 0.f ? usum / lsum : 0.f;
+      u_out[row * RV + d] = uv;
+      if (a.u_tiles) store_u_tiles(a.u_tiles, b, (g * G + h) * RV + d, a.n_q * RV, uv);
     } else {
       float *rp = part + (row * a.n_split + split) * rec;
       store_coherent(rp + 2 + d, usum);
@@ -362,7 +365,9 @@ void attend_split_kernel(
         }
       }
     }
-    u_out[row * RV + d] = lsum > 0.f ? usum / lsum : 0.f;
+    const float uv = lsum > 0.f ? usum / lsum : 0.f;
+    u_out[row * RV + d] = uv;
+    if (a.u_tiles) store_u_tiles(a.u_tiles, b, (g * G + h) * RV + d, a.n_q * RV, uv);
   }
 }
 
@@ -429,7 +434,7 @@ bool attend_supported(const basiskv_dims &d) { return find_attend(d) != nullptr;
 
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
-                         int32_t *counters, hipStream_t s, bool *unsupported) {
+                         int32_t *counters, uint16_t *u_tiles, hipStream_t s, bool *unsupported) {
   const void *fn = find_attend(d);
   if (!fn) {
     *unsupported = true;
@@ -451,6 +456,7 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
   a.scale_log2 = scale * kLog2e;
   a.counters = counters;
+  a.u_tiles = u_tiles;
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};

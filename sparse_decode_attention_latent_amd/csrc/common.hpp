@@ -26,12 +26,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// float32 -> bf16, round to nearest even (NaN kept quiet).
+// float32 -> bf16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32; checked bit for bit against a software round-to-nearest-
+// even over normal, subnormal, tie and NaN inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two float32 values -> packed bf16 pair (a in the low half).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+  const pair_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -160,6 +165,23 @@ __device__ __forceinline__ bool last_to_arrive(int32_t *counter, int total) {
   return is_last;
 }
 
+// The latent output u as the A operand of the reconstruction MFMA
+// (v_mfma_f32_16x16x32_bf16): per row tile of 8 sequences and per
+// 32-slot contraction step, one 1 KB run of 64 lanes x 8 bf16, lane
+// (r + 16 q) holding row r, slots 8 q .. 8 q + 7.  Rows 0-7 carry the bf16
+// rounding of u for the tile's 8 sequences, rows 8-15 the bf16 rounding of
+// the remainder (u - hi), so one MFMA sees u to about 16 significant bits.
+// Element (b, k), K = n_q * r_v (a multiple of 32):
+__device__ __forceinline__ int64_t utile_index(int b, int k, int K, bool lo) {
+  const int r = (b & 7) + (lo ? 8 : 0);
+  return (((int64_t)(b >> 3) * (K / 32) + k / 32) * 64 + (k % 32) / 8 * 16 + r) * 8 + k % 8;
+}
+__device__ __forceinline__ void store_u_tiles(uint16_t *ut, int b, int k, int K, float x) {
+  const uint16_t hi = f32_to_bf16(x);
+  ut[utile_index(b, k, K, false)] = hi;
+  ut[utile_index(b, k, K, true)] = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
 // Work-item index of this workgroup for a 1-D grid of `padded` (multiple of 8)
 // workgroups: consecutive work items land on the same XCD, so workgroups that
 // share per-(sequence, head) data (projected queries, block-table rows) hit
@@ -187,9 +209,9 @@ hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32
 int attend_splits(const basiskv_dims &d, int32_t top_k);
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
-                         int32_t *counters, hipStream_t s, bool *unsupported);
-hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const void *M, void *y,
-                              hipStream_t s);
+                         int32_t *counters, uint16_t *u_tiles, hipStream_t s, bool *unsupported);
+hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const uint16_t *u_tiles,
+                              const void *M, void *y, hipStream_t s);
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
                        hipStream_t s);
 hipError_t launch_append(const basiskv_dims &d, const void *k, const void *v,

@@ -45,18 +45,32 @@ __device__ __forceinline__ void split_bf16(const float *x, bf16x8 *hi, bf16x8 *l
   uint32_t h[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint16_t h0 = f32_to_bf16(x[2 * i]), h1 = f32_to_bf16(x[2 * i + 1]);
-    const uint16_t l0 = f32_to_bf16(x[2 * i] - bf16_to_f32(h0));
-    const uint16_t l1 = f32_to_bf16(x[2 * i + 1] - bf16_to_f32(h1));
-    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    h[i] = f32x2_to_bf16x2(x[2 * i], x[2 * i + 1]);
+    l[i] = f32x2_to_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16),
+                           x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
   }
   *hi = bits_to_frag(make_uint4(h[0], h[1], h[2], h[3]));
   *lo = bits_to_frag(make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // ---------------------------------------------------------------------------
-// (a5) y[b][n] = sum_k u[b][k] M[n][k],  K = n_q * r_v.
+// Tiled layout of the fused output matrix.  Element (n, k) of M (row n =
+// output feature, k = h * r_v + i) sits at
+//   ((n / 16 * (K / KSTEP) + k / KSTEP) * 64 + (k % KSTEP) / KPL * 16 + n % 16) * KPL + k % KPL
+// with KPL = 16 / sizeof(element) and KSTEP = 4 * KPL: the B fragment of one
+// MFMA step (16 output features x KSTEP contraction slots) is one contiguous
+// 1 KB run, lane l holding its 16 bytes at l * 16.
+// ---------------------------------------------------------------------------
+template <typename T>
+__host__ __device__ __forceinline__ int64_t mtile_index(int n, int k, int K) {
+  constexpr int KPL = 16 / (int)sizeof(T);
+  constexpr int KSTEP = 4 * KPL;
+  return (((int64_t)(n / 16) * (K / KSTEP) + k / KSTEP) * 64 + (k % KSTEP) / KPL * 16 + n % 16) *
+             KPL + k % KPL;
+}
+
+// ---------------------------------------------------------------------------
+// (a5) y[b][n] = sum_k u[b][k] M[n][k],  K = n_q * r_v, M in the tiled layout.
 // One workgroup of 8 wavefronts per 16 output columns; the wavefronts split K
 // and their 16x16 tiles are summed through LDS.  bf16: the A rows are
 // [hi(u) of 8 sequences ; lo(u) of the same 8], so one MFMA carries both
@@ -64,8 +78,9 @@ __device__ __forceinline__ void split_bf16(const float *x, bf16x8 *hi, bf16x8 *l
 // ---------------------------------------------------------------------------
 constexpr int kReconWaves = 8;
 
-template <typename T, int RT>
+template <typename T, int RT, bool UT>
 __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restrict__ u,
+                                                         const uint16_t *__restrict__ u_tiles,
                                                          const T *__restrict__ M,
                                                          T *__restrict__ y, int batch, int K,
                                                          int N) {
@@ -76,13 +91,38 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int i = lane & 15, qg = lane >> 4;
-  const int n = n0 + i;
   const int n_steps = (K + MF::KS - 1) / MF::KS;
   floatx4 acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (kBf) {
+  if constexpr (UT) {
+    // u already split into its bf16 A operand (utile_index): fragments are
+    // loaded as they are; rows past the batch read as zero
+    constexpr int U = 8;
+    for (int ks0 = wave; ks0 < n_steps; ks0 += kReconWaves * U) {
+      uint4 braw[U], araw[U][RT];
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int ks = ks0 + uu * kReconWaves;
+        braw[uu] = make_uint4(0, 0, 0, 0);
+        if (ks < n_steps)
+          braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          araw[uu][rt] = make_uint4(0, 0, 0, 0);
+          if (ks < n_steps && rt * ROWS + (i & 7) < batch)
+            araw[uu][rt] = reinterpret_cast<const uint4 *>(u_tiles)[((int64_t)rt * n_steps + ks) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt] = MF::mma(bits_to_frag(araw[uu][rt]), bits_to_frag(braw[uu]), acc[rt]);
+    }
+  } else {
     // U k-steps per round: every load of the round is issued before the first MFMA
     constexpr int U = 8 / RT;
     for (int ks0 = wave; ks0 < n_steps; ks0 += kReconWaves * U) {
@@ -90,9 +130,11 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
       float4 ux[U][RT][2];
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
-        const int k = (ks0 + uu * kReconWaves) * MF::KS + qg * 8;
+        const int ks = ks0 + uu * kReconWaves;
+        const int k = ks * MF::KS + qg * 8;
         braw[uu] = make_uint4(0, 0, 0, 0);
-        if (n < N && k < K) braw[uu] = *reinterpret_cast<const uint4 *>(M + (int64_t)n * K + k);
+        if (ks < n_steps)
+          braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int b = rt * ROWS + (i & 7);
@@ -117,6 +159,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
         }
       }
     }
+  }
   } else {
     // float32: each lane loads 4 consecutive k and feeds 4 MFMAs (k slot (qg, s) -> k0 + 4 qg + s)
     constexpr int U = 8 / RT;
@@ -125,10 +168,11 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
       float4 bq[U], aq[U][RT];
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
-        const int k = (kq0 + uu * kReconWaves) * 16 + qg * 4;
+        const int kq = kq0 + uu * kReconWaves;
+        const int k = kq * 16 + qg * 4;
         bq[uu] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (n < N && k < K)
-          bq[uu] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(M) + (int64_t)n * K + k);
+        if (kq < n_quads)
+          bq[uu] = reinterpret_cast<const float4 *>(M)[((int64_t)blockIdx.x * n_quads + kq) * 64 + lane];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int b = rt * ROWS + i;
@@ -167,7 +211,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
-// Set-up: M[n][h*r_v + i] = sum_d Bf[h/G][i][d] W_O[h*dh + d][n].
+// Set-up: M[n][h*r_v + i] = sum_d Bf[h/G][i][d] W_O[h*dh + d][n], stored tiled.
 // grid (ceil(N/64), n_q), 256 threads; W_O's 128 x 64 tile staged in LDS.
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -188,7 +232,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(const T *__restrict__ Bf,
     const T *brow = Bf + ((int64_t)g * rv + i) * kHeadDim;
     float s = 0.f;
     for (int d = 0; d < kHeadDim; ++d) s = fmaf(to_f32(brow[d]), wt[d][c], s);
-    if (n0 + c < N) M[(int64_t)(n0 + c) * K + (int64_t)h * rv + i] = from_f32<T>(s);
+    if (n0 + c < N) M[mtile_index<T>(n0 + c, h * rv + i, K)] = from_f32<T>(s);
   }
 }
 
@@ -393,26 +437,33 @@ namespace bkv_host {
 using namespace bkv;
 
 template <typename T>
-static hipError_t recon_t(const basiskv_dims &d, const float *u, const void *M, void *y,
-                          hipStream_t s) {
+static hipError_t recon_t(const basiskv_dims &d, const float *u, const uint16_t *u_tiles,
+                          const void *M, void *y, hipStream_t s) {
   const int rows = sizeof(T) == 2 ? 8 : 16;
   const int rt = (d.batch + rows - 1) / rows;
   const int K = d.n_q_heads * d.r_v, N = d.hidden;
   dim3 grid((N + 15) / 16), block(512);
   const T *Mt = (const T *)M;
   T *yt = (T *)y;
-  if (rt <= 1)
-    hipLaunchKernelGGL((reconstruct_kernel<T, 1>), grid, block, 0, s, u, Mt, yt, d.batch, K, N);
-  else if (rt <= 2)
-    hipLaunchKernelGGL((reconstruct_kernel<T, 2>), grid, block, 0, s, u, Mt, yt, d.batch, K, N);
-  else
-    hipLaunchKernelGGL((reconstruct_kernel<T, 4>), grid, block, 0, s, u, Mt, yt, d.batch, K, N);
+#define BKV_RECON(RTV, UTV)                                                                    \
+  hipLaunchKernelGGL((reconstruct_kernel<T, RTV, UTV>), grid, block, 0, s, u, u_tiles, Mt, yt, \
+                     d.batch, K, N)
+  const bool ut = sizeof(T) == 2 && u_tiles != nullptr;
+  if (rt <= 1) {
+    if (ut) BKV_RECON(1, true); else BKV_RECON(1, false);
+  } else if (rt <= 2) {
+    if (ut) BKV_RECON(2, true); else BKV_RECON(2, false);
+  } else {
+    if (ut) BKV_RECON(4, true); else BKV_RECON(4, false);
+  }
+#undef BKV_RECON
   return hipGetLastError();
 }
 
-hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const void *M, void *y,
-                              hipStream_t s) {
-  return d.dtype == BASISKV_BF16 ? recon_t<uint16_t>(d, u, M, y, s) : recon_t<float>(d, u, M, y, s);
+hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const uint16_t *u_tiles,
+                              const void *M, void *y, hipStream_t s) {
+  return d.dtype == BASISKV_BF16 ? recon_t<uint16_t>(d, u, u_tiles, M, y, s)
+                                 : recon_t<float>(d, u, nullptr, M, y, s);
 }
 
 template <typename T>

@@ -255,3 +255,36 @@ def test_all_scores_tied_selects_lowest_pages(wl_index, ctx):
         for g in range(wl.n_kv_heads):
             np.testing.assert_array_equal(out["sel"][b, g], np.arange(24))
     compare_step(wl, inp, prob, out, range(2))
+
+
+def untile_output_matrix(flat, hidden, K, itemsize):
+    """The documented tiled layout of the fused output matrix back to [hidden][K]."""
+    kl = 16 // itemsize
+    ks = 4 * kl
+    n = np.arange(hidden)[:, None]
+    k = np.arange(K)[None, :]
+    idx = ((n // 16 * (K // ks) + k // ks) * 64 + (k % ks) // kl * 16 + n % 16) * kl + k % kl
+    return flat[idx]
+
+
+@pytest.mark.parametrize("wl_index", [0, 2, 3])
+def test_fused_output_matrix_layout(wl_index):
+    """basiskv_fuse_output_matrix writes M = (blockdiag(B) W_O)^T in the tiled
+    layout the header documents (checked against numpy in float64)."""
+    wl = workload(wl_index)
+    inp = synth.decode_inputs(wl, batch=1, ctx=64)
+    prob = DecodeProblem(wl, inp)
+    st = inp["storage"]
+    K = wl.n_q_heads * wl.r_v
+    from sparse_decode_attention_latent_amd.runner import to_host_storage
+    flat = ref.storage_to_f64(to_host_storage(prob.M.reshape(-1), st), st)
+    got = untile_output_matrix(flat, wl.hidden, K, 2 if st == "bf16" else 4)
+    Bf = ref.storage_to_f64(inp["Bf"], st)
+    W_O = ref.storage_to_f64(inp["W_O"], st)
+    want = np.zeros((wl.hidden, K))
+    for h in range(wl.n_q_heads):
+        blk = Bf[h // wl.group] @ W_O[h * wl.head_dim:(h + 1) * wl.head_dim]  # [r_v, hidden]
+        want[:, h * wl.r_v:(h + 1) * wl.r_v] = blk.T
+    tol = 1e-5 if st == "f32" else 8e-3
+    err = np.abs(got - want).max() / np.abs(want).max()
+    assert err <= tol, err
