@@ -56,15 +56,16 @@ int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout:
-//   [0, C)       per-(sequence, KV head) counters with which the attention
+//   [0, C)       per-(sequence, query subgroup) counters with which the attention
 //                launch elects the workgroup that merges a row's splits;
 //                zero after allocation, and every call leaves them zero
 //   [C, C + U)   (bf16 decode step) u as the reconstruction's A operand
 //   [C + U, ..)  scratch: the projected queries during routing, then the
 //                attention splits' partial records (stream order keeps the
 //                two uses apart)
-size_t counter_bytes(const basiskv_dims &d) {
-  return align_up((size_t)d.batch * d.n_kv_heads * sizeof(int32_t));
+size_t counter_bytes(const basiskv_dims &d) {  // one per (sequence, query subgroup)
+  return align_up((size_t)d.batch * d.n_kv_heads * bkv_host::attend_group_split(d) *
+                  sizeof(int32_t));
 }
 
 size_t utile_bytes(const basiskv_dims &d) {

@@ -39,9 +39,10 @@ constexpr int kAttendBlocks = BKV_ATTEND_BLOCKS;  // 64-token blocks per wavefro
 
 struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
+  int gs;  // query subgroups per KV head (the kernel's group is n_q / n_kv / gs heads)
   int pages_per_split, n_split, total, padded;
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
-  int32_t *counters;  // [batch * n_kv], zero between calls (see the merge)
+  int32_t *counters;  // [batch * n_kv * gs], zero between calls (see the merge)
   uint16_t *u_tiles;  // optional: u also written as the reconstruction's A operand (bf16)
 };
 
@@ -58,12 +59,34 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Each wavefront owns kAttendBlocks 64-token blocks of the split; their
 // selection entries and block-table rows are requested before the queries are
 // staged, so the chain selection -> block table -> Key gather costs its
-// latency once per wavefront rather than once per block.  With a wide query
-// group (G * latent chunks > 48) the latent chunks are gathered after the
-// scores instead of beside the Key, keeping the live registers within two
-// wavefronts per SIMD.
+// latency once per wavefront rather than once per block.
+//
+// bf16: the scores of a query group of 2 to 8 heads run on the 4x4x4 bf16
+// matrix instruction (16 independent 4x4 products per wavefront: lane l
+// supplies 4 Key dims of its own token and receives its token's scores for
+// four heads, so the one-token-per-lane layout carries through), and the
+// next block's Key and latent chunks are requested as soon as the current
+// block has consumed the registers they land in, so the gathers of block
+// i + 1 are in flight while block i is scored and summed.
+// float32: the scores are float32 FMAs against the queries held in LDS, and
+// each block is gathered when it starts (latents after the scores: their
+// registers would not fit beside the Key).
+// Wavefronts per SIMD the register budget is sized for: two, except for the
+// widest bf16 groups, whose streamed Key (64) and latent (4 per token group)
+// registers and accumulators (8 per head) come to 170 or more of the 256,
+// leaving too few for the rest, and for float32 (a 128-register Key): these
+// take one wavefront per SIMD and its whole register file.
 template <typename T, int G, int NVC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BKV_ATTEND_WAVES_PER_EU)))
+constexpr int attend_waves_per_eu() {
+  constexpr int nj = (kWave + kWave / NVC - 1) / (kWave / NVC);
+  return sizeof(T) == 4 || 64 + 4 * nj + 8 * G >= 170 ? 1 : BKV_ATTEND_WAVES_PER_EU;
+}
+
+typedef short attend_s4 __attribute__((ext_vector_type(4)));
+typedef float attend_f4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int G, int NVC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<T, G, NVC>())))
 void attend_split_kernel(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ zpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -76,19 +99,34 @@ void attend_split_kernel(
   constexpr int NJ = (kWave + TG - 1) / TG;
   constexpr int NW = kAttendWaves;
   constexpr int NB = kAttendBlocks;
-  constexpr bool kZLate = G * NVC > 48 || sizeof(T) == 4;
+  constexpr bool kBf = sizeof(T) == 2;
+  constexpr bool kMfma = kBf;            // scores on the matrix cores
+  constexpr bool kStream = kBf;          // next block's gathers overlap this block
+  constexpr int QG = (G + 3) / 4;        // head quads (matrix-instruction row sets)
 
-  __shared__ __align__(16) float q_lds[G][kHeadDim];
+  // queries: matrix operands [quad][Key chunk][head in quad][8 dims] (bf16),
+  // else [head][dims] (packed bf16 pairs or float32)
+  __shared__ __align__(16) uint4 qa_lds[kMfma ? QG * NKC * 4 : 1];
+  __shared__ __align__(16) float q_lds[kMfma ? 1 : G][kMfma ? 4 : kHeadDim];
   __shared__ float p_lds[NW][G][kWave];
   __shared__ float m_lds[NW][G];
   __shared__ float l_lds[NW][G];
-  __shared__ float u_lds[NW][G][RV];
+  // token-group sums of HC heads at a time (the merge walks the group in passes)
+  constexpr int HC = (32768 / (NW * TG * RV * 4)) < 1 ? 1
+                     : (32768 / (NW * TG * RV * 4)) > G ? G : (32768 / (NW * TG * RV * 4));
+  static_assert(G % HC == 0, "head passes must tile the group");
+  __shared__ __align__(16) float u_part[NW][TG][HC][RV];
 
   const int work = xcd_work_index(a.padded);
   if (work >= a.total) return;  // uniform per workgroup
-  const int bg = work / a.n_split;
-  const int split = work - bg * a.n_split;
-  const int b = bg / a.n_kv, g = bg - b * a.n_kv;
+  // work item = (sequence, query subgroup, split); subgroup gv holds query
+  // heads gv G .. gv G + G - 1 and reads KV head g = gv / gs
+  const int bv = work / a.n_split;
+  const int split = work - bv * a.n_split;
+  const int nv = a.n_kv * a.gs;
+  const int b = bv / nv, gv = bv - b * nv;
+  const int g = gv / a.gs;
+  const int bg = b * a.n_kv + g;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -120,24 +158,33 @@ void attend_split_kernel(
   };
   fetch_pages(0);
 
-  // The group's queries: bf16 kept as packed pairs (the scores use the
-  // two-term bf16 dot instruction, products exact, float32 sums), float32 as is.
+  // ---- the group's queries into LDS ----
   {
-    constexpr int QW = G * kHeadDim * (int)sizeof(T) / 4;  // 32-bit words
-    constexpr int QL = (QW + 255) / 256;
-    const uint32_t *qg = reinterpret_cast<const uint32_t *>(
-        q + ((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim);
-    uint32_t *qw = reinterpret_cast<uint32_t *>(&q_lds[0][0]);
-    uint32_t qv[QL];
+    const T *qg = q + ((int64_t)b * a.n_q + (int64_t)gv * G) * kHeadDim;
+    if constexpr (kMfma) {
+      // entry (quad, chunk c, head hq): dims 8c .. 8c + 7 of head 4 quad + hq (zero past G)
+      for (int i = threadIdx.x; i < QG * NKC * 4; i += blockDim.x) {
+        const int hq = i & 3, c = (i >> 2) % NKC, qd = i / (NKC * 4);
+        const int h = qd * 4 + hq;
+        qa_lds[i] = h < G ? *reinterpret_cast<const uint4 *>(qg + h * kHeadDim + c * CE)
+                          : make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      constexpr int QW = G * kHeadDim * (int)sizeof(T) / 4;  // 32-bit words
+      constexpr int QL = (QW + 255) / 256;
+      const uint32_t *qw_g = reinterpret_cast<const uint32_t *>(qg);
+      uint32_t *qw = reinterpret_cast<uint32_t *>(&q_lds[0][0]);
+      uint32_t qv[QL];
 #pragma unroll
-    for (int u = 0; u < QL; ++u) {
-      const int i = u * 256 + threadIdx.x;
-      if (i < QW) qv[u] = qg[i];
-    }
+      for (int u = 0; u < QL; ++u) {
+        const int i = u * 256 + threadIdx.x;
+        if (i < QW) qv[u] = qw_g[i];
+      }
 #pragma unroll
-    for (int u = 0; u < QL; ++u) {
-      const int i = u * 256 + threadIdx.x;
-      if (i < QW) qw[i] = qv[u];
+      for (int u = 0; u < QL; ++u) {
+        const int i = u * 256 + threadIdx.x;
+        if (i < QW) qw[i] = qv[u];
+      }
     }
   }
   __syncthreads();
@@ -151,6 +198,40 @@ void attend_split_kernel(
   const int vc = lane % NVC;
   const int tg = lane / NVC;
 
+  auto lane_valid = [&](int i) {
+    const int tok = page[i] * a.page_size + slot;
+    return page[i] >= 0 && page[i] < NP && tok < L && phys[i] >= 0 && phys[i] < a.num_phys;
+  };
+  // block (r, i) is wavefront-uniformly present or absent
+  auto block_live = [&](int r, int i) { return (r * NB + i) * NW + wave < n_blocks; };
+
+  // byte offset of this lane's Key in block i
+  auto k_off = [&](int i) {
+    return (head_page0 + phys[i]) * kpage_bytes + (int64_t)slot * 16;
+  };
+  // latent chunk j of block i: token t = j * TG + tg, whose page lives in lane t;
+  // returns whether this lane loads it, and from where
+  auto z_src = [&](int i, bool v, int j, int64_t &off) {
+    const int t = j * TG + tg;
+    const bool role = tg < TG && t < kWave;
+    const int src = role ? t : 0;
+    const int phys_t = __shfl(phys[i], src);
+    const int valid_t = __shfl((int)v, src);
+    off = (head_page0 + phys_t) * zpage_bytes + vc * chunk_stride +
+          (int64_t)(src & (a.page_size - 1)) * 16;
+    return role && valid_t != 0;
+  };
+
+  // gather registers: streamed (bf16) they carry block i + 1's chunks while
+  // block i finishes; a lane with no valid token scores whatever they hold
+  // and masks the result
+  uint4 kc[NKC], zc[NJ];
+  bool zv[NJ];
+  if constexpr (kStream) {
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kc[c] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
   float m_run[G], l_lane[G], acc[G][CE];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -162,49 +243,70 @@ void attend_split_kernel(
 
   for (int r = 0; r < n_rounds; ++r) {
   if (r > 0) fetch_pages(r);
+  if constexpr (kStream) {  // the round's first block; later ones are requested by their predecessor
+    const bool v0 = lane_valid(0);
+    const int64_t ko = k_off(0);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      if (v0) kc[c] = load_chunk(kpool, ko + c * chunk_stride);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      int64_t zo;
+      zv[j] = z_src(0, v0, j, zo);
+      if (zv[j]) zc[j] = load_chunk(zpool, zo);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    if ((r * NB + i) * NW + wave >= n_blocks) break;  // wavefront-uniform
-    const int tok = page[i] * a.page_size + slot;
-    const bool valid = page[i] >= 0 && page[i] < NP && tok < L && phys[i] >= 0 &&
-                       phys[i] < a.num_phys;
-
-    // ---- gathers: this lane's Key, and the latent chunks it sums ----
-    uint4 kc[NKC];
-    if (valid) {
-      const int64_t koff = (head_page0 + phys[i]) * kpage_bytes + (int64_t)slot * 16;
+    if (!block_live(r, i)) break;  // wavefront-uniform
+    const bool valid = lane_valid(i);
+    const bool nxt = kStream && i + 1 < NB && block_live(r, i + 1);  // wavefront-uniform
+    const int inx = i + 1 < NB ? i + 1 : i;
+    const bool vn = nxt && lane_valid(inx);
+    const int64_t ko_next = k_off(inx);
+    if constexpr (!kStream) {
+      const int64_t ko = k_off(i);
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) kc[c] = load_chunk(kpool, koff + c * chunk_stride);
+      for (int c = 0; c < NKC; ++c)
+        if (valid) kc[c] = load_chunk(kpool, ko + c * chunk_stride);
     }
-    uint4 zc[NJ];
-    bool zv[NJ];
-    auto gather_latents = [&]() {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int t = j * TG + tg;
-        const bool role = tg < TG && t < kWave;
-        const int src = role ? t : 0;
-        const int phys_t = __shfl(phys[i], src);
-        const int valid_t = __shfl((int)valid, src);
-        zv[j] = role && valid_t;
-        if (zv[j])
-          zc[j] = load_chunk(zpool, (head_page0 + phys_t) * zpage_bytes + vc * chunk_stride +
-                                        (int64_t)(src & (a.page_size - 1)) * 16);
-      }
-    };
-    if (!kZLate) gather_latents();
 
     // ---- exact scores, one token per lane ----
     float s[G];
+    if constexpr (kMfma) {
+      attend_f4 sc[QG][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-    if (valid) {
+      for (int qd = 0; qd < QG; ++qd) sc[qd][0] = sc[qd][1] = attend_f4{0.f, 0.f, 0.f, 0.f};
+      const int hq = lane & 3;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const attend_s4 klo = __builtin_bit_cast(attend_s4, make_uint2(kc[c].x, kc[c].y));
+        const attend_s4 khi = __builtin_bit_cast(attend_s4, make_uint2(kc[c].z, kc[c].w));
+#pragma unroll
+        for (int qd = 0; qd < QG; ++qd) {
+          const uint4 qv = qa_lds[(qd * NKC + c) * 4 + hq];
+          const attend_s4 qlo = __builtin_bit_cast(attend_s4, make_uint2(qv.x, qv.y));
+          const attend_s4 qhi = __builtin_bit_cast(attend_s4, make_uint2(qv.z, qv.w));
+          sc[qd][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qlo, klo, sc[qd][0], 0, 0, 0);
+          sc[qd][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qhi, khi, sc[qd][1], 0, 0, 0);
+        }
+        if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float dot = sc[h / 4][0][h % 4] + sc[h / 4][1][h % 4];
+        s[h] = valid ? dot * a.scale_log2 : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = -INFINITY;
       float dot[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) dot[h] = 0.f;
+      // (float32: only lanes with a valid token, which have gathered this block)
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kBf) {
           const uint32_t *qw = reinterpret_cast<const uint32_t *>(&q_lds[0][0]);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
@@ -214,7 +316,8 @@ void attend_split_kernel(
             dot[h] = dot2_bf16(kc[c].z, q4.z, dot[h]);
             dot[h] = dot2_bf16(kc[c].w, q4.w, dot[h]);
           }
-        } else {
+          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);
+        } else if (valid) {
           float x[CE];
           unpack_chunk<T>(kc[c], x);
 #pragma unroll
@@ -228,10 +331,19 @@ void attend_split_kernel(
         }
         if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted query reads
       }
+      if (valid) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = dot[h] * a.scale_log2;
+        for (int h = 0; h < G; ++h) s[h] = dot[h] * a.scale_log2;
+      }
     }
-    if (kZLate) gather_latents();
+    if constexpr (!kStream) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        int64_t zo;
+        zv[j] = z_src(i, valid, j, zo);
+        if (zv[j]) zc[j] = load_chunk(zpool, zo);
+      }
+    }
 
     // ---- online softmax update (wavefront-uniform running max per head) ----
 #pragma unroll
@@ -251,7 +363,7 @@ void attend_split_kernel(
     }
     wave_lds_sync();
 
-    // ---- latent weighted sum ----
+    // ---- latent weighted sum; each chunk's registers then take block i + 1's ----
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (zv[j]) {
@@ -265,15 +377,20 @@ void attend_split_kernel(
           for (int ee = 0; ee < CE; ++ee) acc[h][ee] = fmaf(pr, x[ee], acc[h][ee]);
         }
       }
+      if (nxt) {
+        int64_t zo;
+        zv[j] = z_src(inx, vn, j, zo);
+        if (zv[j]) zc[j] = load_chunk(zpool, zo);
+      }
       if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted probability reads
     }
     wave_lds_sync();
-    // keep the next block's gathers from being hoisted into this one (registers)
+    // keep the next block's work from being hoisted into this one (registers)
     __builtin_amdgcn_sched_barrier(0);
   }
   }
 
-  // ---- merge inside the wavefront: token groups in a fixed order ----
+  // ---- per-wavefront softmax state into LDS ----
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float lw = wave_sum(l_lane[h]);
@@ -282,92 +399,119 @@ void attend_split_kernel(
       l_lds[wave][h] = lw;
     }
   }
-  for (int i = lane; i < G * RV; i += kWave) u_lds[wave][i / RV][i % RV] = 0.f;
-  wave_lds_sync();
-  for (int t = 0; t < TG; ++t) {
-    if (tg == t) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int ee = 0; ee < CE; ++ee) u_lds[wave][h][vc * CE + ee] += acc[h][ee];
-    }
-    wave_lds_sync();
-  }
-  __syncthreads();
 
-  // ---- merge the wavefronts; write u (one split) or this split's record ----
+  // ---- per pass of HC heads: the token groups' sums into LDS, then token
+  // groups and wavefronts merged in a fixed order; u written (one split) or
+  // this split's record ----
   const int rec = RV + 2;
-  for (int i = threadIdx.x; i < G * RV; i += blockDim.x) {
-    const int h = i / RV, d = i % RV;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][h]);
-    float lsum = 0.f, usum = 0.f;
-    if (M != -INFINITY) {
+  for (int h0 = 0; h0 < G; h0 += HC) {
+    if (h0 > 0) __syncthreads();  // the previous pass has read u_part
+    if (tg < TG) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(m_lds[w][h] - M);
-        lsum = fmaf(l_lds[w][h], f, lsum);
-        usum = fmaf(u_lds[w][h][d], f, usum);
+      for (int hh = 0; hh < HC; ++hh) {
+        float *dst = &u_part[wave][tg][hh][vc * CE];
+#pragma unroll
+        for (int ee = 0; ee < CE; ee += 4)
+          *reinterpret_cast<float4 *>(dst + ee) = make_float4(
+              acc[h0 + hh][ee], acc[h0 + hh][ee + 1], acc[h0 + hh][ee + 2], acc[h0 + hh][ee + 3]);
       }
     }
-    const int64_t row = (int64_t)b * a.n_q + (int64_t)g * G + h;
-    if (a.n_split == 1) {
-      const float uv = lsum > 0.f ? usum / lsum : 0.f;
-      u_out[row * RV + d] = uv;
-      if (a.u_tiles) store_u_tiles(a.u_tiles, b, (g * G + h) * RV + d, a.n_q * RV, uv);
-    } else {
-      float *rp = part + (row * a.n_split + split) * rec;
-      store_coherent(rp + 2 + d, usum);
-      if (d == 0) {
-        store_coherent(rp, M);
-        store_coherent(rp + 1, lsum);
+    __syncthreads();
+    for (int i = threadIdx.x; i < HC * RV; i += blockDim.x) {
+      const int hh = i / RV, d = i % RV, h = h0 + hh;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][h]);
+      float lsum = 0.f, usum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          float uw = 0.f;
+#pragma unroll
+          for (int t = 0; t < TG; ++t) uw += u_part[w][t][hh][d];
+          const float f = exp2f(m_lds[w][h] - M);
+          lsum = fmaf(l_lds[w][h], f, lsum);
+          usum = fmaf(uw, f, usum);
+        }
+      }
+      const int64_t row = (int64_t)b * a.n_q + (int64_t)gv * G + h;
+      if (a.n_split == 1) {
+        const float uv = lsum > 0.f ? usum / lsum : 0.f;
+        u_out[row * RV + d] = uv;
+        if (a.u_tiles) store_u_tiles(a.u_tiles, b, (gv * G + h) * RV + d, a.n_q * RV, uv);
+      } else {
+        float *rp = part + (row * a.n_split + split) * rec;
+        store_coherent(rp + 2 + d, usum);
+        if (d == 0) {
+          store_coherent(rp, M);
+          store_coherent(rp + 1, lsum);
+        }
       }
     }
   }
   if (a.n_split == 1) return;
 
-  // ---- the last split of the (sequence, KV head) to finish merges them all ----
+  // ---- the last split of the (sequence, query subgroup) to finish merges them all ----
   //   u = sum_s u_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),  M = max_s m_s,
-  // in split order; a head with no valid token gets u = 0.
-  if (!last_to_arrive(a.counters + bg, a.n_split)) return;
-  constexpr int U = 8;  // records read per batch of loads
-  for (int i = threadIdx.x; i < G * RV; i += blockDim.x) {
-    const int h = i / RV, d = i % RV;
-    const int64_t row = (int64_t)b * a.n_q + (int64_t)g * G + h;
-    const float *base = part + row * a.n_split * rec;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < a.n_split; s0 += U) {
-      float m[U];
+  // in split order (running maximum per batch of records, earlier sums
+  // rescaled when it grows); a head with no valid token gets u = 0.  Every
+  // thread requests the records of all its outputs before combining any.
+  if (!last_to_arrive(a.counters + bv, a.n_split)) return;
+  constexpr int NT = NW * kWave;
+  constexpr int NI = (G * RV + NT - 1) / NT;     // outputs per thread
+  constexpr int U = 16 / NI < 4 ? 4 : 16 / NI;   // records per batch of loads
+  float Mx[NI], lsum[NI], usum[NI];
 #pragma unroll
-      for (int k = 0; k < U; ++k)
-        m[k] = s0 + k < a.n_split ? load_coherent(base + (s0 + k) * rec) : -INFINITY;
+  for (int n = 0; n < NI; ++n) {
+    Mx[n] = -INFINITY;
+    lsum[n] = usum[n] = 0.f;
+  }
+  for (int s0 = 0; s0 < a.n_split; s0 += U) {
+    float m[NI][U], l[NI][U], uu[NI][U];
 #pragma unroll
-      for (int k = 0; k < U; ++k) M = fmaxf(M, m[k]);
-    }
-    float lsum = 0.f, usum = 0.f;
-    if (M != -INFINITY) {
-      for (int s0 = 0; s0 < a.n_split; s0 += U) {
-        float m[U], l[U], uu[U];
+    for (int n = 0; n < NI; ++n) {
+      const int i = n * NT + threadIdx.x;
+      const int h = i / RV, d = i % RV;
+      const float *base = part + ((int64_t)b * a.n_q + (int64_t)gv * G + h) * a.n_split * rec;
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-          const bool ok = s0 + k < a.n_split;
-          const float *r = base + (s0 + k) * rec;
-          m[k] = ok ? load_coherent(r) : -INFINITY;
-          l[k] = ok ? load_coherent(r + 1) : 0.f;
-          uu[k] = ok ? load_coherent(r + 2 + d) : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-          const float f = exp2f(m[k] - M);
-          lsum = fmaf(l[k], f, lsum);
-          usum = fmaf(uu[k], f, usum);
-        }
+      for (int k = 0; k < U; ++k) {
+        const bool ok = i < G * RV && s0 + k < a.n_split;
+        const float *r = base + (s0 + k) * rec;
+        m[n][k] = ok ? load_coherent(r) : -INFINITY;
+        l[n][k] = ok ? load_coherent(r + 1) : 0.f;
+        uu[n][k] = ok ? load_coherent(r + 2 + d) : 0.f;
       }
     }
-    const float uv = lsum > 0.f ? usum / lsum : 0.f;
-    u_out[row * RV + d] = uv;
-    if (a.u_tiles) store_u_tiles(a.u_tiles, b, (g * G + h) * RV + d, a.n_q * RV, uv);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      float Mb = Mx[n];
+#pragma unroll
+      for (int k = 0; k < U; ++k) Mb = fmaxf(Mb, m[n][k]);
+      if (Mb != -INFINITY) {
+        const float f0 = exp2f(Mx[n] - Mb);  // 0 while the maximum is -inf
+        lsum[n] *= f0;
+        usum[n] *= f0;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          const float f = exp2f(m[n][k] - Mb);
+          lsum[n] = fmaf(l[n][k], f, lsum[n]);
+          usum[n] = fmaf(uu[n][k], f, usum[n]);
+        }
+        Mx[n] = Mb;
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int i = n * NT + threadIdx.x;
+    if (i < G * RV) {
+      const int h = i / RV, d = i % RV;
+      const int64_t row = (int64_t)b * a.n_q + (int64_t)gv * G + h;
+      const float uv = lsum[n] > 0.f ? usum[n] / lsum[n] : 0.f;
+      u_out[row * RV + d] = uv;
+      if (a.u_tiles) store_u_tiles(a.u_tiles, b, (gv * G + h) * RV + d, a.n_q * RV, uv);
+    }
   }
 }
 
@@ -398,6 +542,17 @@ static int ilog2i(int x) {
   return l;
 }
 
+// Query subgroups per KV head.  A bf16 group of 8 heads with latents of 96 or
+// more dims is taken as two groups of 4 sharing the KV head's pages: the
+// 8-head kernel needs the whole register file (one wavefront per SIMD, little
+// latency hiding), two 4-head wavefronts fit two per SIMD and each does half
+// the arithmetic, at the price of gathering the pages twice (the second time
+// mostly from cache).
+int attend_group_split(const basiskv_dims &d) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  return d.dtype == BASISKV_BF16 && G == 8 && d.r_v >= 96 ? 2 : 1;
+}
+
 // Pages per split.  Every wavefront takes up to kAttendBlocks 64-token blocks
 // per round; a split is one round when there is work enough for about two
 // workgroups per compute unit at that size, otherwise one block per
@@ -405,7 +560,8 @@ static int ilog2i(int x) {
 // that would leave more than kMaxSplits splits (the kernel loops over them).
 static int pages_per_split(const basiskv_dims &d, int32_t top_k) {
   const int ppi = 64 / d.page_size;
-  const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * (((int64_t)top_k + ppi - 1) / ppi);
+  const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * attend_group_split(d) *
+                         (((int64_t)top_k + ppi - 1) / ppi);
   const int per_wave = blocks >= (int64_t)kAttendWaves * kAttendBlocks * 512 ? kAttendBlocks : 1;
   const int per_round = kAttendWaves * per_wave * ppi;
   int rounds = 1;
@@ -425,8 +581,9 @@ int attend_splits(const basiskv_dims &d, int32_t top_k) {
 
 static const void *find_attend(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
+  const int gs = attend_group_split(d);
   for (const auto &v : kAttendVariants)
-    if (v.dtype == d.dtype && v.G == G && v.rv == d.r_v) return v.fn;
+    if (v.dtype == d.dtype && v.G == G / gs && v.rv == d.r_v) return v.fn;
   return nullptr;
 }
 
@@ -450,9 +607,10 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.log2_page = ilog2i(d.page_size);
   a.cap = d.max_pages_per_seq * d.page_size;
   a.top_k = top_k;
+  a.gs = attend_group_split(d);
   a.pages_per_split = pages_per_split(d, top_k);
   a.n_split = attend_splits(d, top_k);
-  a.total = d.batch * d.n_kv_heads * a.n_split;
+  a.total = d.batch * d.n_kv_heads * a.gs * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
   a.scale_log2 = scale * kLog2e;
   a.counters = counters;

@@ -207,6 +207,7 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
 hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s);
 int attend_splits(const basiskv_dims &d, int32_t top_k);
+int attend_group_split(const basiskv_dims &d);
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
                          int32_t *counters, uint16_t *u_tiles, hipStream_t s, bool *unsupported);
