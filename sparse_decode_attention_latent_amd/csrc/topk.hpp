@@ -1,0 +1,158 @@
+// Exact top-k of one score row per workgroup (or wavefront): the selection
+// step of BasisKV's routing (arXiv 2611.02583, Table 9's caption: pages are
+// chosen by score under a page budget).  Shared by the standalone selection
+// kernel and the attention launch that selects its own pages.
+//
+// Scores become order-preserving 32-bit keys held in registers, up to KPT per
+// lane.  The k-th largest key tau is built one bit at a time from the top (a
+// candidate is kept when at least k keys reach it; counts by wavefront
+// ballots, and, with several wavefronts, one LDS exchange and barrier per
+// bit).  Bits that every valid key shares -- above the highest bit in which
+// the largest and smallest keys differ -- are taken as given, and the search
+// stops as soon as exactly k keys reach the candidate (the top-k set is then
+// decided, whatever the lower bits of the k-th key).  The compaction
+// then hands out, in page order, every page whose key exceeds tau and the
+// lowest-index pages equal to it; positions come from ballot popcounts.
+#pragma once
+#include "common.hpp"
+
+namespace bkv {
+
+// Order-preserving key of a score: larger score, larger key.  -0 and +0 are
+// one key; NaN ranks below every number; 0 is left for lanes past the row.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 1u;
+  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wavefront-uniform maximum and minimum of unsigned values.
+__device__ __forceinline__ void wave_max_min_u32(uint32_t &mx, uint32_t &mn) {
+#define BKV_STEP(C)                            \
+  mx = max(mx, dpp_move_u32<C>(mx));           \
+  mn = min(mn, dpp_move_u32<C>(mn));
+  BKV_STEP(0xB1) BKV_STEP(0x4E) BKV_STEP(0x141) BKV_STEP(0x140)
+#undef BKV_STEP
+  uint32_t a = 0, b = ~0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    a = max(a, (uint32_t)__builtin_amdgcn_readlane((int)mx, 16 * r));
+    b = min(b, (uint32_t)__builtin_amdgcn_readlane((int)mn, 16 * r));
+  }
+  mx = a;
+  mn = b;
+}
+
+// Top-k of one score row, run by NWV whole wavefronts (threads 0 .. 64 NWV - 1).
+// Page i = 64 (kpt w + j) + l is held by lane l of wavefront w as key j, for
+// j < kpt <= KPT (kpt is uniform; a wavefront loads 64 consecutive scores per
+// instruction); v[j] is its score (any value past the row).  Requires
+// NP <= 64 NWV kpt and 1 <= k < NP.  emit(pos, j) is called by the lane
+// holding the selected page 64 (kpt w + j) + l at position pos (page order).
+template <int KPT, int NWV, typename Emit>
+__device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP, int k,
+                                         Emit &&emit) {
+  __shared__ int xch[2][NWV > 1 ? NWV : 1][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = wave * 64 * kpt + lane;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint32_t key[KPT];
+  uint32_t kmax = 0u, kmin = ~0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool ok = j < kpt && base + 64 * j < NP;
+    key[j] = ok ? order_key(v[j]) : 0u;
+    kmax = ok ? max(kmax, key[j]) : kmax;
+    kmin = ok ? min(kmin, key[j]) : kmin;
+  }
+  // ---- leading bits shared by every valid key ----
+  wave_max_min_u32(kmax, kmin);
+  if (NWV > 1) {
+    if (lane == 0) {
+      xch[0][wave][0] = (int)kmax;
+      xch[0][wave][1] = (int)kmin;
+    }
+    __syncthreads();
+    kmax = 0u;
+    kmin = ~0u;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      kmax = max(kmax, (uint32_t)xch[0][w][0]);
+      kmin = min(kmin, (uint32_t)xch[0][w][1]);
+    }
+    __syncthreads();
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int top = diff ? 31 - __clz(diff) : -1;  // -1: every valid key is equal
+  uint32_t tau = top < 0 ? kmax : top == 31 ? 0u : kmax & ~((2u << top) - 1u);
+  // ---- tau, bit by bit (keys past the row are 0 and reach no candidate) ----
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j < kpt) cnt += __popcll(__ballot(key[j] >= cand));
+    if (NWV > 1) {
+      if (lane == 0) xch[bit & 1][wave][0] = cnt;
+      __syncthreads();
+      cnt = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) cnt += xch[bit & 1][w][0];
+    }
+    if (cnt >= k) tau = cand;
+    if (cnt == k) break;  // exactly k keys reach tau: the set is decided (uniform)
+  }
+  // ---- compaction in page order: every key above tau, then the lowest-index
+  // keys equal to tau up to k in all (tau >= 1: keys past the row never take part;
+  // after an early stop every key reaching tau is taken) ----
+  int gt_run = 0, eq_run = 0, total_gt = 0;
+  if (NWV > 1) {
+    int gt_w = 0, eq_w = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (j < kpt) {
+        gt_w += __popcll(__ballot(key[j] > tau));
+        eq_w += __popcll(__ballot(key[j] == tau));
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      xch[0][wave][0] = gt_w;
+      xch[0][wave][1] = eq_w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const int g = xch[0][w][0], e = xch[0][w][1];
+      total_gt += g;
+      if (w < wave) {
+        gt_run += g;
+        eq_run += e;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j < kpt) total_gt += __popcll(__ballot(key[j] > tau));
+  }
+  const int need = k - total_gt;  // keys equal to tau to take (>= 1)
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (j < kpt) {
+      const uint64_t m_gt = __ballot(key[j] > tau);
+      const uint64_t m_eq = __ballot(key[j] == tau);
+      const int eq_pos = eq_run + __popcll(m_eq & below);
+      const bool take = key[j] > tau || (key[j] == tau && eq_pos < need);
+      if (take) emit(gt_run + __popcll(m_gt & below) + min(eq_pos, need), j);
+      gt_run += __popcll(m_gt);
+      eq_run += __popcll(m_eq);
+    }
+  }
+}
+
+}  // namespace bkv
