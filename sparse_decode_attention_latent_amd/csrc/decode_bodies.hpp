@@ -25,6 +25,31 @@ struct AppendArgs {
   int n_tokens, n_kv, rv, rb, rq, max_pages, num_phys, page_size, cap;
 };
 
+// Sums over the slices of a phase.  Lane l of a wavefront holds the partial
+// of chunk l % cp over one slice (cp a power of two): the wavefront's slices
+// are summed by butterflies over the lanes l ^ cp, l ^ 2 cp, ..., after which
+// lanes l < cp hold the wavefront's sums; those go to red[wave], and after a
+// barrier output n is red[0][n] + red[1][n] + red[2][n] + red[3][n].
+template <int CE>
+__device__ __forceinline__ void slice_sums(float (&acc)[CE], int cp, int c, int n_chunks,
+                                           float (*red)[kHeadDim]) {
+  for (int m = cp; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], m);
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  if (lane < cp && c < n_chunks) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) red[wave][c * CE + e] = acc[e];
+  }
+}
+
+__device__ __forceinline__ int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
 // Compression of token `row` (= b * n_tokens + t) for KV head g, by a
 // workgroup of 256 threads.
 template <typename T>
@@ -37,23 +62,23 @@ __device__ __forceinline__ void append_body(
   constexpr int CE = Elem<T>::CE;
   constexpr int MAXL = 64 / CE;  // factor chunks per thread and phase (see the roles below)
   __shared__ float v_s[DH], k_s[DH], x_s[DH], zf[DH];
-  __shared__ float red[256 * CE];
+  __shared__ float red[4][DH];
   __shared__ __align__(16) T zst[DH];
   __shared__ __align__(16) T rst[DH];
   const int b = row / a.n_tokens, t = row - b * a.n_tokens;
   const int tid = threadIdx.x;
   const int64_t in_off = (((int64_t)b * a.n_tokens + t) * a.n_kv + g) * DH;
 
-  // Roles: each phase splits its output into 16-byte chunks (C) and its
-  // contraction into slices (S = 256 / C, L entries each); thread (c, s) sums
-  // slice s of chunk c.  Every factor chunk is requested up front, since none
-  // depends on the token.
-  const int C1 = a.rv / CE, S1 = 256 / C1, L1 = (DH + S1 - 1) / S1;    // z = v A
-  const int C2 = DH / CE, S2 = 256 / C2, L2 = (a.rb + S2 - 1) / S2;    // c = z_s P
-  const int C3 = a.rq / CE, S3 = 256 / C3, L3 = (DH + S3 - 1) / S3;    // r = x E
-  const int c1 = tid % C1, s1 = tid / C1;
-  const int c2 = tid % C2, s2 = tid / C2;
-  const int c3 = tid % C3, s3 = tid / C3;
+  // Roles: each phase splits its output into 16-byte chunks (C of them,
+  // padded to a power of two Cp) and its contraction into S = 256 / Cp slices
+  // of L entries; thread tid sums slice tid / Cp of chunk tid % Cp.  Every
+  // factor chunk is requested up front, since none depends on the token.
+  const int C1 = a.rv / CE, P1 = pow2_at_least(C1), S1 = 256 / P1, L1 = (DH + S1 - 1) / S1;
+  const int C2 = DH / CE, P2 = pow2_at_least(C2), S2 = 256 / P2, L2 = (a.rb + S2 - 1) / S2;
+  const int C3 = a.rq / CE, P3 = pow2_at_least(C3), S3 = 256 / P3, L3 = (DH + S3 - 1) / S3;
+  const int c1 = tid % P1, s1 = tid / P1;  // z = v A
+  const int c2 = tid % P2, s2 = tid / P2;  // c = z_s P
+  const int c3 = tid % P3, s3 = tid / P3;  // r = x E
   const T *Ag = A + (int64_t)g * DH * a.rv;
   const T *Pg = P + (int64_t)g * a.rb * DH;
   const T *Eg = E + (int64_t)g * DH * a.rq;
@@ -61,13 +86,13 @@ __device__ __forceinline__ void append_body(
 #pragma unroll
   for (int l = 0; l < MAXL; ++l) {
     const int d = s1 * L1 + l;
-    if (s1 < S1 && l < L1 && d < DH)
+    if (c1 < C1 && l < L1 && d < DH)
       fa[l] = *reinterpret_cast<const uint4 *>(Ag + (int64_t)d * a.rv + c1 * CE);
     const int j = s2 * L2 + l;
-    if (s2 < S2 && l < L2 && j < a.rb)
+    if (c2 < C2 && l < L2 && j < a.rb)
       fp[l] = *reinterpret_cast<const uint4 *>(Pg + (int64_t)j * DH + c2 * CE);
     const int d3 = s3 * L3 + l;
-    if (s3 < S3 && l < L3 && d3 < DH)
+    if (c3 < C3 && l < L3 && d3 < DH)
       fe[l] = *reinterpret_cast<const uint4 *>(Eg + (int64_t)d3 * a.rq + c3 * CE);
   }
   // the destination slot, looked up while the factors are in flight
@@ -86,7 +111,7 @@ __device__ __forceinline__ void append_body(
   // ---- z = v A_g; z_s = round(z) ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (s1 < S1) {
+  if (c1 < C1) {
 #pragma unroll
     for (int l = 0; l < MAXL; ++l) {
       const int d = s1 * L1 + l;
@@ -98,13 +123,11 @@ __device__ __forceinline__ void append_body(
         for (int e = 0; e < CE; ++e) acc[e] = fmaf(vd, x[e], acc[e]);
       }
     }
-#pragma unroll
-    for (int e = 0; e < CE; ++e) red[s1 * a.rv + c1 * CE + e] = acc[e];
   }
+  slice_sums<CE>(acc, P1, c1, C1, red);
   __syncthreads();
   if (tid < a.rv) {
-    float z = 0.f;
-    for (int s = 0; s < S1; ++s) z += red[s * a.rv + tid];
+    const float z = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     const T zs = from_f32<T>(z);
     zst[tid] = zs;
     zf[tid] = to_f32(zs);
@@ -114,7 +137,7 @@ __device__ __forceinline__ void append_body(
   // ---- x = k - z_s[:r_b] P_g ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (s2 < S2) {
+  if (c2 < C2) {
 #pragma unroll
     for (int l = 0; l < MAXL; ++l) {
       const int j = s2 * L2 + l;
@@ -126,21 +149,16 @@ __device__ __forceinline__ void append_body(
         for (int e = 0; e < CE; ++e) acc[e] = fmaf(zj, x[e], acc[e]);
       }
     }
-#pragma unroll
-    for (int e = 0; e < CE; ++e) red[s2 * DH + c2 * CE + e] = acc[e];
   }
+  slice_sums<CE>(acc, P2, c2, C2, red);
   __syncthreads();
-  if (tid < DH) {
-    float c = 0.f;
-    for (int s = 0; s < S2; ++s) c += red[s * DH + tid];
-    x_s[tid] = k_s[tid] - c;
-  }
+  if (tid < DH) x_s[tid] = k_s[tid] - (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
   __syncthreads();
 
   // ---- r = x E_g; r_s = round(r) ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (s3 < S3) {
+  if (c3 < C3) {
 #pragma unroll
     for (int l = 0; l < MAXL; ++l) {
       const int d = s3 * L3 + l;
@@ -152,15 +170,11 @@ __device__ __forceinline__ void append_body(
         for (int e = 0; e < CE; ++e) acc[e] = fmaf(xd, x[e], acc[e]);
       }
     }
-#pragma unroll
-    for (int e = 0; e < CE; ++e) red[s3 * a.rq + c3 * CE + e] = acc[e];
   }
+  slice_sums<CE>(acc, P3, c3, C3, red);
   __syncthreads();
-  if (tid < a.rq) {
-    float r = 0.f;
-    for (int s = 0; s < S3; ++s) r += red[s * a.rq + tid];
-    rst[tid] = from_f32<T>(r);
-  }
+  if (tid < a.rq)
+    rst[tid] = from_f32<T>(red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
   __syncthreads();
 
   // ---- page stores: one 16-byte chunk per thread ----
