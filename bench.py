@@ -8,8 +8,8 @@ projection, page scoring, top-k selection, sparse attention, reconstruction).
 Inputs are seeded synthetic arrays already resident in device memory when
 the timed region starts; K steps run back to back on one stream and are
 bracketed by torch.cuda.synchronize().  A second pass runs the same step as
-its separate library calls with HIP events recorded on that stream between
-them, which gives every launch's average duration.
+its separate library calls, each call K times back to back between two HIP
+events recorded on that stream, which gives every launch's average duration.
 
 The default workload is the Llama-3.1-8B-shaped layer at 32K context
 (batch 8, 32 query / 8 KV heads, head dim 128, latent width 64, residual
@@ -222,8 +222,6 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs resident ({time.perf_counter() - t0:.1f} s)")
 
-    # the routing call's two launches are timed apart: query projection, then
-    # page scoring with the top-k selection fused in (the dominant kernel)
     # the step as one library call (five launches: compression + projection,
     # scoring, selection, attention, reconstruction)
     for _ in range(args.warmup):
@@ -245,22 +243,32 @@ def main():
     ms_per_step = wall / K * 1e3
     log(f"[bench] timed {K} steps in {wall * 1e3:.2f} ms")
 
-    # per-launch durations: the same step as its separate calls, with HIP
-    # events recorded on the library's stream between them
+    # per-launch durations: each stage's library call K times back to back
+    # on the same stream, bracketed by one pair of HIP events (average per
+    # launch, including the gap between consecutive launches); a stage whose
+    # host-side call takes about as long as its launch is marked host-bound
     stages = ("append", "project", "score", "select", "attend", "reconstruct")
     calls = [prob.append, prob.project, prob.score, prob.select, prob.attend, prob.reconstruct]
     for _ in range(2):
         prob.step_unfused()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record()
-        for j, c in enumerate(calls):
-            c()
-            ev[i][j + 1].record()
+    per_stage, host_bound = {}, {}
+    for s_name, call in zip(stages, calls):
+        call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for _ in range(K):
+            call()
+        e1.record()
+        host_us = (time.perf_counter() - h0) / K * 1e6
+        torch.cuda.synchronize()
+        per_stage[s_name] = e0.elapsed_time(e1) / K * 1e3
+        host_bound[s_name] = host_us >= 0.9 * per_stage[s_name]
+    prob.step_unfused()  # leave the cache and outputs as one step leaves them
     torch.cuda.synchronize()
-    per_stage = {s: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K * 1e3
-                 for j, s in enumerate(stages)}
 
     shape = _shape(wl_step, inp["q"].shape[0], inp)
     sb = traffic.step_bytes(shape, inp["seq_lens"])
@@ -286,6 +294,7 @@ def main():
                    "r_v": wl.r_v, "r_b": wl.r_b, "r_q": wl.r_q, "top_k": wl.top_k},
         "algorithmic_bytes_per_step": sb["total"],
         "stages_us": {k: round(v, 3) for k, v in per_stage.items()},
+        "stages_host_bound": [k for k in stages if host_bound[k]],
         "stages_gbs": {k: round(sb[k] / (per_stage[k] * 1e-6) / 1e9, 1) for k in stages},
         "roofline": {"kernel": "route_scan_kernel (page scoring)", "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

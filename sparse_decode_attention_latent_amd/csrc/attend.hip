@@ -56,7 +56,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Partial record per (b, h, split): [m, l, u[0..r_v)] with m in base-2 logit
 // units (scale * log2 e already applied), l = sum 2^(s - m), u = sum 2^(s - m) z.
 //
-// Each wavefront owns kAttendBlocks 64-token blocks of the split; their
+// Each wavefront owns up to NB 64-token blocks of the split per round (NB is
+// 1, or kAttendBlocks when the split is that long); their
 // selection entries and block-table rows are requested before the queries are
 // staged, so the chain selection -> block table -> Key gather costs its
 // latency once per wavefront rather than once per block.
@@ -85,7 +86,7 @@ constexpr int attend_waves_per_eu() {
 typedef short attend_s4 __attribute__((ext_vector_type(4)));
 typedef float attend_f4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int G, int NVC>
+template <typename T, int G, int NVC, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<T, G, NVC>())))
 void attend_split_kernel(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ zpool,
@@ -98,7 +99,6 @@ void attend_split_kernel(
   constexpr int TG = kWave / NVC;     // token groups in the latent phase
   constexpr int NJ = (kWave + TG - 1) / TG;
   constexpr int NW = kAttendWaves;
-  constexpr int NB = kAttendBlocks;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr bool kMfma = kBf;            // scores on the matrix cores
   constexpr bool kStream = kBf;          // next block's gathers overlap this block
@@ -517,11 +517,13 @@ void attend_split_kernel(
 
 struct AttendVariant {
   int dtype, G, rv;
-  const void *fn;
+  const void *fn1, *fn;  // one block per wavefront and round; kAttendBlocks
 };
 
-#define BKV_ATT(T, DT, G, RV) \
-  {DT, G, RV, reinterpret_cast<const void *>(&attend_split_kernel<T, G, (RV) / Elem<T>::CE>)}
+#define BKV_ATT(T, DT, G, RV)                                                                   \
+  {DT, G, RV,                                                                                   \
+   reinterpret_cast<const void *>(&attend_split_kernel<T, G, (RV) / Elem<T>::CE, 1>),          \
+   reinterpret_cast<const void *>(&attend_split_kernel<T, G, (RV) / Elem<T>::CE, kAttendBlocks>)}
 #define BKV_ATT_G(T, DT, RV) \
   BKV_ATT(T, DT, 1, RV), BKV_ATT(T, DT, 2, RV), BKV_ATT(T, DT, 4, RV), BKV_ATT(T, DT, 8, RV)
 
@@ -579,11 +581,11 @@ int attend_splits(const basiskv_dims &d, int32_t top_k) {
   return (top_k + pps - 1) / pps;
 }
 
-static const void *find_attend(const basiskv_dims &d) {
+static const AttendVariant *find_attend(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   const int gs = attend_group_split(d);
   for (const auto &v : kAttendVariants)
-    if (v.dtype == d.dtype && v.G == G / gs && v.rv == d.r_v) return v.fn;
+    if (v.dtype == d.dtype && v.G == G / gs && v.rv == d.r_v) return &v;
   return nullptr;
 }
 
@@ -592,8 +594,8 @@ bool attend_supported(const basiskv_dims &d) { return find_attend(d) != nullptr;
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
                          int32_t *counters, uint16_t *u_tiles, hipStream_t s, bool *unsupported) {
-  const void *fn = find_attend(d);
-  if (!fn) {
+  const AttendVariant *v = find_attend(d);
+  if (!v) {
     *unsupported = true;
     return hipSuccess;
   }
@@ -618,7 +620,9 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};
-  return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
+  // a split of at most one block per wavefront takes the one-block kernel
+  const bool one = a.pages_per_split <= kAttendWaves * (64 / d.page_size);
+  return hipLaunchKernel(one ? v->fn1 : v->fn, dim3(a.padded), dim3(256), args, 0, s);
 }
 
 }  // namespace bkv_host
