@@ -46,8 +46,11 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a step is ~0.1 ms: a few hundred steps give a timed region of tens of
+    # milliseconds, long enough for clocks and caches to settle (a 50-step
+    # run after 5 warm-up steps reads about 4% slower)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b-ctx32k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip)")

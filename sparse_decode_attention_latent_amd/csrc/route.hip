@@ -47,18 +47,16 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // ---------------------------------------------------------------------------
 // (a2) page scores.
 //
-// One lane per token: a wavefront covers 64 tokens (64 / page_size pages) per
-// step, each lane issuing NZ + NR 16-byte loads (its token's chunks of the
+// One lane per token: a wavefront scores one 64-token step (64 / page_size
+// pages), each lane issuing NZ + NR 16-byte loads (its token's chunks of the
 // latent and residual pages).  With the chunk-major page layout those loads
 // are page_size * 16 contiguous bytes per chunk, i.e. fully coalesced.  The
 // projected queries are wave-uniform and are read through the scalar cache,
 // so every FMA takes one scalar and one vector operand.  Page maxima are
-// butterfly reductions over the page's lanes.
+// butterfly reductions over the page's lanes.  A workgroup is four such
+// steps: many short workgroups keep more loads in flight than a few long
+// ones walking several steps each.
 // ---------------------------------------------------------------------------
-#ifndef BKV_ROUTE_STEPS
-#define BKV_ROUTE_STEPS 1
-#endif
-constexpr int kRouteSteps = BKV_ROUTE_STEPS;
 
 struct ScoreArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, zc_total, cap;
@@ -95,7 +93,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int64_t page_z_bytes = (int64_t)a.zc_total * a.page_size * 16;
   const int64_t page_r_bytes = (int64_t)NR * a.page_size * 16;
 
-  for (int step = wave; step < n_steps; step += 4) {
+  if (const int step = wave; step < n_steps) {
     const int p = p_begin + step * ppi + (lane >> a.log2_page);
     const bool in_range = p < p_end;
     const int tok = p * a.page_size + slot;
@@ -219,9 +217,9 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   a.log2_page = ilog2(d.page_size);
   a.zc_total = d.r_v / ce;
   a.cap = d.max_pages_per_seq * d.page_size;
-  // 4 wavefronts per workgroup, each streaming kRouteSteps steps of 64 tokens.
+  // 4 wavefronts per workgroup, one step of 64 tokens each
   const int ppi = 64 / d.page_size;
-  a.pages_per_wg = ppi * 4 * kRouteSteps;
+  a.pages_per_wg = ppi * 4;
   a.chunks_per_bg = (d.max_pages_per_seq + a.pages_per_wg - 1) / a.pages_per_wg;
   a.total = d.batch * d.n_kv_heads * a.chunks_per_bg;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
