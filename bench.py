@@ -111,9 +111,13 @@ def pmc_summary(fetch_dir, write_dir, workload_name):
                            "write_size_kib": round(write["calib"], 1),
                            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
            "hbm_bytes_per_launch": round(hbm),
-           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 "
-                        f"bench.py --workload {workload_name} --steps 5 --warmup 2 --cpu-seconds 0 "
-                        f"--calibration-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+           "commands": [f"cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} --output-format csv -d "
+                        f"$REPO/{os.path.relpath(d, ROOT)} -o run -- python3 $REPO/bench.py "
+                        f"--workload {workload_name} --steps 5 --warmup 2 --cpu-seconds 0 "
+                        f"--calibration-copy"
+                        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))],
+           "summary_command": f"python3 bench.py --workload {workload_name} --pmc-summary "
+                              f"{os.path.relpath(fetch_dir, ROOT)} {os.path.relpath(write_dir, ROOT)}"}
     os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
     with open(PMC_SUMMARY, "w") as f:
         json.dump(out, f, indent=1)
