@@ -10,6 +10,10 @@ the timed region starts; K steps run back to back on one stream and are
 bracketed by torch.cuda.synchronize().  A second pass runs the same step as
 its separate library calls, each call K times back to back between two HIP
 events recorded on that stream, which gives every launch's average duration.
+Then 100 steps are timed one by one with L2 and the memory-side cache flushed
+before each ("cold_step"); for the prefill + decode workload, the prompts'
+compression and the 128 decode steps of growing context are timed as well
+("prefill", "decode_sequence").
 
 The default workload is the Llama-3.1-8B-shaped layer at 32K context
 (batch 8, 32 query / 8 KV heads, head dim 128, latent width 64, residual
@@ -52,6 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b-ctx32k")
+    ap.add_argument("--cold-steps", type=int, default=100,
+                    help="steps timed one by one after a 512 MiB cache flush (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -64,6 +70,7 @@ def parse():
 
 
 CALIB_BYTES = 64 << 20
+FLUSH_BYTES = 512 << 20  # > L2 (4 MB per XCD) + the 256 MB memory-side cache
 
 
 def calibration_copy():
@@ -184,6 +191,97 @@ def cpu_baseline(wl, inp, target_seconds):
             "us_per_layer_equiv": round(elapsed / done * B * 1e6, 1)}
 
 
+def cold_steps(prob, n, flush_bytes=FLUSH_BYTES):
+    """Step times with L2 and the memory-side cache flushed before every step:
+    a 512 MiB read between steps, outside the timed pair of events (a read,
+    so that the caches are left holding clean lines; a fill would leave dirty
+    lines whose write-back the step would pay for)."""
+    import torch
+    flush = torch.zeros(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t = []
+    for _ in range(n):
+        flush.sum()
+        e0.record()
+        prob.decode_step()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    return _dist(t)
+
+
+def _dist(t):
+    t = sorted(t)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"n": len(t), "median_us": round(q(0.5), 3), "p10_us": round(q(0.1), 3),
+            "p90_us": round(q(0.9), 3), "min_us": round(t[0], 3), "max_us": round(t[-1], 3)}
+
+
+def prefill_and_sequence(wl, prob, inp, steps):
+    """The prefill + decode workload's two other parts: compression of the
+    prompts (prefill_batch x prefill_tokens, back to back between two HIP
+    events), and its decode_steps one-call steps with the context growing by
+    one token per step up to wl.ctx, each step timed by its own events."""
+    import torch
+
+    from sparse_decode_attention_latent_amd import synth, traffic
+    from sparse_decode_attention_latent_amd.runner import PrefillProblem, to_device
+
+    # -- prefill ---------------------------------------------------------------
+    B, T = wl.prefill_batch, wl.prefill_tokens
+    k, v = synth.kv_activations(wl, batch=B, tokens=T, stream=0)
+    pre = PrefillProblem(wl, k, v, synth.factors(wl), storage=wl.storage)
+    for _ in range(3):
+        pre.run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        pre.run()
+    e1.record()
+    torch.cuda.synchronize()
+    pre_us = e0.elapsed_time(e1) / reps * 1e3
+    e = 2 if wl.storage == "bf16" else 4
+    pre_bytes = traffic.prefill_bytes(B, T, wl.n_kv_heads, wl.head_dim, wl.r_v, wl.r_b, wl.r_q, e)
+    del pre
+
+    # -- decode steps with a growing context ----------------------------------
+    Bd = inp["q"].shape[0]
+    qs = [to_device(synth.step_queries(wl, batch=Bd, step=i), wl.storage) for i in range(steps)]
+    L_last = int(inp["seq_lens"].max())
+    shape = _shape(wl, Bd, inp)
+    t, gbs = [], []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for i in range(steps):
+        L = L_last - (steps - 1) + i
+        prob.seq_lens.fill_(L)
+        prob.start_pos.fill_(L - 1)
+        prob.q.copy_(qs[i])
+        e0.record()
+        prob.decode_step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        t.append(us)
+        gbs.append(traffic.step_bytes(shape, [L] * Bd)["total"] / (us * 1e-6) / 1e9)
+    # back to the full-context state the other passes use
+    prob.seq_lens.copy_(torch.from_numpy(prob.seq_lens_host).to(prob.seq_lens.device))
+    prob.start_pos.copy_(prob.seq_lens - 1)
+    prob.q.copy_(to_device(inp["q"], wl.storage))
+    torch.cuda.synchronize()
+    d = _dist(t)
+    d.update({"ctx_first": L_last - (steps - 1), "ctx_last": L_last, "batch": Bd,
+              "gbs_median": round(sorted(gbs)[len(gbs) // 2], 1)})
+    return ({"batch": B, "tokens": T, "us": round(pre_us, 3),
+             "algorithmic_bytes": pre_bytes, "gbs": round(pre_bytes / (pre_us * 1e-6) / 1e9, 1)},
+            d)
+
+
 def _shape(wl, B, inp):
     from sparse_decode_attention_latent_amd import traffic
     T = inp["z"].shape[2]
@@ -277,6 +375,14 @@ def main():
     prob.step_unfused()  # leave the cache and outputs as one step leaves them
     torch.cuda.synchronize()
 
+    # cold-cache steps (flushed before each), and for the prefill + decode
+    # workload its prefill and its sequence of decode steps
+    cold = cold_steps(prob, args.cold_steps) if args.cold_steps > 0 else None
+    prefill = sequence = None
+    if wl.decode_steps > 0:
+        log(f"[bench] prefill and {wl.decode_steps} decode steps ...")
+        prefill, sequence = prefill_and_sequence(wl, prob, inp, wl.decode_steps)
+
     shape = _shape(wl_step, inp["q"].shape[0], inp)
     sb = traffic.step_bytes(shape, inp["seq_lens"])
     value = sb["total"] / (ms_per_step * 1e-3) / 1e9
@@ -309,8 +415,12 @@ def main():
                      "algorithmic_bytes": sb["score"],
                      "launch_us": round(per_stage["score"], 3),
                      "traffic": traffic_bytes},
+        "cold_step": cold,
         "cpu_baseline": cpu,
     }
+    if prefill is not None:
+        out["prefill"] = prefill
+        out["decode_sequence"] = sequence
     print(json.dumps(out), flush=True)
 
 

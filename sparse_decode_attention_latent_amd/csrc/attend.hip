@@ -46,13 +46,6 @@ struct AttendArgs {
   uint16_t *u_tiles;  // optional: u also written as the reconstruction's A operand (bf16)
 };
 
-// Ordering point for LDS traffic between the lanes of one wavefront.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Partial record per (b, h, split): [m, l, u[0..r_v)] with m in base-2 logit
 // units (scale * log2 e already applied), l = sum 2^(s - m), u = sum 2^(s - m) z.
 //

@@ -77,6 +77,13 @@ __device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte
   return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
 }
 
+// Ordering point for LDS traffic between the lanes of one wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Cross-lane steps through DPP (no LDS round trip).  Control codes of the
 // GFX9 data-parallel-primitives modifier: quad_perm [1,0,3,2] (0xB1) and
 // [2,3,0,1] (0x4E) swap neighbours at distance 1 and 2; row_half_mirror

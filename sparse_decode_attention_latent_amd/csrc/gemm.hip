@@ -238,16 +238,45 @@ __global__ __launch_bounds__(256) void fuse_kernel(const T *__restrict__ Bf,
 
 // ---------------------------------------------------------------------------
 // (a0) compression of new tokens.  Rows are (sequence, token) pairs of one KV
-// head g; a wavefront handles 16 rows at a time:
-//   Z  = V A_g                 (MFMA)  -> stored latent z_s (rounded)
-//   C  = z_s[:, :r_b] P_g      (MFMA)
-//   R  = (K - C) E_g           (MFMA; bf16: K - C split into hi + lo terms)
-// and writes z_s, round(R) and K into their pages.  The factors are staged once
-// per workgroup, transposed so that every B fragment is a contiguous k run.
+// head g; every wavefront walks its own 16-row blocks:
+//   Z  = V A_g                                (MFMA)  -> stored latent z_s (rounded)
+//   R  = K E_g - z_s[:, :r_b] (P_g E_g)       (MFMA)  -> stored residual (rounded)
+// i.e. r = (k - z_s P_g) E_g with the product taken in the other association
+// (same value up to float32 rounding), and K is copied into its pages.  The
+// workgroup stages A_g and E_g transposed (every B fragment one contiguous k
+// run) and forms P_g E_g once with MFMA (bf16: kept as hi + lo bf16 terms, so
+// no precision is lost before the product).  A wavefront's V and K rows go
+// straight from HBM into the A fragments, the next block's requested while
+// the current one is computed; its latents and residuals pass through a
+// wavefront-private LDS tile to the page stores, so wavefronts never wait for
+// one another.
 // grid (workgroups per head, n_kv), 256 threads, dynamic LDS.
 // ---------------------------------------------------------------------------
 struct CompressArgs {
   int batch, n_tokens, n_kv, rv, rb, rq, rb_pad, max_pages, num_phys, page_size, cap;
+};
+
+// LDS rows are padded by 16 bytes, so the 16 rows a fragment load touches
+// start in different banks.
+template <typename T>
+struct CompressLds {  // byte offsets into the dynamic LDS block; strides in elements
+  int at, et, pe_hi, pe_lo, wave0, per_wave, zs_stride, fs, pe_stride, total;
+  __host__ __device__ CompressLds(int rv, int rq, int rb_pad) {
+    constexpr int KS = sizeof(T) == 2 ? 32 : 4;
+    constexpr int PAD = 16 / (int)sizeof(T);
+    const int rv_pad = (rv + KS - 1) / KS * KS;
+    const int e = (int)sizeof(T);
+    fs = kHeadDim + PAD;
+    pe_stride = rb_pad + PAD;
+    zs_stride = rv_pad + PAD;
+    at = 0;
+    et = at + rv * fs * e;
+    pe_hi = et + rq * fs * e;
+    pe_lo = pe_hi + rq * pe_stride * e;
+    wave0 = pe_lo + (sizeof(T) == 2 ? rq * pe_stride * e : 0);
+    per_wave = ((16 * zs_stride + 16 * rq) * e + 15) / 16 * 16;
+    total = wave0 + 4 * per_wave;
+  }
 };
 
 template <typename T>
@@ -261,174 +290,222 @@ __global__ __launch_bounds__(256) void compress_kernel(
   constexpr int CE = Elem<T>::CE;
   constexpr int DH = kHeadDim;
   constexpr bool kBf = sizeof(T) == 2;
+  constexpr int NKS = DH / MF::KS;  // k steps over head_dim
   extern __shared__ __align__(16) unsigned char smem[];
-  // layout: At [rv][DH] T | Pt [DH][rb_pad] T | Et [rq][DH] T | per wave: Zs [16][rv_pad] T,
-  //         C [16][DH+4] float, Rs [16][rq] T
+  const CompressLds<T> L(a.rv, a.rq, a.rb_pad);
+  T *At = reinterpret_cast<T *>(smem + L.at);        // [rv][fs]
+  T *Et = reinterpret_cast<T *>(smem + L.et);        // [rq][fs]
+  T *PEh = reinterpret_cast<T *>(smem + L.pe_hi);    // [rq][pe_stride]: (P E)^T, hi term
+  T *PEl = reinterpret_cast<T *>(smem + L.pe_lo);    // bf16: lo term
+  const int fs = L.fs, ps = L.pe_stride;
   const int g = blockIdx.y;
-  const int rv_pad = (a.rv + MF::KS - 1) / MF::KS * MF::KS;
-  T *At = reinterpret_cast<T *>(smem);
-  T *Pt = At + a.rv * DH;
-  T *Et = Pt + DH * a.rb_pad;
-  unsigned char *wave_base = reinterpret_cast<unsigned char *>(Et + a.rq * DH);
-  const size_t zs_bytes = (size_t)16 * rv_pad * sizeof(T);
-  const size_t c_bytes = (size_t)16 * (DH + 4) * sizeof(float);
-  const size_t rs_bytes = (size_t)16 * a.rq * sizeof(T);
-  const size_t per_wave = (zs_bytes + c_bytes + rs_bytes + 15) / 16 * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  T *Zs = reinterpret_cast<T *>(wave_base + wave * per_wave);
-  float *Cs = reinterpret_cast<float *>(wave_base + wave * per_wave + zs_bytes);
-  T *Rs = reinterpret_cast<T *>(wave_base + wave * per_wave + zs_bytes + c_bytes);
+  const int i = lane & 15, qg = lane >> 4;
+  T *Zs = reinterpret_cast<T *>(smem + L.wave0 + wave * L.per_wave);  // [16][zs_stride]
+  T *Rs = Zs + 16 * L.zs_stride;                                       // [16][rq]
 
-  // stage transposed factors of head g
+  // ---- stage A_g and E_g transposed ----
   const T *Ag = A + (int64_t)g * DH * a.rv;
   const T *Pg = P + (int64_t)g * a.rb * DH;
   const T *Eg = E + (int64_t)g * DH * a.rq;
-  for (int o = threadIdx.x; o < DH * a.rv; o += blockDim.x) {
-    const int d = o / a.rv, i = o % a.rv;
-    At[i * DH + d] = Ag[o];
-  }
-  for (int o = threadIdx.x; o < DH * a.rb_pad; o += blockDim.x) {
-    const int d = o / a.rb_pad, j = o % a.rb_pad;
-    Pt[o] = j < a.rb ? Pg[(int64_t)j * DH + d] : from_f32<T>(0.f);
-  }
-  for (int o = threadIdx.x; o < DH * a.rq; o += blockDim.x) {
-    const int d = o / a.rq, m = o % a.rq;
-    Et[m * DH + d] = Eg[o];
+  // thread (d, chunk): one 16-byte chunk of row d in, CE column entries out
+  // (consecutive threads write consecutive d: no bank conflicts)
+  auto stage_t = [&](const T *src, int width, T *dst) {
+    for (int o = threadIdx.x; o < DH * (width / CE); o += blockDim.x) {
+      const int d = o % DH, c0 = (o / DH) * CE;
+      float x[CE];
+      unpack_chunk<T>(*reinterpret_cast<const uint4 *>(src + (int64_t)d * width + c0), x);
+#pragma unroll
+      for (int e = 0; e < CE; ++e) dst[(c0 + e) * fs + d] = from_f32<T>(x[e]);
+    }
+  };
+  stage_t(Ag, a.rv, At);
+  stage_t(Eg, a.rq, Et);
+  __syncthreads();
+
+  // ---- P_g E_g: tile (j tile, m tile) per wavefront, A = rows of P_g ----
+  {
+    const int jt_n = a.rb_pad / 16, mt_n = a.rq / 16;
+    for (int t = wave; t < jt_n * mt_n; t += 4) {
+      const int jt = t / mt_n, mt = t % mt_n;
+      const int j = jt * 16 + i;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int k = ks * MF::KS + qg * MF::KPL;
+        frag af, bfr;
+        if constexpr (kBf) {
+          af = bits_to_frag(j < a.rb ? *reinterpret_cast<const uint4 *>(Pg + (int64_t)j * DH + k)
+                                     : make_uint4(0, 0, 0, 0));
+          bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(Et + (mt * 16 + i) * fs + k));
+        } else {
+          af = j < a.rb ? reinterpret_cast<const float *>(Pg)[(int64_t)j * DH + k] : 0.f;
+          bfr = reinterpret_cast<const float *>(Et)[(mt * 16 + i) * fs + k];
+        }
+        acc = MF::mma(af, bfr, acc);
+      }
+      // lane holds (P E)[jt*16 + 4 qg + r][mt*16 + i]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jj = jt * 16 + qg * 4 + r, mm = mt * 16 + i;
+        if constexpr (kBf) {
+          const uint16_t hi = f32_to_bf16(acc[r]);
+          PEh[mm * ps + jj] = hi;
+          PEl[mm * ps + jj] = f32_to_bf16(acc[r] - bf16_to_f32(hi));
+        } else {
+          reinterpret_cast<float *>(PEh)[mm * ps + jj] = acc[r];
+        }
+      }
+    }
   }
   __syncthreads();
 
   const int rows = a.batch * a.n_tokens;
   const int n_blocks = (rows + 15) / 16;
-  const int i = lane & 15, qg = lane >> 4;
   const int zc_total = a.rv / CE, rc_total = a.rq / CE, kc_total = DH / CE;
 
-  // Every wavefront runs the same number of iterations (the barriers below are
-  // block-wide); a wavefront past the last row block computes on zero rows and
-  // stores nothing.
-  for (int base = blockIdx.x * 4; base < n_blocks; base += gridDim.x * 4) {
-    const int rb16 = base + wave;
-    const int row = rb16 * 16 + i;  // this lane's A row
-    const bool row_ok = row < rows;
-    const int sb = row_ok ? row / a.n_tokens : 0;
-    const int st = row_ok ? row - sb * a.n_tokens : 0;
-    const int64_t in_off = (((int64_t)sb * a.n_tokens + st) * a.n_kv + g) * DH;
+  // A fragments of one 16-row block: lane (i, qg) holds row i's k slots of every k step
+  frag va[NKS], ka[NKS];
+  auto load_rows = [&](int blk, frag (&v)[NKS], frag (&k)[NKS]) {
+    const int row = blk * 16 + i;
+    const bool ok = blk < n_blocks && row < rows;
+    const int sb = ok ? row / a.n_tokens : 0;
+    const int st = ok ? row - sb * a.n_tokens : 0;
+    const int64_t off = (((int64_t)sb * a.n_tokens + st) * a.n_kv + g) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kk = ks * MF::KS + qg * MF::KPL;
+      if constexpr (kBf) {
+        v[ks] = bits_to_frag(ok ? *reinterpret_cast<const uint4 *>(vin + off + kk)
+                                : make_uint4(0, 0, 0, 0));
+        k[ks] = bits_to_frag(ok ? *reinterpret_cast<const uint4 *>(kin + off + kk)
+                                : make_uint4(0, 0, 0, 0));
+      } else {
+        v[ks] = ok ? reinterpret_cast<const float *>(vin)[off + kk] : 0.f;
+        k[ks] = ok ? reinterpret_cast<const float *>(kin)[off + kk] : 0.f;
+      }
+    }
+  };
+  const int n_waves = gridDim.x * 4;
+  int blk = blockIdx.x * 4 + wave;
+  load_rows(blk, va, ka);
+  for (; blk < n_blocks; blk += n_waves) {  // wavefront-uniform
+    // this block's destination slots, looked up while the MFMAs run
+    const int row = blk * 16 + i;
+    int phys = -1, slot = 0;
+    if (row < rows) {
+      const int b = row / a.n_tokens, t = row - b * a.n_tokens;
+      const int pos = start_pos[b] + t;
+      if (pos >= 0 && pos < a.cap) {
+        const int page = pos / a.page_size;
+        slot = pos - page * a.page_size;
+        const int ph = block_table[(int64_t)b * a.max_pages + page];
+        if (ph >= 0 && ph < a.num_phys) phys = ph;
+      }
+    }
+    // the next block's rows, in flight during this one (bf16)
+    frag vn[kBf ? NKS : 1], kn[kBf ? NKS : 1];
+    if constexpr (kBf) load_rows(blk + n_waves, vn, kn);
 
     // ---- Z = V A ----
     for (int nt = 0; nt < a.rv / 16; ++nt) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < DH / MF::KS; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
         const int k = ks * MF::KS + qg * MF::KPL;
-        frag af, bfr;
-        if constexpr (kBf) {
-          af = bits_to_frag(row_ok ? *reinterpret_cast<const uint4 *>(vin + in_off + k)
-                                   : make_uint4(0, 0, 0, 0));
-          bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(At + (nt * 16 + i) * DH + k));
-        } else {
-          af = row_ok ? reinterpret_cast<const float *>(vin)[in_off + k] : 0.f;
-          bfr = reinterpret_cast<const float *>(At)[(nt * 16 + i) * DH + k];
-        }
-        acc = MF::mma(af, bfr, acc);
+        frag bfr;
+        if constexpr (kBf)
+          bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(At + (nt * 16 + i) * fs + k));
+        else
+          bfr = reinterpret_cast<const float *>(At)[(nt * 16 + i) * fs + k];
+        acc = MF::mma(va[ks], bfr, acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zs[(qg * 4 + r) * rv_pad + nt * 16 + i] = from_f32<T>(acc[r]);
+      for (int r = 0; r < 4; ++r) Zs[(qg * 4 + r) * L.zs_stride + nt * 16 + i] = from_f32<T>(acc[r]);
     }
-    for (int o = lane; o < 16 * (rv_pad - a.rv); o += 64) {
-      const int rr = o / (rv_pad - a.rv), cc = a.rv + o % (rv_pad - a.rv);
-      Zs[rr * rv_pad + cc] = from_f32<T>(0.f);
+    for (int o = lane; o < 16 * (L.zs_stride - a.rv); o += 64) {
+      const int rr = o / (L.zs_stride - a.rv), cc = a.rv + o % (L.zs_stride - a.rv);
+      Zs[rr * L.zs_stride + cc] = from_f32<T>(0.f);
     }
-    __syncthreads();
+    wave_lds_sync();
 
-    // ---- C = z_s[:, :rb] P ----
-    for (int nt = 0; nt < DH / 16; ++nt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < a.rb_pad / MF::KS; ++ks) {
-        const int k = ks * MF::KS + qg * MF::KPL;
-        frag af, bfr;
-        if constexpr (kBf) {
-          // columns past r_b are zero in Pt, so the latent's extra dims drop out
-          af = bits_to_frag(*reinterpret_cast<const uint4 *>(Zs + i * rv_pad + k));
-          bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(Pt + (nt * 16 + i) * a.rb_pad + k));
-        } else {
-          af = reinterpret_cast<const float *>(Zs)[i * rv_pad + k];
-          bfr = reinterpret_cast<const float *>(Pt)[(nt * 16 + i) * a.rb_pad + k];
-        }
-        acc = MF::mma(af, bfr, acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Cs[(qg * 4 + r) * (DH + 4) + nt * 16 + i] = acc[r];
-    }
-    __syncthreads();
-
-    // ---- R = (K - C) E ; also copy K into its pages ----
+    // ---- R = K E - z_s (P E) ----
     for (int nt = 0; nt < a.rq / 16; ++nt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < DH / MF::KS; ++ks) {
-        const int k = ks * MF::KS + qg * MF::KPL;
-        if constexpr (kBf) {
-          float x[8];
-          const uint4 kraw = row_ok ? *reinterpret_cast<const uint4 *>(kin + in_off + k)
-                                    : make_uint4(0, 0, 0, 0);
-          unpack_chunk<uint16_t>(kraw, x);
+      floatx4 acc_k = {0.f, 0.f, 0.f, 0.f}, acc_z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] -= Cs[i * (DH + 4) + k + e];
-          bf16x8 hi, lo;
-          split_bf16(x, &hi, &lo);
-          const bf16x8 bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(Et + (nt * 16 + i) * DH + k));
-          acc = MF::mma(hi, bfr, acc);
-          acc = MF::mma(lo, bfr, acc);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int k = ks * MF::KS + qg * MF::KPL;
+        frag bfr;
+        if constexpr (kBf)
+          bfr = bits_to_frag(*reinterpret_cast<const uint4 *>(Et + (nt * 16 + i) * fs + k));
+        else
+          bfr = reinterpret_cast<const float *>(Et)[(nt * 16 + i) * fs + k];
+        acc_k = MF::mma(ka[ks], bfr, acc_k);
+      }
+      for (int ks = 0; ks < a.rb_pad / MF::KS; ++ks) {
+        const int k = ks * MF::KS + qg * MF::KPL;  // latent dims past r_b meet zero rows of P E
+        if constexpr (kBf) {
+          const frag af = bits_to_frag(*reinterpret_cast<const uint4 *>(Zs + i * L.zs_stride + k));
+          const frag bh = bits_to_frag(*reinterpret_cast<const uint4 *>(PEh + (nt * 16 + i) * ps + k));
+          const frag bl = bits_to_frag(*reinterpret_cast<const uint4 *>(PEl + (nt * 16 + i) * ps + k));
+          acc_z = MF::mma(af, bh, acc_z);
+          acc_z = MF::mma(af, bl, acc_z);
         } else {
-          const float kv = row_ok ? reinterpret_cast<const float *>(kin)[in_off + k] : 0.f;
-          const float x = kv - Cs[i * (DH + 4) + k];
-          acc = MF::mma(x, reinterpret_cast<const float *>(Et)[(nt * 16 + i) * DH + k], acc);
+          const frag af = reinterpret_cast<const float *>(Zs)[i * L.zs_stride + k];
+          acc_z = MF::mma(af, reinterpret_cast<const float *>(PEh)[(nt * 16 + i) * ps + k],
+                          acc_z);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Rs[(qg * 4 + r) * a.rq + nt * 16 + i] = from_f32<T>(acc[r]);
+      for (int r = 0; r < 4; ++r)
+        Rs[(qg * 4 + r) * a.rq + nt * 16 + i] = from_f32<T>(acc_k[r] - acc_z[r]);
     }
-    __syncthreads();
+    wave_lds_sync();
 
-    // ---- page stores: one 16-byte chunk per (row, chunk) ----
-    const int per_row = zc_total + rc_total + kc_total;
-    for (int o = lane; o < 16 * per_row; o += 64) {
-      const int rr = o / per_row, c = o % per_row;
-      const int grow = rb16 * 16 + rr;
-      if (grow >= rows) continue;
-      const int b = grow / a.n_tokens, t = grow - b * a.n_tokens;
-      const int pos = start_pos[b] + t;
-      if (pos < 0 || pos >= a.cap) continue;
-      const int page = pos / a.page_size, slot = pos - page * a.page_size;
-      const int phys = block_table[(int64_t)b * a.max_pages + page];
-      if (phys < 0 || phys >= a.num_phys) continue;
-      const int64_t hp = (int64_t)g * a.num_phys + phys;
-      uint4 val;
-      char *dst;
-      if (c < zc_total) {
-        val = *reinterpret_cast<const uint4 *>(Zs + rr * rv_pad + c * CE);
-        dst = reinterpret_cast<char *>(zpool) + ((hp * zc_total + c) * a.page_size + slot) * 16;
-      } else if (c < zc_total + rc_total) {
-        const int cc = c - zc_total;
-        val = *reinterpret_cast<const uint4 *>(Rs + rr * a.rq + cc * CE);
-        dst = reinterpret_cast<char *>(rpool) + ((hp * rc_total + cc) * a.page_size + slot) * 16;
-      } else {
-        const int cc = c - zc_total - rc_total;
-        val = *reinterpret_cast<const uint4 *>(
-            kin + (((int64_t)b * a.n_tokens + t) * a.n_kv + g) * DH + cc * CE);
-        dst = reinterpret_cast<char *>(kpool) + ((hp * kc_total + cc) * a.page_size + slot) * 16;
+    // ---- page stores: latent and residual chunks from LDS, Key chunks from the fragments ----
+    const int64_t hp_own = (int64_t)g * a.num_phys + phys;
+    auto store_tile = [&](const T *tile, int stride, int n_chunks, T *pool) {
+      for (int it = 0; it < (16 * n_chunks + 63) / 64; ++it) {
+        const int o = it * 64 + lane;
+        const int rr = o < 16 * n_chunks ? o / n_chunks : 0, c = o - rr * n_chunks;
+        const int ph = __shfl(phys, rr), sl = __shfl(slot, rr);
+        if (o < 16 * n_chunks && ph >= 0) {
+          const int64_t hp = (int64_t)g * a.num_phys + ph;
+          *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(pool) +
+                                     ((hp * n_chunks + c) * a.page_size + sl) * 16) =
+              *reinterpret_cast<const uint4 *>(tile + rr * stride + c * CE);
+        }
       }
-      *reinterpret_cast<uint4 *>(dst) = val;
+    };
+    store_tile(Zs, L.zs_stride, zc_total, zpool);
+    store_tile(Rs, a.rq, rc_total, rpool);
+    if (phys >= 0) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int k = ks * MF::KS + qg * MF::KPL;  // element k of this lane's row
+        char *base = reinterpret_cast<char *>(kpool) +
+                     ((hp_own * kc_total + k / CE) * a.page_size + slot) * 16;
+        if constexpr (kBf)
+          *reinterpret_cast<uint4 *>(base) = __builtin_bit_cast(uint4, ka[ks]);
+        else
+          reinterpret_cast<float *>(base)[k % CE] = ka[ks];
+      }
     }
-    __syncthreads();
+    wave_lds_sync();  // the tiles are read before the next block overwrites them
+    if constexpr (kBf) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        va[ks] = vn[ks];
+        ka[ks] = kn[ks];
+      }
+    } else {
+      load_rows(blk + n_waves, va, ka);
+    }
   }
 }
 
 template <typename T>
 static size_t compress_lds_bytes(const basiskv_dims &d, int rb_pad) {
-  const int ks = sizeof(T) == 2 ? 32 : 4;
-  const int rv_pad = (d.r_v + ks - 1) / ks * ks;
-  const size_t fac = (size_t)(d.r_v * kHeadDim + kHeadDim * rb_pad + d.r_q * kHeadDim) * sizeof(T);
-  const size_t per_wave = ((size_t)16 * rv_pad * sizeof(T) + (size_t)16 * (kHeadDim + 4) * 4 +
-                           (size_t)16 * d.r_q * sizeof(T) + 15) / 16 * 16;
-  return fac + 4 * per_wave;
+  return (size_t)CompressLds<T>(d.r_v, d.r_q, rb_pad).total;
 }
 
 }  // namespace bkv
@@ -480,11 +557,16 @@ hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, v
   return d.dtype == BASISKV_BF16 ? fuse_t<uint16_t>(d, Bf, W_O, M, s) : fuse_t<float>(d, Bf, W_O, M, s);
 }
 
+#ifndef BKV_COMPRESS_WGS
+#define BKV_COMPRESS_WGS 96
+#endif
+constexpr int kCompressWgsPerHead = BKV_COMPRESS_WGS;
+
 template <typename T>
 static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v,
                              const int32_t *start_pos, int32_t n_tokens, const void *A,
                              const void *P, const void *E, const basiskv_cache &c, hipStream_t s) {
-  const int ks = sizeof(T) == 2 ? 32 : 4;
+  const int pad = sizeof(T) == 2 ? 32 : 16;  // a whole number of k steps and of 16-row tiles
   CompressArgs a;
   a.batch = d.batch;
   a.n_tokens = n_tokens;
@@ -492,7 +574,7 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   a.rv = d.r_v;
   a.rb = d.r_b;
   a.rq = d.r_q;
-  a.rb_pad = (d.r_b + ks - 1) / ks * ks;
+  a.rb_pad = (d.r_b + pad - 1) / pad * pad;
   a.max_pages = d.max_pages_per_seq;
   a.num_phys = d.num_phys_pages;
   a.page_size = d.page_size;
@@ -506,7 +588,7 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   const int rows = d.batch * n_tokens;
   const int n_blocks = (rows + 15) / 16;
   int wgs = (n_blocks + 3) / 4;
-  if (wgs > 32) wgs = 32;  // persistent: factors are staged once per workgroup
+  if (wgs > kCompressWgsPerHead) wgs = kCompressWgsPerHead;  // persistent: factors staged once each
   hipLaunchKernelGGL(compress_kernel<T>, dim3(wgs, d.n_kv_heads), dim3(256), lds, s, (const T *)k,
                      (const T *)v, start_pos, (const T *)A, (const T *)P, (const T *)E,
                      (T *)c.z_pages, (T *)c.r_pages, (T *)c.k_pages, c.block_table, a);
@@ -526,8 +608,8 @@ hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
 }
 
 size_t compress_lds(const basiskv_dims &d) {
-  const int ks = d.dtype == BASISKV_BF16 ? 32 : 4;
-  const int rb_pad = (d.r_b + ks - 1) / ks * ks;
+  const int pad = d.dtype == BASISKV_BF16 ? 32 : 16;
+  const int rb_pad = (d.r_b + pad - 1) / pad * pad;
   return d.dtype == BASISKV_BF16 ? compress_lds_bytes<uint16_t>(d, rb_pad)
                                  : compress_lds_bytes<float>(d, rb_pad);
 }

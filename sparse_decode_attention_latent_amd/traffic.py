@@ -108,3 +108,12 @@ def step_bytes(s: StepShape, seq_lens, append=True):
         parts["append"] = append_bytes(s)
     parts["total"] = sum(parts.values())
     return parts
+
+
+def prefill_bytes(batch, tokens, n_kv_heads, head_dim, r_v, r_b, r_q, elem):
+    """compress_prefill of ``tokens`` tokens per sequence: read K and V and
+    the three factors once; write one latent, residual and Key row per
+    (token, KV head)."""
+    rows = batch * tokens * n_kv_heads
+    fac = n_kv_heads * head_dim * (r_v + r_b + r_q) * elem
+    return rows * (2 * head_dim) * elem + fac + rows * (r_v + r_q + head_dim) * elem
