@@ -40,7 +40,11 @@ Readings of points the pages leave open (each used below):
      tokens of the selected pages only;  R9 ties in page score go to the lower
      page index, the selection is reported in ascending page order and padded
      with -1 when k exceeds the number of pages;  R10 a sequence with no valid
-     token yields u = 0 and y = 0.
+     token yields u = 0 and y = 0;  R11 a recent window of W tokens (the
+     pages' adopted router: 64 recent tokens besides the routed budget) is
+     taken page by page: the pages holding the last W valid tokens are always
+     attended, and the top-k routed pages are chosen among the pages before
+     them.
 """
 
 import math
@@ -184,6 +188,18 @@ def select_pages(scores, n_pages, k):
     return np.array(chosen + [-1] * (k - len(chosen)), dtype=np.int64)
 
 
+def recent_window_first_page(seq_len, page_size, recent_tokens):
+    """First page of the recent window (reading R11): the pages from here to
+    the last valid page hold the last ``recent_tokens`` valid tokens and are
+    attended whatever their score; routing picks among the pages before.
+    Appendix Table 9 caption: the sparse routers keep 64 recent tokens beside
+    the routed budget.  Without a window this is the number of valid pages."""
+    L = max(0, int(seq_len))
+    if recent_tokens <= 0:
+        return -(-L // page_size)
+    return max(0, L - int(recent_tokens)) // page_size
+
+
 def selected_tokens(sel, seq_len, page_size):
     """Token positions covered by the selected pages (valid ones only)."""
     toks = []
@@ -243,7 +259,7 @@ def reconstruct(u, Bf, W_O, group):
 
 def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
                 top_k, n_pages_out, storage, scale=None, k_new=None, v_new=None,
-                store_output=True):
+                store_output=True, recent_tokens=0):
     """One decode step of one layer for a batch.
 
     Inputs are float64 (decode stored values with storage_to_f64 first);
@@ -251,7 +267,10 @@ def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
     "f64").  If k_new / v_new ([B, Hkv, dh]) are given, the step first
     compresses that token into position seq_lens[b] - 1 of each sequence
     (a0); then it routes (a1, a2), selects (a3), attends (a4) and
-    reconstructs (a5).  Arrays z, r, kc are copied, not modified.
+    reconstructs (a5).  With recent_tokens > 0 the top-k pages are chosen
+    before the recent window and the window's pages are attended as well
+    (R11); ``sel`` holds the routed pages only.  Arrays z, r, kc are copied,
+    not modified.
 
     Returns a dict: scores [B, Hkv, n_pages_out], sel [B, Hkv, top_k],
     u [B, Hq, rV], y [B, D] (float64, unrounded), y_stored (y rounded to
@@ -286,12 +305,15 @@ def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
         if L <= 0:
             continue
         n_pages = -(-L // page_size)
+        first_recent = recent_window_first_page(L, page_size, recent_tokens)
+        recent = np.arange(first_recent, n_pages, dtype=np.int64)
         for g in range(hkv):
             qg = q[b, g * group:(g + 1) * group]
             scores[b, g] = route_page_scores(qg, z[b, g], r[b, g], P[g], Q[g], rb, L,
                                              page_size, n_pages_out)
-            sel[b, g] = select_pages(scores[b, g], n_pages, top_k)
-            u[b, g * group:(g + 1) * group] = attend_group(qg, kc[b, g], z[b, g], sel[b, g],
+            sel[b, g] = select_pages(scores[b, g], first_recent, top_k)
+            pages = np.concatenate([sel[b, g], recent])
+            u[b, g * group:(g + 1) * group] = attend_group(qg, kc[b, g], z[b, g], pages,
                                                            L, page_size, scale)
         y[b] = reconstruct(u[b], Bf, W_O, group)
     out = dict(scores=scores, sel=sel, u=u, y=y, z=z, r=r, kc=kc)

@@ -118,3 +118,20 @@ def reconstruct(u, Bf, W_O, group):
         contrib = _vecmat(list(u[h]), M_h)
         y = [a + b for a, b in zip(y, contrib)]
     return y
+
+
+def attend_tokens(q_group, kc, z, tokens, scale):
+    """Latent attention over an explicit token list (explicit loops, an
+    unshifted softmax): for the recent-window pins, where the attended set is
+    written as a per-token predicate instead of a list of pages."""
+    G, rv = len(q_group), len(z[0])
+    out = [[0.0] * rv for _ in range(G)]
+    if not tokens:
+        return out
+    for h in range(G):
+        w = [math.exp(scale * _dot(q_group[h], kc[t])) for t in tokens]
+        tot = sum(w)
+        for wi, t in zip(w, tokens):
+            for d in range(rv):
+                out[h][d] += wi / tot * z[t][d]
+    return out

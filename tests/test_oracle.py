@@ -359,6 +359,69 @@ def test_decode_step_matches_brute_end_to_end(seq_lens):
 
 
 # ---------------------------------------------------------------------------
+# the recent window (appendix Table 9 caption: 64 recent tokens beside the
+# routed budget; reading R11: whole pages holding the last W tokens)
+# ---------------------------------------------------------------------------
+
+def test_recent_window_first_page_closed_forms():
+    f = ref.recent_window_first_page
+    assert f(100, 4, 0) == 25 and f(101, 4, 0) == 26 and f(0, 4, 0) == 0
+    assert f(100, 4, 64) == 9          # tokens 36..99 -> pages 9..24
+    assert f(101, 4, 64) == 9          # tokens 37..100 -> pages 9..25
+    assert f(40, 4, 64) == 0 and f(0, 4, 64) == 0
+    assert f(65, 32, 64) == 0 and f(97, 32, 64) == 1
+
+
+@pytest.mark.parametrize("seq_lens,recent", [([11, 7], 3), ([11, 6], 4), ([9, 11], 1), ([1, 0], 5)])
+def test_recent_window_matches_token_predicate_brute(seq_lens, recent):
+    """Routed pages are the top-k of the pages before the window (brute
+    exhaustive search over that prefix) and the attention runs over the
+    tokens t with page(t) routed or t >= first_recent_page * S (brute token
+    loop)."""
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl, seq_lens=np.array(seq_lens))
+    d = unpack(inp)
+    G, S, k = wl.group, wl.page_size, wl.top_k
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rb=wl.r_b, page_size=S, top_k=k,
+                          n_pages_out=wl.max_pages, storage="f64", recent_tokens=recent)
+    scale = 1 / math.sqrt(wl.head_dim)
+    for b in range(wl.batch):
+        L = int(seq_lens[b])
+        first = max(0, L - recent) // S          # written out again from the definition
+        for g in range(wl.n_kv_heads):
+            qg = d["q"][b, g * G:(g + 1) * G].tolist()
+            sc = brute.route_page_scores(qg, d["z"][b, g].tolist(), d["r"][b, g].tolist(),
+                                         d["P"][g].tolist(), d["Q"][g].tolist(), wl.r_b, L, S,
+                                         wl.max_pages)
+            sel = brute.select_pages(sc, first if L > 0 else 0, k)
+            assert out["sel"][b, g].tolist() == sel
+            toks = [t for t in range(L) if (t // S) in sel or t >= first * S]
+            u = brute.attend_tokens(qg, d["kc"][b, g].tolist(), d["z"][b, g].tolist(), toks, scale)
+            np.testing.assert_allclose(out["u"][b, g * G:(g + 1) * G], u, rtol=1e-11, atol=1e-12)
+
+
+def test_recent_window_covering_everything_is_dense_attention():
+    """A window at least as long as the sequence routes nothing and attends
+    every token: the step equals dense softmax attention (torch SDPA)."""
+    wl = tiny_workload(batch=1)
+    inp = synth.decode_inputs(wl, seq_lens=np.array([11]))
+    d = unpack(inp)
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rb=wl.r_b, page_size=wl.page_size,
+                          top_k=wl.top_k, n_pages_out=wl.max_pages, storage="f64",
+                          recent_tokens=11)
+    assert (out["sel"] == -1).all()
+    G = wl.group
+    for g in range(wl.n_kv_heads):
+        q = torch.from_numpy(d["q"][0, g * G:(g + 1) * G])[:, None, :]
+        kk = torch.from_numpy(d["kc"][0, g])[None].expand(G, -1, -1)
+        zz = torch.from_numpy(d["z"][0, g])[None].expand(G, -1, -1)
+        want = torch.nn.functional.scaled_dot_product_attention(q, kk, zz)[:, 0].numpy()
+        np.testing.assert_allclose(out["u"][0, g * G:(g + 1) * G], want, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # semantics of the synthetic workloads: planted pages are routed
 # ---------------------------------------------------------------------------
 
