@@ -80,6 +80,13 @@ typedef struct {
   int32_t max_pages_per_seq; /* columns of block_table, <= 32768 */
   int32_t num_phys_pages;    /* pages per pool and per KV head */
   int32_t dtype;             /* BASISKV_F32 or BASISKV_BF16 */
+  int32_t recent_tokens;     /* >= 0: recent window (appendix Table 9 caption: 64 recent
+                                tokens beside the routed budget).  With W > 0 the pages
+                                holding a sequence's last W valid tokens, from page
+                                max(0, seq_len - W) / page_size on, are attended whatever
+                                their score, and the top_k routed pages are chosen among the
+                                pages before them; sel still holds the routed pages only.
+                                0: no window. */
 } basiskv_dims;
 
 /* The paged cache (device pointers, caller-owned). */
@@ -145,7 +152,9 @@ int32_t basiskv_score_pages(const basiskv_dims *dims, const float *q_proj,
  * the selected pages' Keys are fetched).  Exact: the top_k largest scores
  * among the sequence's ceil(seq_len / page_size) pages; equal scores go to
  * the lower page index; the list is in ascending page order and padded with
- * -1 when top_k exceeds the page count (all -1 for an empty sequence).
+ * -1 when top_k exceeds the page count (all -1 for an empty sequence).  With
+ * dims.recent_tokens = W > 0 the candidates are the pages before the recent
+ * window, i.e. the first max(0, seq_len - W) / page_size pages.
  *   seq_lens [batch] device; sel [batch][n_kv_heads][top_k] int32 out. */
 int32_t basiskv_select_pages(const basiskv_dims *dims, const float *page_scores,
                              const int32_t *seq_lens, int32_t top_k, int32_t *sel,
@@ -165,7 +174,9 @@ int32_t basiskv_route_pages(const basiskv_dims *dims, const void *q, const void 
  *   s_t = scale * q_h . k_t over the valid tokens of the pages in sel[b][g],
  *   p = softmax(s) over those tokens, u[b][h] = sum_t p_t z_t.
  * Entries of sel that are -1 or outside the sequence are skipped; a head with
- * no valid token gets u = 0.  scale is usually 1/sqrt(head_dim).
+ * no valid token gets u = 0.  scale is usually 1/sqrt(head_dim).  With
+ * dims.recent_tokens > 0 the recent window's pages are attended too; sel must
+ * then hold pages before the window only (as basiskv_select_pages gives).
  *   q [batch][n_q_heads][head_dim]; sel [batch][n_kv_heads][top_k];
  *   u [batch][n_q_heads][r_v] float32 out.
  * The workspace (see basiskv_workspace_bytes) holds the per-split partial

@@ -34,7 +34,7 @@ class BasisKVError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "r_v", "r_b", "r_q",
-        "page_size", "max_pages_per_seq", "num_phys_pages", "dtype")]
+        "page_size", "max_pages_per_seq", "num_phys_pages", "dtype", "recent_tokens")]
 
 
 class Cache(ctypes.Structure):
@@ -98,9 +98,9 @@ def _check(status, where):
 
 
 def make_dims(*, batch, n_q_heads, n_kv_heads, head_dim, hidden, r_v, r_b, r_q, page_size,
-              max_pages_per_seq, num_phys_pages, dtype):
+              max_pages_per_seq, num_phys_pages, dtype, recent_tokens=0):
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, hidden, r_v, r_b, r_q, page_size,
-                max_pages_per_seq, num_phys_pages, dtype)
+                max_pages_per_seq, num_phys_pages, dtype, recent_tokens)
 
 
 def make_cache(z_pages, r_pages, k_pages, block_table, seq_lens):

@@ -29,6 +29,7 @@ int32_t check_dims(const basiskv_dims *d) {
       d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
     return BASISKV_ERR_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0 || d->r_b > d->r_v) return BASISKV_ERR_SHAPE;
+  if (d->recent_tokens < 0) return BASISKV_ERR_SHAPE;
   if (d->head_dim != bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!pow2_page(d->page_size)) return BASISKV_ERR_UNSUPPORTED;
   const int ce = elem_chunk(d->dtype);

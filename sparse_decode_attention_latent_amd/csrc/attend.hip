@@ -39,6 +39,8 @@ constexpr int kAttendBlocks = BKV_ATTEND_BLOCKS;  // 64-token blocks per wavefro
 
 struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
+  int recent;     // recent-window tokens (0: none)
+  int n_entries;  // entries per row: top_k routed, then the recent window's pages
   int gs;  // query subgroups per KV head (the kernel's group is n_q / n_kv / gs heads)
   int pages_per_split, n_split, total, padded;
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
@@ -126,7 +128,7 @@ void attend_split_kernel(
   const int slot = lane & (a.page_size - 1);
   const int ppi = kWave >> a.log2_page;  // pages per 64-token block
   const int e_begin = split * a.pages_per_split;
-  const int e_end = min(a.top_k, e_begin + a.pages_per_split);
+  const int e_end = min(a.n_entries, e_begin + a.pages_per_split);
   const int n_blocks = (e_end - e_begin + ppi - 1) / ppi;
   const int32_t *sel_bg = sel + (int64_t)bg * a.top_k;
   const int32_t *bt = block_table + (int64_t)b * a.max_pages;
@@ -134,6 +136,8 @@ void attend_split_kernel(
   // ---- this wavefront's blocks of round r: selection entries, then physical pages ----
   const int L = clamp_len(seq_lens[b], a.cap);
   const int NP = (L + a.page_size - 1) >> a.log2_page;
+  // entries past top_k are the recent window's pages, from first_recent on
+  const int first_recent = max(0, L - a.recent) >> a.log2_page;
   const int n_rounds = (n_blocks + NW * NB - 1) / (NW * NB);
   int page[NB], phys[NB];
   auto fetch_pages = [&](int r) {
@@ -141,7 +145,9 @@ void attend_split_kernel(
     for (int i = 0; i < NB; ++i) {
       const int blk = (r * NB + i) * NW + wave;
       const int e = e_begin + blk * ppi + (lane >> a.log2_page);
-      page[i] = (blk < n_blocks && e < e_end) ? sel_bg[e] : -1;
+      const int pr = first_recent + (e - a.top_k);
+      page[i] = (blk < n_blocks && e < e_end) ? (e < a.top_k ? sel_bg[e] : (pr < NP ? pr : -1))
+                                               : -1;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -553,14 +559,14 @@ int attend_group_split(const basiskv_dims &d) {
 // workgroups per compute unit at that size, otherwise one block per
 // wavefront (more, smaller workgroups).  A split grows by whole rounds when
 // that would leave more than kMaxSplits splits (the kernel loops over them).
-static int pages_per_split(const basiskv_dims &d, int32_t top_k) {
+static int pages_per_split(const basiskv_dims &d, int32_t entries) {
   const int ppi = 64 / d.page_size;
   const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * attend_group_split(d) *
-                         (((int64_t)top_k + ppi - 1) / ppi);
+                         (((int64_t)entries + ppi - 1) / ppi);
   const int per_wave = blocks >= (int64_t)kAttendWaves * kAttendBlocks * 512 ? kAttendBlocks : 1;
   const int per_round = kAttendWaves * per_wave * ppi;
   int rounds = 1;
-  const int64_t need = ((int64_t)top_k + kMaxSplits - 1) / kMaxSplits;
+  const int64_t need = ((int64_t)entries + kMaxSplits - 1) / kMaxSplits;
   if (need > per_round) {
     const int full = kAttendWaves * kAttendBlocks * ppi;  // several rounds: full rounds
     rounds = (int)((need + full - 1) / full);
@@ -569,9 +575,19 @@ static int pages_per_split(const basiskv_dims &d, int32_t top_k) {
   return per_round;
 }
 
+// Entries of one row: the top_k routed pages, then room for the recent
+// window's pages (ceil(W / page_size) + 1: the window may start mid-page).
+static int attend_entries(const basiskv_dims &d, int32_t top_k) {
+  if (d.recent_tokens <= 0) return top_k;
+  const int w = d.recent_tokens < d.max_pages_per_seq * d.page_size
+                    ? d.recent_tokens : d.max_pages_per_seq * d.page_size;
+  return top_k + (w + d.page_size - 1) / d.page_size + 1;
+}
+
 int attend_splits(const basiskv_dims &d, int32_t top_k) {
-  const int pps = pages_per_split(d, top_k);
-  return (top_k + pps - 1) / pps;
+  const int n = attend_entries(d, top_k);
+  const int pps = pages_per_split(d, n);
+  return (n + pps - 1) / pps;
 }
 
 static const AttendVariant *find_attend(const basiskv_dims &d) {
@@ -602,8 +618,10 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.log2_page = ilog2i(d.page_size);
   a.cap = d.max_pages_per_seq * d.page_size;
   a.top_k = top_k;
+  a.recent = d.recent_tokens;
+  a.n_entries = attend_entries(d, top_k);
   a.gs = attend_group_split(d);
-  a.pages_per_split = pages_per_split(d, top_k);
+  a.pages_per_split = pages_per_split(d, a.n_entries);
   a.n_split = attend_splits(d, top_k);
   a.total = d.batch * d.n_kv_heads * a.gs * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;

@@ -22,11 +22,13 @@ __global__ __launch_bounds__(128) void project_queries_kernel(
 // ---------------------------------------------------------------------------
 // (a3) exact top-k per (sequence, KV head); topk_row is in topk.hpp.
 // ---------------------------------------------------------------------------
-// Standalone selection: grid (n_kv, batch), 64 * NWV threads.
+// Standalone selection: grid (n_kv, batch), 64 * NWV threads.  With a recent
+// window of `recent` tokens the candidates are the pages before the window.
 template <int KPT, int NWV>
 __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
-    int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k) {
+    int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k,
+    int recent) {
   const int g = blockIdx.x, b = blockIdx.y;
   // the whole row is requested before the sequence length arrives
   const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) v[j] = base + 64 * j < max_pages ? row[base + 64 * j] : 0.f;
   const int L = clamp_len(seq_lens[b], cap);
-  const int NP = (L + page_size - 1) / page_size;
+  const int NP = recent > 0 ? max(0, L - recent) / page_size : (L + page_size - 1) / page_size;
   int32_t *out = sel + ((int64_t)b * n_kv + g) * k;
   if (k >= NP) {
     for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < NP ? i : -1;
@@ -240,16 +242,16 @@ hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32
   if (mp <= 1024)
     hipLaunchKernelGGL((topk_select_kernel<16 / kSelectSmallWaves, kSelectSmallWaves>), grid,
                        dim3(64 * kSelectSmallWaves), 0, s, scores, seq_lens, sel, d.n_kv_heads, mp,
-                       d.page_size, cap, top_k);
+                       d.page_size, cap, top_k, d.recent_tokens);
   else if (mp <= 4096)
     hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
   else if (mp <= 16384)
     hipLaunchKernelGGL((topk_select_kernel<16, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
   else
     hipLaunchKernelGGL((topk_select_kernel<32, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
   return hipGetLastError();
 }
 

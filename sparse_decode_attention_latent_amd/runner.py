@@ -42,7 +42,7 @@ class DecodeProblem:
     """
 
     def __init__(self, wl, inp, *, top_k=None, shuffle_seed=12345, device="cuda",
-                 max_pages=None):
+                 max_pages=None, recent_tokens=0):
         self.wl = wl
         self.storage = inp["storage"]
         st = self.storage
@@ -58,7 +58,9 @@ class DecodeProblem:
                                   hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                   page_size=S, max_pages_per_seq=self.max_pages,
                                   num_phys_pages=self.num_phys,
-                                  dtype=api.BF16 if st == "bf16" else api.F32)
+                                  dtype=api.BF16 if st == "bf16" else api.F32,
+                                  recent_tokens=recent_tokens)
+        self.recent_tokens = int(recent_tokens)
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         dev = device
         self.block_table = torch.from_numpy(self.block_table_host).to(dev)

@@ -51,12 +51,14 @@ def f64(a, storage):
 
 
 def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_pages_out=None,
-                    scale=None):
+                    scale=None, recent_tokens=0):
     """The oracle's decode step for sequence b of a workload's stored inputs.
 
     Returns scores [Hkv, NPout], sel [Hkv, k], u [Hq, rV], y [D], y_stored,
     and the appended token's stored codes (z_new, r_new: [Hkv, w]).
     sel_override [Hkv, k] replaces the oracle's own selection for attention.
+    With a recent window the routed candidates are the pages before it
+    (n_candidates) and its pages are attended as well.
     """
     st = inp["storage"]
     G, hkv, S = wl.group, wl.n_kv_heads, wl.page_size
@@ -73,8 +75,10 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
     u = np.zeros((wl.n_q_heads, wl.r_v))
     z_new = np.zeros((hkv, wl.r_v))
     r_new = np.zeros((hkv, wl.r_q))
+    n_cand = ref.recent_window_first_page(L, S, recent_tokens)
     if L > 0:
         n_pages = -(-L // S)
+        recent = np.arange(n_cand, n_pages, dtype=np.int64)
         if append:
             zs, rs, _ = ref.compress_tokens(f64(inp["k_new"][b:b + 1], st), f64(inp["v_new"][b:b + 1], st),
                                             fac["A"], fac["P"], fac["E"], wl.r_b, st)
@@ -88,12 +92,14 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
             qg = q[g * G:(g + 1) * G]
             scores[g] = ref.route_page_scores(qg, z, r, fac["P"][g], fac["Q"][g], wl.r_b, L, S,
                                               n_pages_out)
-            sel[g] = ref.select_pages(scores[g], n_pages, top_k)
+            sel[g] = ref.select_pages(scores[g], n_cand, top_k)
             use = sel[g] if sel_override is None else np.asarray(sel_override[g], dtype=np.int64)
-            u[g * G:(g + 1) * G] = ref.attend_group(qg, kc, z, use, L, S, scale)
+            u[g * G:(g + 1) * G] = ref.attend_group(qg, kc, z, np.concatenate([use, recent]),
+                                                    L, S, scale)
     y = ref.reconstruct(u, fac["Bf"], fac["W_O"], G) if L > 0 else np.zeros(wl.hidden)
     return dict(scores=scores, sel=sel, u=u, y=y, y_stored=ref.round_to_storage(y, st),
-                z_new=z_new, r_new=r_new, n_pages=(-(-L // S) if L > 0 else 0))
+                z_new=z_new, r_new=r_new, n_pages=(-(-L // S) if L > 0 else 0),
+                n_candidates=n_cand)
 
 
 def check_scores(gpu, want, n_pages, where=""):

@@ -60,6 +60,10 @@ def test_workspace_bytes():
         assert ws >= wl.batch * wl.n_q_heads * (wl.r_b + wl.r_q) * 4
     assert api.workspace_bytes(dims_of(WORKLOADS[2], n_q_heads=30), 8) == 0
     assert api.workspace_bytes(dims_of(WORKLOADS[2]), 0) == 0
+    # a recent window adds its pages to every attention row: never less room
+    wl = WORKLOADS[2]
+    assert (api.workspace_bytes(dims_of(wl, recent_tokens=64), wl.top_k)
+            >= api.workspace_bytes(dims_of(wl), wl.top_k))
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
@@ -81,6 +85,7 @@ def _cache(**kw):
     (dict(r_q=36), 3),                # not a multiple of 16 bytes
     (dict(dtype=7), 3),
     (dict(max_pages_per_seq=40000), 3),
+    (dict(recent_tokens=-1), 2),
 ])
 def test_dims_validation(over, code):
     lib = api.lib()

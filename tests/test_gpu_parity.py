@@ -33,18 +33,20 @@ def _say(msg):
 def compare_step(wl, inp, prob, out, seqs):
     """Check scores, selection, u, y and the appended codes for sequences seqs."""
     st = inp["storage"]
+    rw = prob.recent_tokens
     for b in seqs:
-        want = parity.oracle_sequence(wl, inp, b, top_k=prob.top_k, n_pages_out=prob.max_pages)
-        n_pages = want["n_pages"]
+        want = parity.oracle_sequence(wl, inp, b, top_k=prob.top_k, n_pages_out=prob.max_pages,
+                                      recent_tokens=rw)
+        n_pages = want["n_candidates"]  # routed among the pages before any recent window
         for g in range(wl.n_kv_heads):
             where = f"{wl.name} b={b} g={g}"
-            parity.check_scores(out["scores"][b, g], want["scores"][g], n_pages, where)
+            parity.check_scores(out["scores"][b, g], want["scores"][g], want["n_pages"], where)
             parity.check_selection(out["sel"][b, g], out["scores"][b, g], want["scores"][g], n_pages,
                                    prob.top_k, where)
         same_sel = np.array_equal(out["sel"][b], want["sel"])
         if not same_sel:  # several selections are correct: attend over the library's own
             want = parity.oracle_sequence(wl, inp, b, top_k=prob.top_k, n_pages_out=prob.max_pages,
-                                          sel_override=out["sel"][b])
+                                          sel_override=out["sel"][b], recent_tokens=rw)
         eu = parity.rel_rows(out["u"][b], want["u"])
         assert eu.max() <= parity.U_RTOL, f"{wl.name} b={b}: u rel err {eu.max():.3g} head {eu.argmax()}"
         ey = parity.rel_rows(ref.storage_to_f64(out["y"][b], st), want["y"])
@@ -58,10 +60,13 @@ def compare_step(wl, inp, prob, out, seqs):
         _say(f"  {wl.name} b={b} L={L} ok (sel {'=' if same_sel else 'band'}; u {eu.max():.2e}; y {float(ey):.2e})")
 
 
-def run_case(wl, *, batch=None, ctx=None, seq_lens=None, seqs=None, top_k=None, shuffle_seed=12345):
-    _say(f"case {wl.name}: batch={batch or wl.batch} ctx={ctx or wl.ctx} seq_lens={seq_lens} top_k={top_k or wl.top_k}")
+def run_case(wl, *, batch=None, ctx=None, seq_lens=None, seqs=None, top_k=None, shuffle_seed=12345,
+             recent_tokens=0):
+    _say(f"case {wl.name}: batch={batch or wl.batch} ctx={ctx or wl.ctx} seq_lens={seq_lens} "
+         f"top_k={top_k or wl.top_k} recent={recent_tokens}")
     inp = synth.decode_inputs(wl, batch=batch, ctx=ctx, seq_lens=seq_lens)
-    prob = DecodeProblem(wl, inp, top_k=top_k, shuffle_seed=shuffle_seed)
+    prob = DecodeProblem(wl, inp, top_k=top_k, shuffle_seed=shuffle_seed,
+                         recent_tokens=recent_tokens)
     prob.step(append=True)
     out = prob.outputs()
     B = inp["q"].shape[0]
@@ -188,6 +193,43 @@ def test_block_table_permutation_and_determinism_bit_exact():
     for o in outs[1:]:
         for key in ("scores", "sel", "u", "y"):
             np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
+
+
+# ---------------------------------------------------------------------------
+# the recent window and the pages' adopted router (appendix Tables 9 and 10:
+# B16R16 routing, Page4, 2048 routed tokens plus 64 recent tokens, V96)
+# ---------------------------------------------------------------------------
+
+def test_recent_window_ragged():
+    """Recent window of 64 tokens on 32-token pages (it may start mid-page),
+    ragged lengths including sequences shorter than the window."""
+    run_case(workload(1), batch=6, ctx=1000, seq_lens=[1000, 999, 33, 1, 0, 517],
+             recent_tokens=64)
+
+
+def test_recent_window_wider_than_some_sequences():
+    run_case(workload(2), batch=4, ctx=4096, seq_lens=[4096, 300, 2, 1500], top_k=8,
+             recent_tokens=400)
+
+
+def test_adopted_router_b16r16_page4():
+    wl = workload(1).with_(name="llama8b-v96-b16r16-page4", r_b=16, r_q=16, page_size=4,
+                           top_k=512, ctx=16384, batch=2, n_planted=8, planted="random")
+    run_case(wl, seq_lens=[16384, 12001], recent_tokens=64)
+
+
+def test_recent_window_one_call_step_equals_separate_calls():
+    wl = workload(1)
+    inp = synth.decode_inputs(wl, batch=3, ctx=4096, seq_lens=[4096, 3000, 70])
+    prob = DecodeProblem(wl, inp, top_k=16, recent_tokens=64)
+    prob.step_unfused(append=True)
+    base = prob.outputs()
+    prob.u.fill_(float("nan"))
+    prob.decode_step()
+    got = prob.outputs()
+    for key in ("scores", "sel", "u", "y"):
+        np.testing.assert_array_equal(got[key], base[key], err_msg=key)
+    compare_step(wl, inp, prob, got, range(3))
 
 
 @pytest.mark.parametrize("wl_index", [1, 2, 4])
