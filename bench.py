@@ -178,7 +178,7 @@ def cpu_baseline(wl, inp, target_seconds):
         ref.decode_step(x["q"], x["z"], x["r"], x["kc"], x["L"], f["A"], f["Bf"], f["P"], f["Q"],
                         f["E"], f["W_O"], rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k,
                         n_pages_out=-(-x["z"].shape[2] // wl.page_size), storage=st,
-                        k_new=x["k_new"], v_new=x["v_new"])
+                        k_new=x["k_new"], v_new=x["v_new"], recent_tokens=wl.recent_tokens)
         elapsed += time.perf_counter() - t0
         nbytes += traffic.step_bytes(one, x["L"])["total"]
         done += 1
@@ -288,7 +288,8 @@ def _shape(wl, B, inp):
     return traffic.StepShape(batch=B, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
                              head_dim=wl.head_dim, hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b,
                              r_q=wl.r_q, page_size=wl.page_size, max_pages=-(-T // wl.page_size),
-                             top_k=wl.top_k, elem=2 if inp["storage"] == "bf16" else 4)
+                             top_k=wl.top_k, elem=2 if inp["storage"] == "bf16" else 4,
+                             recent_tokens=wl.recent_tokens)
 
 
 def main():
@@ -404,7 +405,8 @@ def main():
         "config": {"workload": wl.name, "batch": shape.batch, "ctx": int(inp["z"].shape[2]),
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "hidden": wl.hidden, "page_size": wl.page_size,
-                   "r_v": wl.r_v, "r_b": wl.r_b, "r_q": wl.r_q, "top_k": wl.top_k},
+                   "r_v": wl.r_v, "r_b": wl.r_b, "r_q": wl.r_q, "top_k": wl.top_k,
+                   "recent_tokens": wl.recent_tokens},
         "algorithmic_bytes_per_step": sb["total"],
         "stages_us": {k: round(v, 3) for k, v in per_stage.items()},
         "stages_host_bound": [k for k in stages if host_bound[k]],

@@ -29,6 +29,7 @@ class Workload:
     latent_norm_sigma: float = 0.0  # >0: per-token latent norms ~ LogNormal(0, sigma)
     noise: float = 0.05
     seed: int = 1000
+    recent_tokens: int = 0  # recent window attended besides the routed pages
     # prefill + decode workload only
     prefill_batch: int = 0
     prefill_tokens: int = 0
@@ -70,13 +71,23 @@ WORKLOADS = (
              top_k=128, seed=1004, prefill_batch=4, prefill_tokens=4096, decode_steps=128),
 )
 
+# Beyond the five: the pages' adopted router configuration (appendix Tables 9
+# and 10: B16R16 routing, Page4, 2048 routed tokens plus 64 recent tokens,
+# V96) on the 8B-shaped layer at c2's batch and context.
+EXTRA_WORKLOADS = (
+    Workload("llama8b-ctx32k-b16r16-page4", "bf16", batch=8, n_q_heads=32, n_kv_heads=8,
+             head_dim=128, hidden=4096, ctx=32768, page_size=4, r_v=96, r_b=16, r_q=16,
+             top_k=512, recent_tokens=64, n_planted=8, planted="random",
+             latent_norm_sigma=0.5, seed=1005),
+)
+
 HEADLINE = 2
 
 
 def workload(index_or_name):
     if isinstance(index_or_name, int):
         return WORKLOADS[index_or_name]
-    for w in WORKLOADS:
+    for w in WORKLOADS + EXTRA_WORKLOADS:
         if w.name == index_or_name:
             return w
     raise KeyError(index_or_name)

@@ -1,15 +1,17 @@
 // Exact top-k of one score row per workgroup (or wavefront): the selection
 // step of BasisKV's routing (arXiv 2611.02583, Table 9's caption: pages are
-// chosen by score under a page budget).  Shared by the standalone selection
-// kernel and the attention launch that selects its own pages.
+// chosen by score under a page budget).
 //
 // Scores become order-preserving 32-bit keys held in registers, up to KPT per
-// lane.  The k-th largest key tau is built one bit at a time from the top (a
-// candidate is kept when at least k keys reach it; counts by wavefront
-// ballots, and, with several wavefronts, one LDS exchange and barrier per
-// bit).  Bits that every valid key shares -- above the highest bit in which
-// the largest and smallest keys differ -- are taken as given, and the search
-// stops as soon as exactly k keys reach the candidate (the top-k set is then
+// lane.  The k-th largest key tau is built from the top.  Bits that every
+// valid key shares -- above the highest bit in which the largest and smallest
+// keys differ -- are taken as given.  A row held by one wavefront resolves
+// one bit per round (a candidate is kept when at least k keys reach it;
+// counts by ballots); a row held by several wavefronts resolves 8 bits per
+// round (a histogram of the next digit over the keys that share the decided
+// bits, by LDS atomics, and a suffix scan over its 256 bins), paying one
+// barrier pair per digit instead of one per bit.  Either way the search stops
+// as soon as exactly k keys share the decided bits (the top-k set is then
 // decided, whatever the lower bits of the k-th key).  The compaction
 // then hands out, in page order, every page whose key exceeds tau and the
 // lowest-index pages equal to it; positions come from ballot popcounts.
@@ -17,6 +19,11 @@
 #include "common.hpp"
 
 namespace bkv {
+
+#ifndef BKV_TOPK_RADIX_WAVES
+#define BKV_TOPK_RADIX_WAVES 4
+#endif
+constexpr int kTopkRadixWaves = BKV_TOPK_RADIX_WAVES;  // rows this wide search by digits
 
 // Order-preserving key of a score: larger score, larger key.  -0 and +0 are
 // one key; NaN ranks below every number; 0 is left for lanes past the row.
@@ -58,6 +65,10 @@ template <int KPT, int NWV, typename Emit>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP, int k,
                                          Emit &&emit) {
   __shared__ int xch[2][NWV > 1 ? NWV : 1][2];
+  // several wavefronts: radix digits (one barrier pair per 8 bits); one: bits
+  constexpr bool kRadix = NWV >= kTopkRadixWaves;
+  __shared__ int hist[kRadix ? 256 : 1];
+  __shared__ int found[kRadix ? 3 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int base = wave * 64 * kpt + lane;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -90,6 +101,58 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
   const uint32_t diff = kmax ^ kmin;
   const int top = diff ? 31 - __clz(diff) : -1;  // -1: every valid key is equal
   uint32_t tau = top < 0 ? kmax : top == 31 ? 0u : kmax & ~((2u << top) - 1u);
+  if constexpr (kRadix) {
+    // ---- tau, 8 bits at a time: histogram of the next digit of the keys that
+    // share the bits decided so far (LDS atomics), then one wavefront finds the
+    // digit holding the k-th largest key by a suffix scan over the bins ----
+    const int tid = threadIdx.x;
+    constexpr int NT = 64 * NWV;
+    int krem = k;  // rank of the k-th largest key among the keys matching tau so far
+    for (int hi = top; hi >= 0;) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool ok = j < kpt && base + 64 * j < NP;
+        const bool match = hi == 31 || (key[j] >> (hi + 1)) == (tau >> (hi + 1));
+        if (ok && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int c[4], s = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          c[t] = hist[4 * lane + t];
+          s += c[t];
+        }
+        int suf = s;  // inclusive suffix sum over lanes >= this one
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_down(suf, off);
+          if (lane + off < 64) suf += o;
+        }
+        int above = suf - s;  // keys in the bins of higher lanes
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+          if (above < krem && above + c[t] >= krem) {
+            found[0] = 4 * lane + t;
+            found[1] = above;
+            found[2] = c[t];
+          }
+          above += c[t];
+        }
+      }
+      __syncthreads();
+      const int digit = found[0];
+      krem -= found[1];
+      tau |= (uint32_t)digit << lo;
+      if (found[2] == krem) break;  // every key sharing these bits is taken
+      hi = lo - 1;
+      __syncthreads();  // found[] and hist are rewritten next pass
+    }
+  } else {
   // ---- tau, bit by bit (keys past the row are 0 and reach no candidate) ----
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
@@ -106,6 +169,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
     }
     if (cnt >= k) tau = cand;
     if (cnt == k) break;  // exactly k keys reach tau: the set is decided (uniform)
+  }
   }
   // ---- compaction in page order: every key above tau, then the lowest-index
   // keys equal to tau up to k in all (tau >= 1: keys past the row never take part;

@@ -42,7 +42,7 @@ class DecodeProblem:
     """
 
     def __init__(self, wl, inp, *, top_k=None, shuffle_seed=12345, device="cuda",
-                 max_pages=None, recent_tokens=0):
+                 max_pages=None, recent_tokens=None):
         self.wl = wl
         self.storage = inp["storage"]
         st = self.storage
@@ -52,6 +52,8 @@ class DecodeProblem:
         T = inp["z"].shape[2]
         S = wl.page_size
         self.top_k = int(top_k or wl.top_k)
+        if recent_tokens is None:
+            recent_tokens = wl.recent_tokens
         self.max_pages = int(max_pages or -(-T // S))
         self.num_phys = B * self.max_pages
         self.dims = api.make_dims(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh,

@@ -27,6 +27,7 @@ class StepShape:
     max_pages: int
     top_k: int
     elem: int  # bytes per stored element: 2 (bf16) or 4 (float32)
+    recent_tokens: int = 0  # recent window: its pages are attended besides the routed ones
 
 
 def _pages(seq_len, page_size):
@@ -75,13 +76,17 @@ def attend_bytes(s: StepShape, seq_lens):
     """attend: head_dim Key + r_v latent elements per selected token.  A
     sequence with more than top_k pages counts top_k full pages (exact when
     its last page is full or not selected); one with fewer counts its valid
-    tokens.  Plus queries, selection and the latent output u."""
+    tokens; a recent window adds the valid tokens of its pages.  Plus queries,
+    selection and the latent output u."""
     e = s.elem
     total = 0
     for L in seq_lens:
         L = max(0, int(L))
         n_pages = _pages(L, s.page_size)
-        if n_pages <= s.top_k:
+        if s.recent_tokens > 0:  # the window's pages, then top_k (or fewer) full pages before it
+            first = max(0, L - s.recent_tokens) // s.page_size
+            toks = L - first * s.page_size + min(first, s.top_k) * s.page_size
+        elif n_pages <= s.top_k:
             toks = L
         else:
             toks = s.top_k * s.page_size

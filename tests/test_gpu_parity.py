@@ -61,9 +61,9 @@ def compare_step(wl, inp, prob, out, seqs):
 
 
 def run_case(wl, *, batch=None, ctx=None, seq_lens=None, seqs=None, top_k=None, shuffle_seed=12345,
-             recent_tokens=0):
+             recent_tokens=None):
     _say(f"case {wl.name}: batch={batch or wl.batch} ctx={ctx or wl.ctx} seq_lens={seq_lens} "
-         f"top_k={top_k or wl.top_k} recent={recent_tokens}")
+         f"top_k={top_k or wl.top_k} recent={wl.recent_tokens if recent_tokens is None else recent_tokens}")
     inp = synth.decode_inputs(wl, batch=batch, ctx=ctx, seq_lens=seq_lens)
     prob = DecodeProblem(wl, inp, top_k=top_k, shuffle_seed=shuffle_seed,
                          recent_tokens=recent_tokens)
@@ -212,10 +212,15 @@ def test_recent_window_wider_than_some_sequences():
              recent_tokens=400)
 
 
-def test_adopted_router_b16r16_page4():
-    wl = workload(1).with_(name="llama8b-v96-b16r16-page4", r_b=16, r_q=16, page_size=4,
-                           top_k=512, ctx=16384, batch=2, n_planted=8, planted="random")
-    run_case(wl, seq_lens=[16384, 12001], recent_tokens=64)
+def test_adopted_router_b16r16_page4_sampled():
+    """The adopted router workload at full size (8 x 32K, 8192 pages of 4
+    tokens, 512 routed pages + 64 recent tokens), two sequences checked."""
+    run_case(workload("llama8b-ctx32k-b16r16-page4"), seqs=(0, 5))
+
+
+def test_adopted_router_ragged():
+    wl = workload("llama8b-ctx32k-b16r16-page4")
+    run_case(wl, batch=4, ctx=8192, seq_lens=[8192, 8191, 2100, 63])
 
 
 def test_recent_window_one_call_step_equals_separate_calls():
