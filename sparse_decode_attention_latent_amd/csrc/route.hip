@@ -246,6 +246,9 @@ hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32
   else if (mp <= 4096)
     hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
                        d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
+  else if (mp <= 8192)
+    hipLaunchKernelGGL((topk_select_kernel<8, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
   else if (mp <= 16384)
     hipLaunchKernelGGL((topk_select_kernel<16, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
                        d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
