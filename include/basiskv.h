@@ -216,6 +216,26 @@ int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void 
                             float *page_scores, int32_t *sel, float *u, void *y,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Dense decode attention over every page, the baseline the pages compare
+ * the method against (sparse decoding latency, Table 3: full-context Key and
+ * Value reads).  For each query head h of KV head g:
+ *   s_t = scale * q_h . k_t over the sequence's valid tokens,
+ *   p = softmax(s), o[b][h] = sum_t p_t v_t.
+ *   q [batch][n_q_heads][head_dim]; k_pages, v_pages: pools laid out as the
+ *   Key pool ([n_kv][num_phys][head_dim/CE][page_size][CE]); block_table
+ *   [batch][max_pages_per_seq] and seq_lens [batch] device; o [batch]
+ *   [n_q_heads][head_dim] float32 out (0 for an empty sequence).
+ * dims.r_v, r_b, r_q and recent_tokens are not used.  The output projection
+ * of the dense path is basiskv_reconstruct with dims.r_v = head_dim and the
+ * matrix basiskv_fuse_output_matrix builds from an identity decoder.
+ * workspace: basiskv_dense_workspace_bytes, zero-filled once, as for the
+ * other calls.  bf16 only (ERR_UNSUPPORTED for float32). */
+size_t basiskv_dense_workspace_bytes(const basiskv_dims *dims);
+int32_t basiskv_dense_attend(const basiskv_dims *dims, const void *q, const void *k_pages,
+                             const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, float scale, float *o, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* Set-up: fuse the Value decoder into the output projection,
  *   M[n][h * r_v + i] = sum_d Bf[h / G][i][d] * W_O[h * head_dim + d][n],
  * i.e. M = (blockdiag_h(Bf_{h/G}) W_O)^T, float32 accumulation, stored in dtype

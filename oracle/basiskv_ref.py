@@ -236,6 +236,20 @@ def attend_group(q_group, kc, z, sel, seq_len, page_size, scale):
     return w @ z[toks]
 
 
+def dense_attention(q_group, k, v, seq_len, scale):
+    """Dense decode attention, the baseline the pages' Table 3 compares with:
+    o_h = softmax(scale * q_h . k_t over the valid tokens) weighted sum of the
+    Values v_t.  q_group [G, dh], k, v [T, dh] -> [G, dh]; zeros when the
+    sequence is empty."""
+    L = max(0, int(seq_len))
+    if L == 0:
+        return np.zeros((q_group.shape[0], v.shape[1]))
+    s = scale * (q_group @ k[:L].T)
+    s = s - s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    return (w / w.sum(axis=1, keepdims=True)) @ v[:L]
+
+
 # ---------------------------------------------------------------------------
 # (a5) reconstruction through the Value decoder and the output projection
 # ---------------------------------------------------------------------------

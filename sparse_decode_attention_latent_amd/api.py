@@ -21,7 +21,8 @@ EXPORTED = (
     "basiskv_status_string", "basiskv_workspace_bytes", "basiskv_compress_prefill",
     "basiskv_project_queries", "basiskv_score_pages", "basiskv_select_pages",
     "basiskv_route_pages", "basiskv_sparse_attend", "basiskv_reconstruct",
-    "basiskv_decode_step", "basiskv_fuse_output_matrix",
+    "basiskv_decode_step", "basiskv_fuse_output_matrix", "basiskv_dense_workspace_bytes",
+    "basiskv_dense_attend",
 )
 
 
@@ -68,6 +69,8 @@ def _lib():
             "basiskv_decode_step": (I32, [DP, P, P, P, P, P, P, P, P, P, CP, I32, ctypes.c_float,
                                           P, P, P, P, P, SZ, P]),
             "basiskv_fuse_output_matrix": (I32, [DP, P, P, P, P]),
+            "basiskv_dense_workspace_bytes": (SZ, [DP]),
+            "basiskv_dense_attend": (I32, [DP, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -178,3 +181,17 @@ def fuse_output_matrix(dims, Bf, W_O, M, stream=None):
     _check(_lib().basiskv_fuse_output_matrix(ctypes.byref(dims), _ptr(Bf), _ptr(W_O), _ptr(M),
                                              _stream(stream)),
            "basiskv_fuse_output_matrix")
+
+
+def dense_workspace_bytes(dims):
+    return int(_lib().basiskv_dense_workspace_bytes(ctypes.byref(dims)))
+
+
+def dense_attend(dims, q, k_pages, v_pages, block_table, seq_lens, scale, o, workspace,
+                 stream=None):
+    """Dense decode attention over every page (the baseline)."""
+    _check(_lib().basiskv_dense_attend(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                       _ptr(block_table), _ptr(seq_lens), float(scale), _ptr(o),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)),
+           "basiskv_dense_attend")

@@ -256,6 +256,45 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   return launched(bkv_host::launch_reconstruct(*d, u, ut, M, y, s));
 }
 
+// The dense baseline's sizes: the attention sums Values (head_dim wide) in the
+// latent's place and attends every page, with no recent window.
+static basiskv_dims dense_dims(const basiskv_dims &d) {
+  basiskv_dims dd = d;
+  dd.r_v = d.head_dim;
+  dd.recent_tokens = 0;
+  return dd;
+}
+
+size_t basiskv_dense_workspace_bytes(const basiskv_dims *d) {
+  if (check_dims(d) != BASISKV_OK) return 0;
+  const basiskv_dims dd = dense_dims(*d);
+  return scratch_offset(dd) + partial_bytes(dd, dd.max_pages_per_seq);
+}
+
+int32_t basiskv_dense_attend(const basiskv_dims *d, const void *q, const void *k_pages,
+                             const void *v_pages, const int32_t *block_table,
+                             const int32_t *seq_lens, float scale, float *o, void *ws,
+                             size_t ws_bytes, void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return BASISKV_ERR_NULL;
+  const basiskv_dims dd = dense_dims(*d);
+  if (!bkv_host::attend_supported(dd)) return BASISKV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < scratch_offset(dd) + partial_bytes(dd, dd.max_pages_per_seq))
+    return BASISKV_ERR_WORKSPACE;
+  basiskv_cache c{};
+  c.k_pages = const_cast<void *>(k_pages);
+  c.z_pages = const_cast<void *>(v_pages);  // Values in the latent's place
+  c.block_table = block_table;
+  c.seq_lens = seq_lens;
+  bool unsupported = false;
+  hipError_t e = bkv_host::launch_attend(dd, q, c, nullptr, dd.max_pages_per_seq, scale, o,
+                                         scratch(ws, dd), attend_counters(ws), nullptr,
+                                         as_stream(stream), &unsupported);
+  if (unsupported) return BASISKV_ERR_UNSUPPORTED;
+  return launched(e);
+}
+
 int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const void *W_O, void *M,
                                    void *stream) {
   int32_t st = check_dims(d);

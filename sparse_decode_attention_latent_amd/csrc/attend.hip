@@ -40,6 +40,7 @@ constexpr int kAttendBlocks = BKV_ATTEND_BLOCKS;  // 64-token blocks per wavefro
 struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
   int recent;     // recent-window tokens (0: none)
+  int all_pages;  // dense attention: entry e is page e (no selection)
   int n_entries;  // entries per row: top_k routed, then the recent window's pages
   int gs;  // query subgroups per KV head (the kernel's group is n_q / n_kv / gs heads)
   int pages_per_split, n_split, total, padded;
@@ -130,7 +131,7 @@ void attend_split_kernel(
   const int e_begin = split * a.pages_per_split;
   const int e_end = min(a.n_entries, e_begin + a.pages_per_split);
   const int n_blocks = (e_end - e_begin + ppi - 1) / ppi;
-  const int32_t *sel_bg = sel + (int64_t)bg * a.top_k;
+  const int32_t *sel_bg = a.all_pages ? sel : sel + (int64_t)bg * a.top_k;
   const int32_t *bt = block_table + (int64_t)b * a.max_pages;
 
   // ---- this wavefront's blocks of round r: selection entries, then physical pages ----
@@ -146,8 +147,12 @@ void attend_split_kernel(
       const int blk = (r * NB + i) * NW + wave;
       const int e = e_begin + blk * ppi + (lane >> a.log2_page);
       const int pr = first_recent + (e - a.top_k);
-      page[i] = (blk < n_blocks && e < e_end) ? (e < a.top_k ? sel_bg[e] : (pr < NP ? pr : -1))
-                                               : -1;
+      int pg = -1;
+      if (blk < n_blocks && e < e_end) {
+        if (a.all_pages) pg = e < NP ? e : -1;
+        else pg = e < a.top_k ? sel_bg[e] : (pr < NP ? pr : -1);
+      }
+      page[i] = pg;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -617,12 +622,15 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.page_size = d.page_size;
   a.log2_page = ilog2i(d.page_size);
   a.cap = d.max_pages_per_seq * d.page_size;
+  // no selection given: dense attention over every page of the sequence
+  a.all_pages = sel == nullptr;
+  if (a.all_pages) top_k = d.max_pages_per_seq;
   a.top_k = top_k;
-  a.recent = d.recent_tokens;
-  a.n_entries = attend_entries(d, top_k);
+  a.recent = a.all_pages ? 0 : d.recent_tokens;
+  a.n_entries = a.all_pages ? top_k : attend_entries(d, top_k);
   a.gs = attend_group_split(d);
   a.pages_per_split = pages_per_split(d, a.n_entries);
-  a.n_split = attend_splits(d, top_k);
+  a.n_split = (a.n_entries + a.pages_per_split - 1) / a.pages_per_split;
   a.total = d.batch * d.n_kv_heads * a.gs * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
   a.scale_log2 = scale * kLog2e;

@@ -163,6 +163,58 @@ class DecodeProblem:
         return to_host_storage(z.contiguous(), self.storage), to_host_storage(r.contiguous(), self.storage)
 
 
+class DenseProblem:
+    """The dense baseline beside a DecodeProblem: the same queries, Key pool,
+    block table and sequence lengths, plus a Value pool of full head_dim
+    Values, and the output projection W_O in the reconstruction's tiled
+    layout (the fused matrix of an identity decoder).  Dense attention reads
+    every valid token's Key and Value (the pages' Table 3 comparison).
+
+    v: stored host Values [B, Hkv, T, dh] (for parity checks), or None for
+    seeded random Values drawn on the device (for timing).
+    """
+
+    def __init__(self, prob, v=None, seed=0):
+        wl, st = prob.wl, prob.storage
+        d = prob.dims
+        self.prob = prob
+        self.dims = api.make_dims(batch=d.batch, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                                  head_dim=d.head_dim, hidden=d.hidden, r_v=d.head_dim,
+                                  r_b=d.head_dim, r_q=d.r_q, page_size=d.page_size,
+                                  max_pages_per_seq=d.max_pages_per_seq,
+                                  num_phys_pages=d.num_phys_pages, dtype=d.dtype)
+        dev = prob.q.device
+        if v is not None:
+            self.v_pages = to_device(layout.pack_pages(v, prob.block_table_host, wl.page_size,
+                                                       prob.num_phys), st, dev)
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            self.v_pages = torch.randn(prob.k_pages.shape, generator=g, device=dev,
+                                       dtype=prob.k_pages.dtype)
+        dh, hq, hkv = d.head_dim, d.n_q_heads, d.n_kv_heads
+        eye = torch.eye(dh, dtype=prob.k_pages.dtype, device=dev).expand(hkv, dh, dh).contiguous()
+        self.M = torch.empty((wl.hidden, hq * dh), dtype=prob.M.dtype, device=dev)
+        api.fuse_output_matrix(self.dims, eye, prob.fac["W_O"], self.M)
+        self.workspace = torch.zeros(max(api.dense_workspace_bytes(self.dims), 256),
+                                     dtype=torch.uint8, device=dev)
+        self.o = torch.empty((d.batch, hq, dh), dtype=torch.float32, device=dev)
+        self.y = torch.empty_like(prob.y)
+
+    def attend(self):
+        p = self.prob
+        api.dense_attend(self.dims, p.q, p.k_pages, self.v_pages, p.block_table, p.seq_lens,
+                         p.scale, self.o, self.workspace)
+
+    def reconstruct(self):
+        api.reconstruct(self.dims, self.o.view(self.o.shape[0], -1), self.M, self.y)
+
+    def step(self):
+        """Dense decode attention and the output projection: the dense step."""
+        self.attend()
+        self.reconstruct()
+
+
 class PrefillProblem:
     """Compression of a batch of prompts into empty paged pools.
 

@@ -19,7 +19,7 @@ import torch
 from oracle import basiskv_ref as ref
 from sparse_decode_attention_latent_amd import api, synth
 from sparse_decode_attention_latent_amd.configs import workload
-from sparse_decode_attention_latent_amd.runner import DecodeProblem, PrefillProblem
+from sparse_decode_attention_latent_amd.runner import DecodeProblem, DenseProblem, PrefillProblem
 
 import parity
 
@@ -235,6 +235,38 @@ def test_recent_window_one_call_step_equals_separate_calls():
     for key in ("scores", "sel", "u", "y"):
         np.testing.assert_array_equal(got[key], base[key], err_msg=key)
     compare_step(wl, inp, prob, got, range(3))
+
+
+# ---------------------------------------------------------------------------
+# the dense baseline (full-context Key and Value reads; the pages' Table 3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl_index,seq_lens", [(2, [4096, 1000, 0, 33]), (3, [4096, 2047])])
+def test_dense_attend_matches_oracle(wl_index, seq_lens):
+    wl = workload(wl_index)
+    B = len(seq_lens)
+    inp = synth.decode_inputs(wl, batch=B, ctx=4096, seq_lens=seq_lens)
+    st = inp["storage"]
+    rng = np.random.default_rng(31)
+    v = synth.to_storage(rng.standard_normal(inp["kc"].shape), st)
+    prob = DecodeProblem(wl, inp)
+    dense = DenseProblem(prob, v=v)
+    dense.step()
+    torch.cuda.synchronize()
+    o = dense.o.double().cpu().numpy()
+    y = ref.storage_to_f64(dense.y.view(torch.int16).cpu().numpy().view(np.uint16), st)
+    q = ref.storage_to_f64(inp["q"], st)
+    kc, vv = ref.storage_to_f64(inp["kc"], st), ref.storage_to_f64(v, st)
+    W_O = ref.storage_to_f64(inp["W_O"], st)
+    G, scale = wl.group, 1 / math.sqrt(wl.head_dim)
+    for b, L in enumerate(seq_lens):
+        want = np.concatenate([ref.dense_attention(q[b, g * G:(g + 1) * G], kc[b, g], vv[b, g], L, scale)
+                               for g in range(wl.n_kv_heads)])
+        eo = parity.rel_rows(o[b], want)
+        assert eo.max() <= parity.U_RTOL, f"b={b}: o rel err {eo.max():.3g}"
+        ey = parity.rel_rows(y[b], want.reshape(-1) @ W_O)
+        assert ey <= parity.Y_RTOL[st], f"b={b}: y rel err {float(ey):.3g}"
+        _say(f"  dense {wl.name} b={b} L={L}: o {eo.max():.2e} y {float(ey):.2e}")
 
 
 @pytest.mark.parametrize("wl_index", [1, 2, 4])

@@ -421,6 +421,19 @@ def test_recent_window_covering_everything_is_dense_attention():
         np.testing.assert_allclose(out["u"][0, g * G:(g + 1) * G], want, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("L", [1, 7, 11])
+def test_dense_attention_equals_sdpa(L):
+    """The dense baseline's oracle against torch's scaled dot-product attention."""
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((4, 8)), rng.standard_normal((11, 8)), rng.standard_normal((11, 8))
+    got = ref.dense_attention(q, k, v, L, 1 / math.sqrt(8))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None], torch.from_numpy(k[:L])[None].expand(4, -1, -1),
+        torch.from_numpy(v[:L])[None].expand(4, -1, -1))[:, 0].numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    assert not ref.dense_attention(q, k, v, 0, 1.0).any()
+
+
 # ---------------------------------------------------------------------------
 # semantics of the synthetic workloads: planted pages are routed
 # ---------------------------------------------------------------------------
