@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama8b-ctx32k")
+    ap.add_argument("--context-sweep", action="store_true",
+                    help="instead of the bench line: the method's step against dense decode "
+                         "attention over 24K-96K contexts at batch 1 and 8 (JSON lines)")
     ap.add_argument("--cold-steps", type=int, default=100,
                     help="steps timed one by one after a 512 MiB cache flush (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -282,6 +285,69 @@ def prefill_and_sequence(wl, prob, inp, steps):
             d)
 
 
+SWEEP_CTX = (24576, 32768, 49152, 65536, 98304)
+SWEEP_BATCH = (1, 8)
+SWEEP_WORKLOADS = ("llama8b-ctx32k", "llama8b-ctx32k-b16r16-page4")
+
+
+def _time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def context_sweep(steps, warmup):
+    """The MI355X analogue of the pages' sparse-decoding latency table: one
+    decode step of the method against dense decode attention plus the output
+    projection, over 24K-96K contexts at batch 1 and 8.  Timing-only state:
+    pools and queries are seeded N(0, 1) draws made on the device (values do
+    not change the work of either path).  One JSON line per point."""
+    import torch
+
+    from sparse_decode_attention_latent_amd import synth, traffic
+    from sparse_decode_attention_latent_amd.configs import workload
+    from sparse_decode_attention_latent_amd.runner import DecodeProblem, DenseProblem
+
+    for B in SWEEP_BATCH:
+        for T in SWEEP_CTX:
+            row = {"batch": B, "ctx": T}
+            dense_us = None
+            for name in SWEEP_WORKLOADS:
+                wl = workload(name).with_(batch=B, ctx=T)
+                fac = dict(synth.factors(wl), storage=wl.storage)
+                prob = DecodeProblem(wl, fac, device_random=(B, T, 7))
+                us = _time_calls(prob.decode_step, steps, warmup)
+                shape = traffic.StepShape(batch=B, n_q_heads=wl.n_q_heads,
+                                          n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                                          hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
+                                          page_size=wl.page_size, max_pages=prob.max_pages,
+                                          top_k=wl.top_k, elem=2,
+                                          recent_tokens=wl.recent_tokens)
+                row[name] = {"us": round(us, 2),
+                             "gbs": round(traffic.step_bytes(shape, [T] * B)["total"] / (us * 1e-6) / 1e9, 1)}
+                if dense_us is None:  # dense baseline on the first workload's pools
+                    dense = DenseProblem(prob, seed=11)
+                    dense_us = _time_calls(dense.step, steps, warmup)
+                    dbytes = (B * wl.n_kv_heads * T * 2 * wl.head_dim * 2
+                              + wl.hidden * wl.n_q_heads * wl.head_dim * 2)
+                    row["dense"] = {"us": round(dense_us, 2),
+                                    "gbs": round(dbytes / (dense_us * 1e-6) / 1e9, 1)}
+                    del dense
+                row[name]["speedup_vs_dense"] = round(dense_us / us, 3)
+                del prob
+                torch.cuda.empty_cache()
+            print(json.dumps(row), flush=True)
+
+
 def _shape(wl, B, inp):
     from sparse_decode_attention_latent_amd import traffic
     T = inp["z"].shape[2]
@@ -294,6 +360,14 @@ def _shape(wl, B, inp):
 
 def main():
     args = parse()
+    if args.context_sweep:
+        import torch
+        from sparse_decode_attention_latent_amd import api
+        if not torch.cuda.is_available():
+            sys.exit("bench.py needs a GPU")
+        api.lib()
+        context_sweep(args.steps, args.warmup)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
         return

@@ -42,14 +42,22 @@ class DecodeProblem:
     """
 
     def __init__(self, wl, inp, *, top_k=None, shuffle_seed=12345, device="cuda",
-                 max_pages=None, recent_tokens=None):
+                 max_pages=None, recent_tokens=None, device_random=None):
+        """device_random: None, or (batch, ctx, seed) for timing-only state whose
+        pools, queries and new token are seeded N(0, 1) draws made on the device
+        (inp then only supplies the factors); the selection is then arbitrary
+        but valid, and no host copy of the caches exists."""
         self.wl = wl
         self.storage = inp["storage"]
         st = self.storage
-        q = inp["q"]
-        B, Hq, dh = q.shape
-        Hkv = inp["z"].shape[1]
-        T = inp["z"].shape[2]
+        if device_random is None:
+            q = inp["q"]
+            B, Hq, dh = q.shape
+            Hkv = inp["z"].shape[1]
+            T = inp["z"].shape[2]
+        else:
+            B, T, seed = device_random
+            Hq, dh, Hkv = wl.n_q_heads, wl.head_dim, wl.n_kv_heads
         S = wl.page_size
         self.top_k = int(top_k or wl.top_k)
         if recent_tokens is None:
@@ -66,16 +74,28 @@ class DecodeProblem:
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         dev = device
         self.block_table = torch.from_numpy(self.block_table_host).to(dev)
-        self.seq_lens_host = np.asarray(inp["seq_lens"], dtype=np.int32)
-        self.seq_lens = torch.from_numpy(self.seq_lens_host).to(dev)
-        self.z_pages = to_device(layout.pack_pages(inp["z"], self.block_table_host, S, self.num_phys), st, dev)
-        self.r_pages = to_device(layout.pack_pages(inp["r"], self.block_table_host, S, self.num_phys), st, dev)
-        self.k_pages = to_device(layout.pack_pages(inp["kc"], self.block_table_host, S, self.num_phys), st, dev)
-        self.q = to_device(q, st, dev)
         self.fac = {k: to_device(inp[k], st, dev) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
-        # appended token of the step: [B, 1, Hkv, dh], written at seq_len - 1
-        self.k_new = to_device(inp["k_new"][:, None], st, dev)
-        self.v_new = to_device(inp["v_new"][:, None], st, dev)
+        if device_random is None:
+            self.seq_lens_host = np.asarray(inp["seq_lens"], dtype=np.int32)
+            pack = lambda a: to_device(layout.pack_pages(a, self.block_table_host, S, self.num_phys),
+                                       st, dev)
+            self.z_pages, self.r_pages, self.k_pages = pack(inp["z"]), pack(inp["r"]), pack(inp["kc"])
+            self.q = to_device(q, st, dev)
+            # appended token of the step: [B, 1, Hkv, dh], written at seq_len - 1
+            self.k_new = to_device(inp["k_new"][:, None], st, dev)
+            self.v_new = to_device(inp["v_new"][:, None], st, dev)
+        else:
+            self.seq_lens_host = np.full(B, T, dtype=np.int32)
+            tdt = torch.bfloat16 if st == "bf16" else torch.float32
+            ce = 8 if st == "bf16" else 4
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(seed)
+            rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=tdt)
+            pool = lambda w: rnd(Hkv, self.num_phys, w // ce, S, ce)
+            self.z_pages, self.r_pages, self.k_pages = pool(wl.r_v), pool(wl.r_q), pool(dh)
+            self.q = rnd(B, Hq, dh)
+            self.k_new, self.v_new = rnd(B, 1, Hkv, dh), rnd(B, 1, Hkv, dh)
+        self.seq_lens = torch.from_numpy(self.seq_lens_host).to(dev)
         self.start_pos = (self.seq_lens - 1).to(torch.int32)
         self.cache = api.make_cache(self.z_pages, self.r_pages, self.k_pages, self.block_table,
                                     self.seq_lens)
