@@ -19,7 +19,7 @@ import torch
 from oracle import basiskv_ref as ref
 from sparse_decode_attention_latent_amd import api, synth
 from sparse_decode_attention_latent_amd.configs import workload
-from sparse_decode_attention_latent_amd.runner import DecodeProblem, DenseProblem, PrefillProblem
+from sparse_decode_attention_latent_amd.runner import DecodeProblem, DenseProblem, PrefillProblem, to_device
 
 import parity
 
@@ -97,6 +97,38 @@ def test_qwen32b_ctx32k_full_sampled():
 def test_prefill_decode_128k_decode_step_sampled():
     # the decode step at the longest context of the prefill + decode workload
     run_case(workload(4), seqs=(0, 1))
+
+
+def test_prefill_decode_128k_sequence_steps():
+    """Steps 0, 1, 2, 63 and 127 of the workload's 128 decode steps (context
+    131072 - 127 + i, the step's own queries, the new token appended at the
+    end), run in order on one cache: each checked against the oracle on the
+    cache as the earlier checked steps left it."""
+    wl = workload(4)
+    inp = synth.decode_inputs(wl)
+    st = inp["storage"]
+    prob = DecodeProblem(wl, inp)
+    L_last = int(inp["seq_lens"].max())
+    B = inp["q"].shape[0]
+    for i in (0, 1, 2, 63, 127):
+        L = L_last - (wl.decode_steps - 1) + i
+        q = synth.step_queries(wl, batch=B, step=i)
+        prob.seq_lens.fill_(L)
+        prob.start_pos.fill_(L - 1)
+        prob.q.copy_(to_device(q, st))
+        prob.decode_step()
+        out = prob.outputs()
+        step_inp = dict(inp, q=q, seq_lens=np.full(B, L, dtype=np.int32))
+        _say(f"step {i}: ctx {L}")
+        compare_step(wl, step_inp, prob, out, range(B))
+        fac = {n: ref.storage_to_f64(inp[n], st) for n in ("A", "P", "E")}
+        for b in range(B):  # the appended token stays in the cache for the later steps
+            zs, rs, _ = ref.compress_tokens(ref.storage_to_f64(inp["k_new"][b:b + 1], st),
+                                            ref.storage_to_f64(inp["v_new"][b:b + 1], st),
+                                            fac["A"], fac["P"], fac["E"], wl.r_b, st)
+            inp["z"][b, :, L - 1] = synth.to_storage(zs[0], st)
+            inp["r"][b, :, L - 1] = synth.to_storage(rs[0], st)
+            inp["kc"][b, :, L - 1] = inp["k_new"][b]
 
 
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
