@@ -44,14 +44,18 @@ Readings of points the pages leave open (each used below):
      pages' adopted router: 64 recent tokens besides the routed budget) is
      taken page by page: the pages holding the last W valid tokens are always
      attended, and the top-k routed pages are chosen among the pages before
-     them.
+     them;  R12 an FP8 cache (appendix Table 13: E4M3) holds the OCP E4M3FN
+     code of each value with no scale factor (scale 1): exponent bias 7,
+     3 mantissa bits, largest finite magnitude 448, subnormal step 2**-9, no
+     infinities; writes round to nearest even and saturate to +-448 instead
+     of producing the NaN code.
 """
 
 import math
 
 import numpy as np
 
-_STORAGES = ("f32", "bf16", "f64")
+_STORAGES = ("f32", "bf16", "fp8", "f64")
 
 
 # ---------------------------------------------------------------------------
@@ -62,8 +66,8 @@ def storage_to_f64(a, storage):
     """Decode stored values to float64, exactly.
 
     ``storage`` is "f32" (float32 array), "bf16" (uint16 bit patterns: the
-    upper half of an IEEE float32) or "f64" (no storage rounding; used by the
-    exactness pins).
+    upper half of an IEEE float32), "fp8" (uint8 E4M3FN codes, reading R12)
+    or "f64" (no storage rounding; used by the exactness pins).
     """
     if storage == "f64":
         return np.asarray(a, dtype=np.float64)
@@ -72,7 +76,22 @@ def storage_to_f64(a, storage):
     if storage == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if storage == "fp8":
+        return _e4m3_decode(np.asarray(a, dtype=np.uint8))
     raise ValueError(f"unknown storage {storage!r}")
+
+
+def _e4m3_decode(codes):
+    """E4M3FN code -> value (R12): sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent field 0 is subnormal (m * 2**-9); the two
+    codes with every exponent and mantissa bit set are NaN."""
+    c = codes.astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
+    return sign * mag
 
 
 def round_to_storage(x, storage):
@@ -89,6 +108,8 @@ def round_to_storage(x, storage):
         return x.copy()
     if storage == "f32":
         return x.astype(np.float32).astype(np.float64)
+    if storage == "fp8":
+        return _round_e4m3(x)
     if storage != "bf16":
         raise ValueError(f"unknown storage {storage!r}")
     out = np.zeros_like(x)
@@ -102,6 +123,24 @@ def round_to_storage(x, storage):
     rounded = np.where(np.abs(rounded) > bf16_max, np.copysign(np.inf, rounded), rounded)
     out[nz] = rounded
     out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+def _round_e4m3(x):
+    """Nearest E4M3FN value, ties to even, saturating at +-448 (R12).
+
+    E4M3 carries 4 significant bits, so a value with frexp exponent e has the
+    quantum 2**(e-4); below the smallest normal (2**-6, frexp exponent -5) the
+    quantum stays 2**-9 (subnormals).  NaN stays NaN; +-inf saturates.
+    """
+    out = np.zeros_like(x)
+    nz = (x != 0) & ~np.isnan(x)
+    xs = np.clip(x[nz], -448.0, 448.0)
+    _, e = np.frexp(xs)
+    quantum = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    out[nz] = np.clip(np.round(xs / quantum) * quantum, -448.0, 448.0)
+    out[np.isnan(x)] = np.nan
+    out[x == 0] = x[x == 0]
     return out
 
 
@@ -273,12 +312,13 @@ def reconstruct(u, Bf, W_O, group):
 
 def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
                 top_k, n_pages_out, storage, scale=None, k_new=None, v_new=None,
-                store_output=True, recent_tokens=0):
+                store_output=True, recent_tokens=0, cache_storage=None):
     """One decode step of one layer for a batch.
 
     Inputs are float64 (decode stored values with storage_to_f64 first);
-    ``storage`` names the format the cache is written in ("f32", "bf16",
-    "f64").  If k_new / v_new ([B, Hkv, dh]) are given, the step first
+    ``storage`` names the format of the output store ("f32", "bf16",
+    "f64") and ``cache_storage`` (default: ``storage``) the one the cache is
+    written in (also "fp8", R12).  If k_new / v_new ([B, Hkv, dh]) are given, the step first
     compresses that token into position seq_lens[b] - 1 of each sequence
     (a0); then it routes (a1, a2), selects (a3), attends (a4) and
     reconstructs (a5).  With recent_tokens > 0 the top-k pages are chosen
@@ -304,7 +344,8 @@ def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
             pos = int(seq_lens[b]) - 1
             if pos < 0 or pos >= z.shape[2]:
                 continue
-            zs, rs, ks = compress_tokens(k_new[b:b + 1], v_new[b:b + 1], A, P, E, rb, storage)
+            zs, rs, ks = compress_tokens(k_new[b:b + 1], v_new[b:b + 1], A, P, E, rb,
+                                         cache_storage or storage)
             z[b, :, pos, :] = zs[0]
             r[b, :, pos, :] = rs[0]
             kc[b, :, pos, :] = ks[0]

@@ -30,6 +30,7 @@ class Workload:
     noise: float = 0.05
     seed: int = 1000
     recent_tokens: int = 0  # recent window attended besides the routed pages
+    cache_storage: str = ""  # "fp8": z, r and Key pages as E4M3 codes ("" = storage)
     # prefill + decode workload only
     prefill_batch: int = 0
     prefill_tokens: int = 0
@@ -42,6 +43,11 @@ class Workload:
     @property
     def max_pages(self):
         return -(-self.ctx // self.page_size)
+
+    @property
+    def cache(self):
+        """Format of the cached pages (z, r, Keys)."""
+        return self.cache_storage or self.storage
 
     def with_(self, **kw):
         return replace(self, **kw)

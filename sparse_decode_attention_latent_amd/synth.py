@@ -4,7 +4,8 @@ This module only draws random numbers and shapes them into the workloads'
 structure; it holds none of the method's steps (no compression, routing,
 selection, attention or reconstruction).  Both the HIP path and the oracle
 consume what it returns, as stored arrays: float32 for "f32" storage,
-uint16 bf16 bit patterns for "bf16".
+uint16 bf16 bit patterns for "bf16", uint8 E4M3FN codes for "fp8" (the
+cache of an FP8 workload: z, r and the Keys; its other arrays are bf16).
 
 Recipe (per workload, see configs.py):
   factors   P [Hkv, rb, dh] ~ N(0,1)/sqrt(rb), Q [Hkv, rq, dh] ~ N(0,1)/sqrt(rq),
@@ -47,11 +48,14 @@ def _workers():
 
 def to_storage(x, storage):
     """float64 -> stored array.  bf16: float32 bits rounded to the upper 16
-    bits, nearest-even."""
+    bits, nearest-even.  fp8: E4M3FN codes of the float32 value, nearest-even,
+    saturated at +-448."""
     if storage == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     if storage == "f64":
         return np.ascontiguousarray(x, dtype=np.float64)
+    if storage == "fp8":
+        return _e4m3_codes(np.asarray(x, dtype=np.float32))
     if storage != "bf16":
         raise ValueError(storage)
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -59,15 +63,37 @@ def to_storage(x, storage):
     return b.astype(np.uint16)
 
 
+def _e4m3_codes(x32):
+    """float32 -> E4M3FN codes: bias 7, 3 mantissa bits; |x| >= 2**-6 keeps
+    the float32 exponent and rounds its 23-bit mantissa to 3 bits (carry into
+    the exponent included), smaller magnitudes are multiples of 2**-9."""
+    a = np.minimum(np.abs(x32), np.float32(448.0))
+    bits = a.view(np.uint32).astype(np.uint64)
+    bits = (bits + np.uint64(0x7FFFF) + ((bits >> np.uint64(20)) & np.uint64(1))) >> np.uint64(20)
+    normal = ((bits >> np.uint64(3)) - np.uint64(120)) << np.uint64(3) | (bits & np.uint64(7))
+    sub = np.rint(a.astype(np.float64) * 512.0).astype(np.uint64)
+    code = np.where(a >= np.float32(2.0 ** -6), normal, sub).astype(np.uint8)
+    return np.where(np.signbit(x32), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _e4m3_values(codes):
+    c = codes.astype(np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(c & 0x80, -mag, mag)
+
+
 def from_storage(a, storage):
     if storage in ("f32", "f64"):
         return np.asarray(a, dtype=np.float64)
+    if storage == "fp8":
+        return _e4m3_values(np.asarray(a, dtype=np.uint8))
     return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
         np.float32).astype(np.float64)
 
 
 def storage_dtype(storage):
-    return {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}[storage]
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "f64": np.float64}[storage]
 
 
 # ---------------------------------------------------------------------------
@@ -135,7 +161,8 @@ def _codes(wl, key, n):
     return z, r
 
 
-def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, storage=None):
+def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, storage=None,
+                  cache_storage=None):
     """Inputs of one decode step of a decode workload.
 
     Returns a dict of stored arrays:
@@ -144,7 +171,9 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
       seq_lens [B] int32; planted: list of per-sequence page arrays; and the
       factor arrays (A, Bf, P, Q, E, W_O).
     ``exact`` removes the noise terms (keys and values become exact low-rank
-    functions of the codes).  ``storage`` overrides the workload's format.
+    functions of the codes).  ``storage`` overrides the workload's format and
+    ``cache_storage`` its cache format (z, r, kc; default: the workload's
+    cache format, else ``storage``); the dict names both.
     """
     st = storage or wl.storage
     B = batch or wl.batch
@@ -161,9 +190,11 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
     q_st = to_storage(q, st)
 
     sd = storage_dtype(st)
-    z_st = np.empty((B, hkv, T, wl.r_v), dtype=sd)
-    r_st = np.empty((B, hkv, T, wl.r_q), dtype=sd)
-    k_st = np.empty((B, hkv, T, dh), dtype=sd)
+    cst = cache_storage or wl.cache_storage or st
+    cd = storage_dtype(cst)
+    z_st = np.empty((B, hkv, T, wl.r_v), dtype=cd)
+    r_st = np.empty((B, hkv, T, wl.r_q), dtype=cd)
+    k_st = np.empty((B, hkv, T, dh), dtype=cd)
     kn_st = np.empty((B, hkv, dh), dtype=sd)
     vn_st = np.empty((B, hkv, dh), dtype=sd)
     planted = [planted_pages(wl, b, -(-max(int(seq_lens[b]), 1) // wl.page_size)) for b in range(B)]
@@ -179,9 +210,9 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         k = z[:, :wl.r_b] @ Pf[g] + r @ Qf[g]
         if noise:
             k += noise * _rng(wl.seed, _ID["knoise"], b, g).standard_normal((T, dh))
-        z_st[b, g] = to_storage(z, st)
-        r_st[b, g] = to_storage(r, st)
-        k_st[b, g] = to_storage(k, st)
+        z_st[b, g] = to_storage(z, cst)
+        r_st[b, g] = to_storage(r, cst)
+        k_st[b, g] = to_storage(k, cst)
         # the token appended by the step, at position seq_len - 1
         zn = _rng(wl.seed, _ID["znew"], b, g).standard_normal(wl.r_v)
         if wl.latent_norm_sigma > 0:
@@ -203,7 +234,7 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         list(ex.map(one, [(b, g) for b in range(B) for g in range(hkv)]))
 
     out = dict(q=q_st, z=z_st, r=r_st, kc=k_st, k_new=kn_st, v_new=vn_st, seq_lens=seq_lens,
-               planted=planted, storage=st)
+               planted=planted, storage=st, cache_storage=cst)
     out.update(fac)
     return out
 

@@ -60,6 +60,87 @@ def test_bf16_decode_matches_torch():
     np.testing.assert_array_equal(mine, lib)
 
 
+def _e4m3_values():
+    """Every finite non-negative E4M3FN value with its code, enumerated from
+    the format's fields (bias 7, 3 mantissa bits, exponent field 0 subnormal,
+    code 0x7F reserved for NaN), written out independently of the oracle."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append((m / 8.0 * 2.0 ** -6) if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    return vals
+
+
+def _nearest_e4m3(x, vals):
+    """Brute force: the nearest value in the table (ties to the even code),
+    magnitudes past 448 saturated."""
+    a = min(abs(x), 448.0)
+    best = min(range(len(vals)), key=lambda c: (abs(vals[c] - a), c & 1))
+    return math.copysign(vals[best], x)
+
+
+def test_fp8_decode_matches_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = ref.storage_to_f64(codes, "fp8")
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, lib)  # NaN codes compare equal here too
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF])
+    assert mine[0x7E] == 448.0 and mine[0xFE] == -448.0
+    assert mine[0x38] == 1.0 and mine[0xB8] == -1.0
+    assert mine[0x08] == 2.0 ** -6 and mine[0x01] == 2.0 ** -9 and mine[0x07] == 7 * 2.0 ** -9
+    np.testing.assert_array_equal(mine[:0x7F], _e4m3_values())
+
+
+def test_fp8_rounding_matches_brute_nearest_and_torch():
+    rng = np.random.default_rng(11)
+    mag = np.exp2(rng.uniform(-13, 10, 4000))
+    x32 = (mag * np.where(rng.random(4000) < 0.5, -1, 1)).astype(np.float32)
+    vals = _e4m3_values()
+    # halfway cases, saturation, subnormal ties and zeros
+    special = [1.0625, 1.1875, -1.0625, 1.5 * 2 ** -9, 0.5 * 2 ** -9, 2.5 * 2 ** -9,
+               7.5 * 2 ** -9, 440.0, 448.0, 456.0, 464.0, 1000.0, -1e6, 0.0, 2 ** -12]
+    x32[:len(special)] = special
+    mine = ref.round_to_storage(x32.astype(np.float64), "fp8")
+    want = np.array([_nearest_e4m3(float(v), vals) for v in x32])
+    np.testing.assert_array_equal(mine, want)
+    clamped = torch.from_numpy(np.clip(x32, -448, 448))
+    lib = clamped.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, lib)
+    assert mine[0] == 1.0 and mine[1] == 1.25 and mine[2] == -1.0
+    assert mine[3] == 2 * 2.0 ** -9 and mine[4] == 0.0 and mine[5] == 2 * 2.0 ** -9
+    assert mine[6] == 2.0 ** -6 and mine[8] == 448.0 and mine[10] == 448.0 and mine[12] == -448.0
+    assert np.isnan(ref.round_to_storage(np.array([np.nan]), "fp8")[0])
+
+
+def test_compress_into_fp8_cache_matches_brute():
+    """The step's append with an FP8 cache: the latent is rounded to E4M3
+    before the residual is formed from it (R7 with R12), the Key is stored
+    rounded; every stored value is the brute-force nearest E4M3 value."""
+    wl = tiny_workload(batch=2)
+    inp = synth.decode_inputs(wl, seq_lens=np.array([11, 4]))
+    d = unpack(inp)
+    vals = _e4m3_values()
+
+    def rnd(x):
+        return _nearest_e4m3(float(x), vals)
+
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rb=wl.r_b, page_size=wl.page_size,
+                          top_k=wl.top_k, n_pages_out=wl.max_pages, storage="f64",
+                          cache_storage="fp8", k_new=d["k_new"] * 7.0, v_new=d["v_new"] * 7.0)
+    for b, L in enumerate((11, 4)):
+        for g in range(wl.n_kv_heads):
+            zb, rb_ = brute.compress_token(d["k_new"][b, g] * 7.0, d["v_new"][b, g] * 7.0,
+                                           d["A"][g].tolist(), d["P"][g].tolist(),
+                                           d["E"][g].tolist(), wl.r_b, rnd)
+            np.testing.assert_array_equal(out["z"][b, g, L - 1], zb)
+            np.testing.assert_array_equal(out["r"][b, g, L - 1], rb_)
+            np.testing.assert_array_equal(out["kc"][b, g, L - 1],
+                                          [rnd(v) for v in d["k_new"][b, g] * 7.0])
+        # rows other than the appended one are untouched
+        np.testing.assert_array_equal(out["z"][b, :, :L - 1], d["z"][b, :, :L - 1])
+
+
 # ---------------------------------------------------------------------------
 # compression
 # ---------------------------------------------------------------------------
