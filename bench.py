@@ -165,12 +165,13 @@ def cpu_baseline(wl, inp, target_seconds):
     from sparse_decode_attention_latent_amd import traffic
 
     st = inp["storage"]
+    cst = inp.get("cache_storage", st)
     f = {k: ref.storage_to_f64(inp[k], st) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
     B = inp["q"].shape[0]
     one = _shape(wl, 1, inp)
     seqs = []
     for b in range(B):
-        x = {k: ref.storage_to_f64(inp[k][b:b + 1], st)
+        x = {k: ref.storage_to_f64(inp[k][b:b + 1], cst if k in ("z", "r", "kc") else st)
              for k in ("q", "z", "r", "kc", "k_new", "v_new")}
         x["L"] = inp["seq_lens"][b:b + 1]
         seqs.append(x)
@@ -181,7 +182,8 @@ def cpu_baseline(wl, inp, target_seconds):
         ref.decode_step(x["q"], x["z"], x["r"], x["kc"], x["L"], f["A"], f["Bf"], f["P"], f["Q"],
                         f["E"], f["W_O"], rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k,
                         n_pages_out=-(-x["z"].shape[2] // wl.page_size), storage=st,
-                        k_new=x["k_new"], v_new=x["v_new"], recent_tokens=wl.recent_tokens)
+                        k_new=x["k_new"], v_new=x["v_new"], recent_tokens=wl.recent_tokens,
+                        cache_storage=cst)
         elapsed += time.perf_counter() - t0
         nbytes += traffic.step_bytes(one, x["L"])["total"]
         done += 1
@@ -287,7 +289,8 @@ def prefill_and_sequence(wl, prob, inp, steps):
 
 SWEEP_CTX = (24576, 32768, 49152, 65536, 98304)
 SWEEP_BATCH = (1, 8)
-SWEEP_WORKLOADS = ("llama8b-ctx32k", "llama8b-ctx32k-b16r16-page4")
+SWEEP_WORKLOADS = ("llama8b-ctx32k", "llama8b-ctx32k-b16r16-page4", "llama8b-ctx32k-fp8",
+                   "llama8b-ctx32k-b16r16-page4-fp8")
 
 
 def _time_calls(fn, steps, warmup):
@@ -331,7 +334,8 @@ def context_sweep(steps, warmup):
                                           hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                           page_size=wl.page_size, max_pages=prob.max_pages,
                                           top_k=wl.top_k, elem=2,
-                                          recent_tokens=wl.recent_tokens)
+                                          recent_tokens=wl.recent_tokens,
+                                          cache_elem=1 if wl.cache == "fp8" else 0)
                 row[name] = {"us": round(us, 2),
                              "gbs": round(traffic.step_bytes(shape, [T] * B)["total"] / (us * 1e-6) / 1e9, 1)}
                 if dense_us is None:  # dense baseline on the first workload's pools
@@ -355,7 +359,8 @@ def _shape(wl, B, inp):
                              head_dim=wl.head_dim, hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b,
                              r_q=wl.r_q, page_size=wl.page_size, max_pages=-(-T // wl.page_size),
                              top_k=wl.top_k, elem=2 if inp["storage"] == "bf16" else 4,
-                             recent_tokens=wl.recent_tokens)
+                             recent_tokens=wl.recent_tokens,
+                             cache_elem=1 if inp.get("cache_storage") == "fp8" else 0)
 
 
 def main():
@@ -474,13 +479,14 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
         "us_per_layer": round(ms_per_step * 1e3, 3), "gpu_us_per_step": round(gpu_step_us, 3),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.storage,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.storage if wl.cache == wl.storage else f"{wl.storage} (E4M3 cache pages)",
         "data": "synthetic (seeded generator; no weights or datasets)",
         "config": {"workload": wl.name, "batch": shape.batch, "ctx": int(inp["z"].shape[2]),
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "hidden": wl.hidden, "page_size": wl.page_size,
                    "r_v": wl.r_v, "r_b": wl.r_b, "r_q": wl.r_q, "top_k": wl.top_k,
-                   "recent_tokens": wl.recent_tokens},
+                   "recent_tokens": wl.recent_tokens, "cache": wl.cache},
         "algorithmic_bytes_per_step": sb["total"],
         "stages_us": {k: round(v, 3) for k, v in per_stage.items()},
         "stages_host_bound": [k for k in stages if host_bound[k]],

@@ -26,9 +26,15 @@
  *     on `stream` (a hipStream_t; NULL = the default stream).  Calls on one
  *     stream are ordered; concurrent calls that share a workspace race.
  *   - `dims.dtype` is the storage format of queries, caches, factors, K/V
- *     inputs, M and y: BASISKV_F32 (float32) or BASISKV_BF16 (bfloat16).
- *     Arithmetic is float32 throughout (float32 accumulation; bf16 values are
- *     widened exactly; stores to bf16 round to nearest-even).
+ *     inputs, M and y: BASISKV_F32 (float32) or BASISKV_BF16 (bfloat16); or
+ *     BASISKV_BF16_FP8_E4M3: everything bf16 except the three cache pools,
+ *     which hold FP8 E4M3 codes (appendix Table 13: BasisKV under an FP8
+ *     E4M3 KV cache).  The codes are OCP E4M3FN (sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits; largest finite magnitude 448; subnormal step
+ *     2^-9; 0x7F and 0xFF are NaN; no infinities) with no scale factor.
+ *     Arithmetic is float32 throughout (float32 accumulation; bf16 and E4M3
+ *     values are widened exactly; stores round to nearest-even, and stores to
+ *     E4M3 saturate at +-448).
  *   - Query head h uses KV head h / (n_q_heads / n_kv_heads).
  *   - Device-side indices are range-checked by the kernels: a block_table
  *     entry outside [0, num_phys_pages), a selected page outside the
@@ -38,7 +44,7 @@
  *
  * Paged cache layout (one pool per state, head-major):
  *   pool[n_kv_heads][num_phys_pages][width / CE][page_size][CE]
- * where CE = 16 / sizeof(element) (8 for bf16, 4 for float32) and width is
+ * where CE = 16 / sizeof(element) (16 for E4M3, 8 for bf16, 4 for float32) and width is
  * r_v (z pool), r_q (r pool) or head_dim (k pool).  Token t of a page keeps its
  * 16-byte chunk c at ((c * page_size) + t) * 16 bytes from the page start, so
  * one wavefront with a token per lane reads page_size * 16 contiguous bytes per
@@ -64,7 +70,7 @@ typedef enum {
   BASISKV_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
 } basiskv_status;
 
-enum { BASISKV_F32 = 0, BASISKV_BF16 = 1 };
+enum { BASISKV_F32 = 0, BASISKV_BF16 = 1, BASISKV_BF16_FP8_E4M3 = 2 };
 
 /* Sizes of one layer's decode problem (host values). */
 typedef struct {
@@ -79,7 +85,7 @@ typedef struct {
   int32_t page_size;         /* tokens per page: 4, 8, 16, 32 or 64 */
   int32_t max_pages_per_seq; /* columns of block_table, <= 32768 */
   int32_t num_phys_pages;    /* pages per pool and per KV head */
-  int32_t dtype;             /* BASISKV_F32 or BASISKV_BF16 */
+  int32_t dtype;             /* BASISKV_F32, BASISKV_BF16 or BASISKV_BF16_FP8_E4M3 */
   int32_t recent_tokens;     /* >= 0: recent window (appendix Table 9 caption: 64 recent
                                 tokens beside the routed budget).  With W > 0 the pages
                                 holding a sequence's last W valid tokens, from page

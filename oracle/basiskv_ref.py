@@ -165,12 +165,24 @@ def compress_tokens(k_new, v_new, A, P, E, rb, storage):
     z_s = np.empty((n, hkv, A.shape[2]))
     r_s = np.empty((n, hkv, E.shape[2]))
     for g in range(hkv):
-        z = v_new[:, g, :] @ A[g]
-        z_s[:, g, :] = round_to_storage(z, storage)
-        residual_key = k_new[:, g, :] - z_s[:, g, :rb] @ P[g]
-        r_s[:, g, :] = round_to_storage(residual_key @ E[g], storage)
+        z_s[:, g, :] = round_to_storage(latent_code(v_new[:, g, :], A[g]), storage)
+        r_s[:, g, :] = round_to_storage(residual_code(k_new[:, g, :], z_s[:, g, :], P[g], E[g], rb),
+                                        storage)
     k_s = round_to_storage(k_new, storage)
     return z_s, r_s, k_s
+
+
+def latent_code(v, A_g):
+    """Unrounded Value latent z = v A_g of rows v [n, dh] (abstract: the Value
+    is kept only as a low-rank latent)."""
+    return v @ A_g
+
+
+def residual_code(k, z_s, P_g, E_g, rb):
+    """Unrounded residual code r = (k - z_s[:, :rb] P_g) E_g of rows k [n, dh]
+    given their stored latents z_s [n, rV] (reading R7: the part of the Key the
+    latent's leading rb dims do not predict, encoded with E_g)."""
+    return (k - z_s[:, :rb] @ P_g) @ E_g
 
 
 # ---------------------------------------------------------------------------

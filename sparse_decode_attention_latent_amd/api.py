@@ -13,7 +13,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libbasiskv.so")
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_FP8 = 0, 1, 2  # BF16_FP8: bf16 activations, E4M3 cache pages
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_WORKSPACE",
           5: "ERR_LAUNCH"}
 

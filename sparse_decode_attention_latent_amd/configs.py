@@ -85,6 +85,17 @@ EXTRA_WORKLOADS = (
              head_dim=128, hidden=4096, ctx=32768, page_size=4, r_v=96, r_b=16, r_q=16,
              top_k=512, recent_tokens=64, n_planted=8, planted="random",
              latent_norm_sigma=0.5, seed=1005),
+    # FP8 E4M3 caches (appendix Table 13: BasisKV B16R16 Page4 V96 under an
+    # E4M3 KV cache): the headline 8B-shaped step and the adopted router with
+    # latent, residual and Key pages stored as E4M3 codes, bf16 elsewhere.
+    Workload("llama8b-ctx32k-fp8", "bf16", batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
+             hidden=4096, ctx=32768, page_size=32, r_v=64, r_b=64, r_q=32, top_k=128,
+             n_planted=8, planted="random", latent_norm_sigma=0.5, seed=1006,
+             cache_storage="fp8"),
+    Workload("llama8b-ctx32k-b16r16-page4-fp8", "bf16", batch=8, n_q_heads=32, n_kv_heads=8,
+             head_dim=128, hidden=4096, ctx=32768, page_size=4, r_v=96, r_b=16, r_q=16,
+             top_k=512, recent_tokens=64, n_planted=8, planted="random",
+             latent_norm_sigma=0.5, seed=1007, cache_storage="fp8"),
 )
 
 HEADLINE = 2

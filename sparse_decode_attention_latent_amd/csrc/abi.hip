@@ -16,14 +16,13 @@ namespace {
 constexpr int kMaxPages = 32768;
 constexpr int kMaxGroup = 16;
 
-int elem_chunk(int dtype) { return dtype == BASISKV_BF16 ? 8 : 4; }
-
 bool pow2_page(int s) { return s == 4 || s == 8 || s == 16 || s == 32 || s == 64; }
 
 // Sizes common to every call.
 int32_t check_dims(const basiskv_dims *d) {
   if (!d) return BASISKV_ERR_NULL;
-  if (d->dtype != BASISKV_F32 && d->dtype != BASISKV_BF16) return BASISKV_ERR_UNSUPPORTED;
+  if (d->dtype != BASISKV_F32 && d->dtype != BASISKV_BF16 && d->dtype != BASISKV_BF16_FP8_E4M3)
+    return BASISKV_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
       d->hidden < 1 || d->r_v < 1 || d->r_b < 1 || d->r_q < 1 || d->page_size < 1 ||
       d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
@@ -32,7 +31,7 @@ int32_t check_dims(const basiskv_dims *d) {
   if (d->recent_tokens < 0) return BASISKV_ERR_SHAPE;
   if (d->head_dim != bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!pow2_page(d->page_size)) return BASISKV_ERR_UNSUPPORTED;
-  const int ce = elem_chunk(d->dtype);
+  const int ce = bkv_host::cache_chunk(*d);  // whole 16-byte chunks per cached row
   if (d->r_v % ce || d->r_b % ce || d->r_q % ce) return BASISKV_ERR_UNSUPPORTED;
   if (d->n_q_heads / d->n_kv_heads > kMaxGroup) return BASISKV_ERR_UNSUPPORTED;
   if (d->max_pages_per_seq > kMaxPages) return BASISKV_ERR_UNSUPPORTED;
@@ -43,7 +42,7 @@ int32_t check_dims(const basiskv_dims *d) {
 // The fused output matrix is stored in MFMA tiles: 16 output features by 32
 // (bf16) or 16 (float32) contraction slots.
 bool output_tiles_fit(const basiskv_dims &d) {
-  const int kstep = d.dtype == BASISKV_BF16 ? 32 : 16;
+  const int kstep = bkv_host::act_bf16(d) ? 32 : 16;
   return d.hidden % 16 == 0 && (d.n_q_heads * d.r_v) % kstep == 0;
 }
 
@@ -70,7 +69,7 @@ size_t counter_bytes(const basiskv_dims &d) {  // one per (sequence, query subgr
 }
 
 size_t utile_bytes(const basiskv_dims &d) {
-  if (d.dtype != BASISKV_BF16) return 0;
+  if (!bkv_host::act_bf16(d)) return 0;
   const size_t tiles = (size_t)(d.batch + 7) / 8;
   return align_up(tiles * ((size_t)d.n_q_heads * d.r_v / 32) * 1024);
 }
@@ -88,7 +87,7 @@ size_t scratch_offset(const basiskv_dims &d) { return counter_bytes(d) + utile_b
 
 int32_t *attend_counters(void *ws) { return static_cast<int32_t *>(ws); }
 uint16_t *u_tiles(void *ws, const basiskv_dims &d) {
-  return d.dtype == BASISKV_BF16
+  return bkv_host::act_bf16(d)
              ? reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + counter_bytes(d))
              : nullptr;
 }
@@ -213,7 +212,7 @@ int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M
   int32_t st = check_dims(d);
   if (st) return st;
   if (!u || !M || !y) return BASISKV_ERR_NULL;
-  if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
+  if (d->batch > (bkv_host::act_bf16(*d) ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   return launched(bkv_host::launch_reconstruct(*d, u, nullptr, M, y, as_stream(stream)));
 }
@@ -234,7 +233,7 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (d->r_v > bkv::kHeadDim || d->r_q > bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
     return BASISKV_ERR_UNSUPPORTED;
-  if (d->batch > (d->dtype == BASISKV_BF16 ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
+  if (d->batch > (bkv_host::act_bf16(*d) ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
   if (!ws || ws_bytes < scratch_offset(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;

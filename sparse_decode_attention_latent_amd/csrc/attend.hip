@@ -72,37 +72,46 @@ struct AttendArgs {
 // widest bf16 groups, whose streamed Key (64) and latent (4 per token group)
 // registers and accumulators (8 per head) come to 170 or more of the 256,
 // leaving too few for the rest, and for float32 (a 128-register Key): these
-// take one wavefront per SIMD and its whole register file.
-template <typename T, int G, int NVC>
+// take one wavefront per SIMD and its whole register file.  (E4M3 pages:
+// the Key takes 32 registers, the accumulators 16 per head.)
+template <typename C, int G, int NVC>
 constexpr int attend_waves_per_eu() {
   constexpr int nj = (kWave + kWave / NVC - 1) / (kWave / NVC);
-  return sizeof(T) == 4 || 64 + 4 * nj + 8 * G >= 170 ? 1 : BKV_ATTEND_WAVES_PER_EU;
+  constexpr int ce = Elem<C>::CE;
+  return sizeof(C) == 4 || (kHeadDim / ce) * 4 + 4 * nj + ce * G >= 170
+             ? 1 : BKV_ATTEND_WAVES_PER_EU;
 }
 
 typedef short attend_s4 __attribute__((ext_vector_type(4)));
 typedef float attend_f4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int G, int NVC, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<T, G, NVC>())))
+// T: query elements (float32 or bf16); C: cache elements (float32, bf16, or
+// E4M3 codes beside bf16 queries, whose Key chunks are widened to bf16 -- exact
+// -- for the same matrix instruction).
+template <typename T, typename C, int G, int NVC, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<C, G, NVC>())))
 void attend_split_kernel(
-    const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ zpool,
+    const T *__restrict__ q, const C *__restrict__ kpool, const C *__restrict__ zpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel, float *__restrict__ part, float *__restrict__ u_out,
     AttendArgs a) {
-  constexpr int CE = Elem<T>::CE;
+  constexpr int CE = Elem<C>::CE;     // cache elements per 16-byte chunk
   constexpr int NKC = kHeadDim / CE;  // Key chunks per token
   constexpr int RV = NVC * CE;        // latent width
   constexpr int TG = kWave / NVC;     // token groups in the latent phase
   constexpr int NJ = (kWave + TG - 1) / TG;
   constexpr int NW = kAttendWaves;
   constexpr bool kBf = sizeof(T) == 2;
+  constexpr bool kFp8 = sizeof(C) == 1;
+  static_assert(sizeof(C) == sizeof(T) || (kBf && kFp8), "E4M3 pages go with bf16 queries");
   constexpr bool kMfma = kBf;            // scores on the matrix cores
   constexpr bool kStream = kBf;          // next block's gathers overlap this block
   constexpr int QG = (G + 3) / 4;        // head quads (matrix-instruction row sets)
+  constexpr int NQC = kHeadDim / 8;      // 8-dim bf16 query chunks
 
-  // queries: matrix operands [quad][Key chunk][head in quad][8 dims] (bf16),
-  // else [head][dims] (packed bf16 pairs or float32)
-  __shared__ __align__(16) uint4 qa_lds[kMfma ? QG * NKC * 4 : 1];
+  // queries: matrix operands [quad][8-dim chunk][head in quad][8 dims] (bf16),
+  // else [head][dims] (float32)
+  __shared__ __align__(16) uint4 qa_lds[kMfma ? QG * NQC * 4 : 1];
   __shared__ __align__(16) float q_lds[kMfma ? 1 : G][kMfma ? 4 : kHeadDim];
   __shared__ float p_lds[NW][G][kWave];
   __shared__ float m_lds[NW][G];
@@ -167,10 +176,10 @@ void attend_split_kernel(
     const T *qg = q + ((int64_t)b * a.n_q + (int64_t)gv * G) * kHeadDim;
     if constexpr (kMfma) {
       // entry (quad, chunk c, head hq): dims 8c .. 8c + 7 of head 4 quad + hq (zero past G)
-      for (int i = threadIdx.x; i < QG * NKC * 4; i += blockDim.x) {
-        const int hq = i & 3, c = (i >> 2) % NKC, qd = i / (NKC * 4);
+      for (int i = threadIdx.x; i < QG * NQC * 4; i += blockDim.x) {
+        const int hq = i & 3, c = (i >> 2) % NQC, qd = i / (NQC * 4);
         const int h = qd * 4 + hq;
-        qa_lds[i] = h < G ? *reinterpret_cast<const uint4 *>(qg + h * kHeadDim + c * CE)
+        qa_lds[i] = h < G ? *reinterpret_cast<const uint4 *>(qg + h * kHeadDim + c * 8)
                           : make_uint4(0u, 0u, 0u, 0u);
       }
     } else {
@@ -284,17 +293,31 @@ void attend_split_kernel(
       const int hq = lane & 3;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
-        const attend_s4 klo = __builtin_bit_cast(attend_s4, make_uint2(kc[c].x, kc[c].y));
-        const attend_s4 khi = __builtin_bit_cast(attend_s4, make_uint2(kc[c].z, kc[c].w));
-#pragma unroll
-        for (int qd = 0; qd < QG; ++qd) {
-          const uint4 qv = qa_lds[(qd * NKC + c) * 4 + hq];
-          const attend_s4 qlo = __builtin_bit_cast(attend_s4, make_uint2(qv.x, qv.y));
-          const attend_s4 qhi = __builtin_bit_cast(attend_s4, make_uint2(qv.z, qv.w));
-          sc[qd][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qlo, klo, sc[qd][0], 0, 0, 0);
-          sc[qd][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qhi, khi, sc[qd][1], 0, 0, 0);
+        // this Key chunk as 8-dim bf16 chunks (E4M3: two, widened exactly)
+        constexpr int SUB = kFp8 ? 2 : 1;
+        uint4 kb[SUB];
+        if constexpr (kFp8) {
+          kb[0] = fp8x8_to_bf16x8(kc[c].x, kc[c].y);
+          kb[SUB - 1] = fp8x8_to_bf16x8(kc[c].z, kc[c].w);
+          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
+        } else {
+          kb[0] = kc[c];
         }
-        if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          const attend_s4 klo = __builtin_bit_cast(attend_s4, make_uint2(kb[sb].x, kb[sb].y));
+          const attend_s4 khi = __builtin_bit_cast(attend_s4, make_uint2(kb[sb].z, kb[sb].w));
+#pragma unroll
+          for (int qd = 0; qd < QG; ++qd) {
+            const uint4 qv = qa_lds[(qd * NQC + c * SUB + sb) * 4 + hq];
+            const attend_s4 qlo = __builtin_bit_cast(attend_s4, make_uint2(qv.x, qv.y));
+            const attend_s4 qhi = __builtin_bit_cast(attend_s4, make_uint2(qv.z, qv.w));
+            sc[qd][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qlo, klo, sc[qd][0], 0, 0, 0);
+            sc[qd][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qhi, khi, sc[qd][1], 0, 0, 0);
+          }
+        }
+        if constexpr (!kFp8)
+          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -323,7 +346,7 @@ void attend_split_kernel(
           if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);
         } else if (valid) {
           float x[CE];
-          unpack_chunk<T>(kc[c], x);
+          unpack_chunk<C>(kc[c], x);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const float4 q4 = *reinterpret_cast<const float4 *>(&q_lds[h][c * CE]);
@@ -373,7 +396,7 @@ void attend_split_kernel(
       if (zv[j]) {
         const int t = j * TG + tg;
         float x[CE];
-        unpack_chunk<T>(zc[j], x);
+        unpack_chunk<C>(zc[j], x);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float pr = p_lds[wave][h][t];
@@ -524,17 +547,26 @@ struct AttendVariant {
   const void *fn1, *fn;  // one block per wavefront and round; kAttendBlocks
 };
 
-#define BKV_ATT(T, DT, G, RV)                                                                   \
+#define BKV_ATT(T, C, DT, G, RV)                                                                \
   {DT, G, RV,                                                                                   \
-   reinterpret_cast<const void *>(&attend_split_kernel<T, G, (RV) / Elem<T>::CE, 1>),          \
-   reinterpret_cast<const void *>(&attend_split_kernel<T, G, (RV) / Elem<T>::CE, kAttendBlocks>)}
-#define BKV_ATT_G(T, DT, RV) \
-  BKV_ATT(T, DT, 1, RV), BKV_ATT(T, DT, 2, RV), BKV_ATT(T, DT, 4, RV), BKV_ATT(T, DT, 8, RV)
+   reinterpret_cast<const void *>(&attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, 1>),       \
+   reinterpret_cast<const void *>(                                                              \
+       &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks>)}
+#define BKV_ATT_G(T, C, DT, RV)                                                  \
+  BKV_ATT(T, C, DT, 1, RV), BKV_ATT(T, C, DT, 2, RV), BKV_ATT(T, C, DT, 4, RV), \
+      BKV_ATT(T, C, DT, 8, RV)
 
+// (r_v = 128 serves the dense baseline, which sums Values in the latent's place)
 static const AttendVariant kAttendVariants[] = {
-    BKV_ATT_G(uint16_t, BASISKV_BF16, 64), BKV_ATT_G(uint16_t, BASISKV_BF16, 96),
-    BKV_ATT_G(uint16_t, BASISKV_BF16, 32), BKV_ATT_G(uint16_t, BASISKV_BF16, 128),
-    BKV_ATT_G(float, BASISKV_F32, 64),     BKV_ATT_G(float, BASISKV_F32, 32),
+    BKV_ATT_G(uint16_t, uint16_t, BASISKV_BF16, 64),
+    BKV_ATT_G(uint16_t, uint16_t, BASISKV_BF16, 96),
+    BKV_ATT_G(uint16_t, uint16_t, BASISKV_BF16, 32),
+    BKV_ATT_G(uint16_t, uint16_t, BASISKV_BF16, 128),
+    BKV_ATT_G(float, float, BASISKV_F32, 64),
+    BKV_ATT_G(float, float, BASISKV_F32, 32),
+    BKV_ATT_G(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 64),
+    BKV_ATT_G(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 96),
+    BKV_ATT_G(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 128),
 };
 
 }  // namespace bkv
@@ -556,7 +588,7 @@ static int ilog2i(int x) {
 // mostly from cache).
 int attend_group_split(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
-  return d.dtype == BASISKV_BF16 && G == 8 && d.r_v >= 96 ? 2 : 1;
+  return act_bf16(d) && G == 8 && d.r_v >= 96 ? 2 : 1;
 }
 
 // Pages per split.  Every wavefront takes up to kAttendBlocks 64-token blocks

@@ -13,13 +13,18 @@ constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kXcds = 8;        // MI355X: 8 accelerator dies, each with its own L2
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Storage element types: float for BASISKV_F32, uint16_t (bf16 bits) for BASISKV_BF16.
+// Storage element types: float for BASISKV_F32, uint16_t (bf16 bits) for
+// BASISKV_BF16 and for the activations of BASISKV_BF16_FP8_E4M3, uint8_t
+// (E4M3FN codes) for that format's cache pages.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int CE = 4;  // elements per 16-byte chunk
 };
 template <> struct Elem<uint16_t> {
   static constexpr int CE = 8;
+};
+template <> struct Elem<uint8_t> {
+  static constexpr int CE = 16;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -39,12 +44,40 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// FP8 cache codes: OCP E4M3FN (exponent bias 7, 3 mantissa bits, largest
+// finite magnitude 448, no infinities), no scale factor.  gfx950 converts in
+// hardware (v_cvt_pk_fp8_f32 / v_cvt_f32_fp8, round to nearest even); its
+// encoder gives the NaN code for magnitudes of 464 and more, so the cache
+// writes saturate to +-448 first (a NaN input stays NaN).
+__device__ __forceinline__ float sat_e4m3(float x) {
+  return fabsf(x) > 448.f ? copysignf(448.f, x) : x;
+}
+// Four float32 values -> four E4M3 codes (a in the lowest byte).
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), lo, true);
+}
+__device__ __forceinline__ uint8_t f32_to_fp8(float x) {
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(x), 0.f, 0, false) & 0xff);
+}
+__device__ __forceinline__ float fp8_to_f32(uint8_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float to_f32(uint8_t x) { return fp8_to_f32(x); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ uint8_t from_f32<uint8_t>(float x) { return f32_to_fp8(x); }
+
+// x rounded to the cache format C, as float32 (exact: every bf16 and E4M3
+// value is a float32).
+template <typename C> __device__ __forceinline__ float round_to(float x) {
+  return to_f32(from_f32<C>(x));
+}
 
 // Widen one 16-byte chunk to float32 (exact for both formats).
 template <typename T> __device__ __forceinline__ void unpack_chunk(const uint4 &c, float *x);
@@ -63,6 +96,30 @@ template <> __device__ __forceinline__ void unpack_chunk<uint16_t>(const uint4 &
   x[5] = __uint_as_float(c.z & 0xffff0000u);
   x[6] = __uint_as_float(c.w << 16);
   x[7] = __uint_as_float(c.w & 0xffff0000u);
+}
+typedef float bkv_f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float *x) {
+  const bkv_f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const bkv_f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  x[0] = lo[0];
+  x[1] = lo[1];
+  x[2] = hi[0];
+  x[3] = hi[1];
+}
+template <> __device__ __forceinline__ void unpack_chunk<uint8_t>(const uint4 &c, float *x) {
+  fp8x4_to_f32(c.x, x);
+  fp8x4_to_f32(c.y, x + 4);
+  fp8x4_to_f32(c.z, x + 8);
+  fp8x4_to_f32(c.w, x + 12);
+}
+// Eight E4M3 codes (two words) -> eight bf16 values (exact), as one 8-element
+// bf16 chunk's worth of packed pairs.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float x[8];
+  fp8x4_to_f32(w0, x);
+  fp8x4_to_f32(w1, x + 4);
+  return make_uint4(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]),
+                    f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7]));
 }
 
 // acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16:
@@ -207,6 +264,15 @@ __host__ __device__ __forceinline__ int clamp_len(int L, int cap) {
 
 // Host-side launchers (defined in the .hip files, called by abi.hip after validation).
 namespace bkv_host {
+// bf16 activations (queries, factors, K/V inputs, M, y): BASISKV_BF16 and BASISKV_BF16_FP8_E4M3
+inline bool act_bf16(const basiskv_dims &d) { return d.dtype != BASISKV_F32; }
+// E4M3 cache pages
+inline bool cache_fp8(const basiskv_dims &d) { return d.dtype == BASISKV_BF16_FP8_E4M3; }
+// elements per 16-byte chunk of a cache page
+inline int cache_chunk(const basiskv_dims &d) {
+  return cache_fp8(d) ? 16 : (act_bf16(d) ? 8 : 4);
+}
+
 hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                           float *q_proj, hipStream_t s);
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,

@@ -51,20 +51,24 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 }
 
 // Compression of token `row` (= b * n_tokens + t) for KV head g, by a
-// workgroup of 256 threads.
-template <typename T>
+// workgroup of 256 threads.  T: input and factor elements; C: cache elements
+// (T itself, or E4M3 codes beside bf16 inputs: then the Key is rounded too).
+template <typename T, typename C>
 __device__ __forceinline__ void append_body(
     const T *__restrict__ kin, const T *__restrict__ vin, const int32_t *__restrict__ start_pos,
     const T *__restrict__ A, const T *__restrict__ P, const T *__restrict__ E,
-    T *__restrict__ zpool, T *__restrict__ rpool, T *__restrict__ kpool,
+    C *__restrict__ zpool, C *__restrict__ rpool, C *__restrict__ kpool,
     const int32_t *__restrict__ block_table, const AppendArgs &a, int g, int row) {
   constexpr int DH = kHeadDim;
   constexpr int CE = Elem<T>::CE;
+  constexpr int CC = Elem<C>::CE;  // cache elements per 16-byte chunk
+  constexpr bool kRoundKey = sizeof(C) != sizeof(T);
   constexpr int MAXL = 64 / CE;  // factor chunks per thread and phase (see the roles below)
   __shared__ float v_s[DH], k_s[DH], x_s[DH], zf[DH];
   __shared__ float red[4][DH];
-  __shared__ __align__(16) T zst[DH];
-  __shared__ __align__(16) T rst[DH];
+  __shared__ __align__(16) C zst[DH];
+  __shared__ __align__(16) C rst[DH];
+  __shared__ __align__(16) C kst[kRoundKey ? DH : CC];
   const int b = row / a.n_tokens, t = row - b * a.n_tokens;
   const int tid = threadIdx.x;
   const int64_t in_off = (((int64_t)b * a.n_tokens + t) * a.n_kv + g) * DH;
@@ -128,7 +132,7 @@ __device__ __forceinline__ void append_body(
   __syncthreads();
   if (tid < a.rv) {
     const float z = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    const T zs = from_f32<T>(z);
+    const C zs = from_f32<C>(z);
     zst[tid] = zs;
     zf[tid] = to_f32(zs);
   }
@@ -174,26 +178,30 @@ __device__ __forceinline__ void append_body(
   slice_sums<CE>(acc, P3, c3, C3, red);
   __syncthreads();
   if (tid < a.rq)
-    rst[tid] = from_f32<T>(red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
+    rst[tid] = from_f32<C>(red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
+  if (kRoundKey && tid < DH) kst[tid] = from_f32<C>(k_s[tid]);
   __syncthreads();
 
   // ---- page stores: one 16-byte chunk per thread ----
   if (!pos_ok || phys < 0 || phys >= a.num_phys) return;
   const int64_t hp = (int64_t)g * a.num_phys + phys;
-  const int zc = a.rv / CE, rc = a.rq / CE, kc = DH / CE;
+  const int zc = a.rv / CC, rc = a.rq / CC, kc = DH / CC;
   if (tid < zc + rc + kc) {
     uint4 val;
     char *dst;
     if (tid < zc) {
-      val = *reinterpret_cast<const uint4 *>(zst + tid * CE);
+      val = *reinterpret_cast<const uint4 *>(zst + tid * CC);
       dst = reinterpret_cast<char *>(zpool) + ((hp * zc + tid) * a.page_size + slot) * 16;
     } else if (tid < zc + rc) {
       const int c = tid - zc;
-      val = *reinterpret_cast<const uint4 *>(rst + c * CE);
+      val = *reinterpret_cast<const uint4 *>(rst + c * CC);
       dst = reinterpret_cast<char *>(rpool) + ((hp * rc + c) * a.page_size + slot) * 16;
     } else {
       const int c = tid - zc - rc;
-      val = *reinterpret_cast<const uint4 *>(kin + in_off + c * CE);
+      if constexpr (kRoundKey)
+        val = *reinterpret_cast<const uint4 *>(kst + c * CC);
+      else
+        val = *reinterpret_cast<const uint4 *>(kin + in_off + c * CC);
       dst = reinterpret_cast<char *>(kpool) + ((hp * kc + c) * a.page_size + slot) * 16;
     }
     *reinterpret_cast<uint4 *>(dst) = val;

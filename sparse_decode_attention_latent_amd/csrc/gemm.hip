@@ -279,15 +279,26 @@ struct CompressLds {  // byte offsets into the dynamic LDS block; strides in ele
   }
 };
 
-template <typename T>
+// T: input and factor elements; C: cache elements (T, or E4M3 codes beside
+// bf16 inputs: the latent and residual tiles then hold E4M3-rounded values in
+// bf16, which is exact, and the Key is rounded on its way to the pages).
+template <typename T, typename C>
 __global__ __launch_bounds__(256) void compress_kernel(
     const T *__restrict__ kin, const T *__restrict__ vin, const int32_t *__restrict__ start_pos,
     const T *__restrict__ A, const T *__restrict__ P, const T *__restrict__ E,
-    T *__restrict__ zpool, T *__restrict__ rpool, T *__restrict__ kpool,
+    C *__restrict__ zpool, C *__restrict__ rpool, C *__restrict__ kpool,
     const int32_t *__restrict__ block_table, CompressArgs a) {
   using MF = typename MfmaFor<T>::type;
   using frag = typename MF::frag;
   constexpr int CE = Elem<T>::CE;
+  constexpr int CC = Elem<C>::CE;  // cache elements per 16-byte chunk
+  constexpr bool kFp8 = sizeof(C) == 1;
+  static_assert(sizeof(C) == sizeof(T) || (kFp8 && sizeof(T) == 2), "E4M3 goes with bf16 inputs");
+  // a float32 result as it is stored (cache rounding), in the tile's type T
+  auto stored = [](float x) {
+    if constexpr (kFp8) return from_f32<T>(round_to<C>(x));
+    else return from_f32<T>(x);
+  };
   constexpr int DH = kHeadDim;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NKS = DH / MF::KS;  // k steps over head_dim
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
 
   const int rows = a.batch * a.n_tokens;
   const int n_blocks = (rows + 15) / 16;
-  const int zc_total = a.rv / CE, rc_total = a.rq / CE, kc_total = DH / CE;
+  const int zc_total = a.rv / CC, rc_total = a.rq / CC, kc_total = DH / CC;
 
   // A fragments of one 16-row block: lane (i, qg) holds row i's k slots of every k step
   frag va[NKS], ka[NKS];
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
         acc = MF::mma(va[ks], bfr, acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zs[(qg * 4 + r) * L.zs_stride + nt * 16 + i] = from_f32<T>(acc[r]);
+      for (int r = 0; r < 4; ++r) Zs[(qg * 4 + r) * L.zs_stride + nt * 16 + i] = stored(acc[r]);
     }
     for (int o = lane; o < 16 * (L.zs_stride - a.rv); o += 64) {
       const int rr = o / (L.zs_stride - a.rv), cc = a.rv + o % (L.zs_stride - a.rv);
@@ -457,22 +468,33 @@ __global__ __launch_bounds__(256) void compress_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        Rs[(qg * 4 + r) * a.rq + nt * 16 + i] = from_f32<T>(acc_k[r] - acc_z[r]);
+        Rs[(qg * 4 + r) * a.rq + nt * 16 + i] = stored(acc_k[r] - acc_z[r]);
     }
     wave_lds_sync();
 
     // ---- page stores: latent and residual chunks from LDS, Key chunks from the fragments ----
     const int64_t hp_own = (int64_t)g * a.num_phys + phys;
-    auto store_tile = [&](const T *tile, int stride, int n_chunks, T *pool) {
+    auto store_tile = [&](const T *tile, int stride, int n_chunks, C *pool) {
       for (int it = 0; it < (16 * n_chunks + 63) / 64; ++it) {
         const int o = it * 64 + lane;
         const int rr = o < 16 * n_chunks ? o / n_chunks : 0, c = o - rr * n_chunks;
         const int ph = __shfl(phys, rr), sl = __shfl(slot, rr);
         if (o < 16 * n_chunks && ph >= 0) {
           const int64_t hp = (int64_t)g * a.num_phys + ph;
+          uint4 val;
+          if constexpr (kFp8) {  // 16 tile values (already E4M3 values) -> 16 codes
+            float x[16];
+            unpack_chunk<T>(*reinterpret_cast<const uint4 *>(tile + rr * stride + c * CC), x);
+            unpack_chunk<T>(*reinterpret_cast<const uint4 *>(tile + rr * stride + c * CC + 8), x + 8);
+            val = make_uint4(f32x4_to_fp8x4(x[0], x[1], x[2], x[3]),
+                             f32x4_to_fp8x4(x[4], x[5], x[6], x[7]),
+                             f32x4_to_fp8x4(x[8], x[9], x[10], x[11]),
+                             f32x4_to_fp8x4(x[12], x[13], x[14], x[15]));
+          } else {
+            val = *reinterpret_cast<const uint4 *>(tile + rr * stride + c * CC);
+          }
           *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(pool) +
-                                     ((hp * n_chunks + c) * a.page_size + sl) * 16) =
-              *reinterpret_cast<const uint4 *>(tile + rr * stride + c * CE);
+                                     ((hp * n_chunks + c) * a.page_size + sl) * 16) = val;
         }
       }
     };
@@ -483,11 +505,17 @@ __global__ __launch_bounds__(256) void compress_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
         const int k = ks * MF::KS + qg * MF::KPL;  // element k of this lane's row
         char *base = reinterpret_cast<char *>(kpool) +
-                     ((hp_own * kc_total + k / CE) * a.page_size + slot) * 16;
-        if constexpr (kBf)
+                     ((hp_own * kc_total + k / CC) * a.page_size + slot) * 16;
+        if constexpr (kFp8) {  // 8 Key elements -> 8 codes, half a chunk
+          float x[8];
+          unpack_chunk<T>(__builtin_bit_cast(uint4, ka[ks]), x);
+          *reinterpret_cast<uint2 *>(base + k % CC) =
+              make_uint2(f32x4_to_fp8x4(x[0], x[1], x[2], x[3]), f32x4_to_fp8x4(x[4], x[5], x[6], x[7]));
+        } else if constexpr (kBf) {
           *reinterpret_cast<uint4 *>(base) = __builtin_bit_cast(uint4, ka[ks]);
-        else
+        } else {
           reinterpret_cast<float *>(base)[k % CE] = ka[ks];
+        }
       }
     }
     wave_lds_sync();  // the tiles are read before the next block overwrites them
@@ -539,8 +567,8 @@ static hipError_t recon_t(const basiskv_dims &d, const float *u, const uint16_t 
 
 hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const uint16_t *u_tiles,
                               const void *M, void *y, hipStream_t s) {
-  return d.dtype == BASISKV_BF16 ? recon_t<uint16_t>(d, u, u_tiles, M, y, s)
-                                 : recon_t<float>(d, u, nullptr, M, y, s);
+  return act_bf16(d) ? recon_t<uint16_t>(d, u, u_tiles, M, y, s)
+                     : recon_t<float>(d, u, nullptr, M, y, s);
 }
 
 template <typename T>
@@ -554,7 +582,7 @@ static hipError_t fuse_t(const basiskv_dims &d, const void *Bf, const void *W_O,
 
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
                        hipStream_t s) {
-  return d.dtype == BASISKV_BF16 ? fuse_t<uint16_t>(d, Bf, W_O, M, s) : fuse_t<float>(d, Bf, W_O, M, s);
+  return act_bf16(d) ? fuse_t<uint16_t>(d, Bf, W_O, M, s) : fuse_t<float>(d, Bf, W_O, M, s);
 }
 
 #ifndef BKV_COMPRESS_WGS
@@ -562,7 +590,7 @@ hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, v
 #endif
 constexpr int kCompressWgsPerHead = BKV_COMPRESS_WGS;
 
-template <typename T>
+template <typename T, typename C>
 static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v,
                              const int32_t *start_pos, int32_t n_tokens, const void *A,
                              const void *P, const void *E, const basiskv_cache &c, hipStream_t s) {
@@ -581,7 +609,7 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   a.cap = d.max_pages_per_seq * d.page_size;
   const size_t lds = compress_lds_bytes<T>(d, a.rb_pad);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compress_kernel<T>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compress_kernel<T, C>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -589,9 +617,10 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   const int n_blocks = (rows + 15) / 16;
   int wgs = (n_blocks + 3) / 4;
   if (wgs > kCompressWgsPerHead) wgs = kCompressWgsPerHead;  // persistent: factors staged once each
-  hipLaunchKernelGGL(compress_kernel<T>, dim3(wgs, d.n_kv_heads), dim3(256), lds, s, (const T *)k,
-                     (const T *)v, start_pos, (const T *)A, (const T *)P, (const T *)E,
-                     (T *)c.z_pages, (T *)c.r_pages, (T *)c.k_pages, c.block_table, a);
+  hipLaunchKernelGGL((compress_kernel<T, C>), dim3(wgs, d.n_kv_heads), dim3(256), lds, s,
+                     (const T *)k, (const T *)v, start_pos, (const T *)A, (const T *)P,
+                     (const T *)E, (C *)c.z_pages, (C *)c.r_pages, (C *)c.k_pages, c.block_table,
+                     a);
   return hipGetLastError();
 }
 
@@ -603,15 +632,17 @@ hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s) {
   if ((int64_t)d.batch * n_tokens <= kAppendMaxRows && d.r_v <= kHeadDim && d.r_q <= kHeadDim)
     return launch_append(d, k, v, start_pos, n_tokens, A, P, E, c, s);
-  return d.dtype == BASISKV_BF16 ? compress_t<uint16_t>(d, k, v, start_pos, n_tokens, A, P, E, c, s)
-                                 : compress_t<float>(d, k, v, start_pos, n_tokens, A, P, E, c, s);
+  if (cache_fp8(d))
+    return compress_t<uint16_t, uint8_t>(d, k, v, start_pos, n_tokens, A, P, E, c, s);
+  return act_bf16(d) ? compress_t<uint16_t, uint16_t>(d, k, v, start_pos, n_tokens, A, P, E, c, s)
+                     : compress_t<float, float>(d, k, v, start_pos, n_tokens, A, P, E, c, s);
 }
 
 size_t compress_lds(const basiskv_dims &d) {
-  const int pad = d.dtype == BASISKV_BF16 ? 32 : 16;
+  const int pad = act_bf16(d) ? 32 : 16;
   const int rb_pad = (d.r_b + pad - 1) / pad * pad;
-  return d.dtype == BASISKV_BF16 ? compress_lds_bytes<uint16_t>(d, rb_pad)
-                                 : compress_lds_bytes<float>(d, rb_pad);
+  return act_bf16(d) ? compress_lds_bytes<uint16_t>(d, rb_pad)
+                     : compress_lds_bytes<float>(d, rb_pad);
 }
 
 }  // namespace bkv_host

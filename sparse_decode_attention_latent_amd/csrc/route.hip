@@ -167,12 +167,17 @@ struct ScoreVariant {
   BKV_SCORE(T, DT, 1, RB, RQ), BKV_SCORE(T, DT, 2, RB, RQ), BKV_SCORE(T, DT, 4, RB, RQ), \
       BKV_SCORE(T, DT, 8, RB, RQ)
 
+// (the kernel's element type is the cache's: E4M3 codes for BASISKV_BF16_FP8_E4M3)
 static const ScoreVariant kScoreVariants[] = {
     BKV_SCORE_G(uint16_t, BASISKV_BF16, 64, 32), BKV_SCORE_G(uint16_t, BASISKV_BF16, 96, 48),
     BKV_SCORE_G(uint16_t, BASISKV_BF16, 16, 16), BKV_SCORE_G(uint16_t, BASISKV_BF16, 32, 32),
     BKV_SCORE_G(uint16_t, BASISKV_BF16, 32, 16),
     BKV_SCORE_G(uint16_t, BASISKV_BF16, 128, 32), BKV_SCORE_G(float, BASISKV_F32, 64, 32),
     BKV_SCORE_G(float, BASISKV_F32, 16, 16), BKV_SCORE_G(float, BASISKV_F32, 32, 16),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 64, 32),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 96, 48),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 16, 16),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 32, 16),
 };
 
 }  // namespace bkv
@@ -182,8 +187,8 @@ using namespace bkv;
 
 hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                           float *q_proj, hipStream_t s) {
-  return d.dtype == BASISKV_BF16 ? project_t<uint16_t>(d, q, P, Q, q_proj, s)
-                                 : project_t<float>(d, q, P, Q, q_proj, s);
+  return act_bf16(d) ? project_t<uint16_t>(d, q, P, Q, q_proj, s)
+                     : project_t<float>(d, q, P, Q, q_proj, s);
 }
 
 static int ilog2(int x) {
@@ -209,7 +214,7 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
     return hipSuccess;
   }
   *unsupported = false;
-  const int ce = d.dtype == BASISKV_BF16 ? 8 : 4;
+  const int ce = cache_chunk(d);
   ScoreArgs a;
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;

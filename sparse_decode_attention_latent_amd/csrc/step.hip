@@ -11,16 +11,16 @@ struct PrologueArgs {
   int n_append, proj_x, n_q, n_kv, rb, rq;
 };
 
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(256) void step_prologue_kernel(
     const T *__restrict__ k_new, const T *__restrict__ v_new, const int32_t *__restrict__ start_pos,
     const T *__restrict__ A, const T *__restrict__ P, const T *__restrict__ E,
-    const T *__restrict__ Q, const T *__restrict__ q, T *__restrict__ zpool,
-    T *__restrict__ rpool, T *__restrict__ kpool, const int32_t *__restrict__ block_table,
+    const T *__restrict__ Q, const T *__restrict__ q, C *__restrict__ zpool,
+    C *__restrict__ rpool, C *__restrict__ kpool, const int32_t *__restrict__ block_table,
     float *__restrict__ q_proj, PrologueArgs a) {
   const int idx = blockIdx.x;
   if (idx < a.n_append) {
-    append_body<T>(k_new, v_new, start_pos, A, P, E, zpool, rpool, kpool, block_table, a.ap,
+    append_body<T, C>(k_new, v_new, start_pos, A, P, E, zpool, rpool, kpool, block_table, a.ap,
                    idx % a.n_kv, idx / a.n_kv);
   } else {
     const int j = idx - a.n_append;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(
 namespace bkv_host {
 using namespace bkv;
 
-template <typename T>
+template <typename T, typename C>
 static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k_new,
                              const void *v_new, const int32_t *start_pos, const void *A,
                              const void *P, const void *Q, const void *E, const basiskv_cache &c,
@@ -58,10 +58,10 @@ static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k
   a.rb = d.r_b;
   a.rq = d.r_q;
   const int grid = a.n_append + a.proj_x * d.n_kv_heads * d.batch;
-  hipLaunchKernelGGL(step_prologue_kernel<T>, dim3(grid), dim3(256), 0, s, (const T *)k_new,
-                     (const T *)v_new, start_pos, (const T *)A, (const T *)P, (const T *)E,
-                     (const T *)Q, (const T *)q, (T *)c.z_pages, (T *)c.r_pages, (T *)c.k_pages,
-                     c.block_table, q_proj, a);
+  hipLaunchKernelGGL((step_prologue_kernel<T, C>), dim3(grid), dim3(256), 0, s,
+                     (const T *)k_new, (const T *)v_new, start_pos, (const T *)A, (const T *)P,
+                     (const T *)E, (const T *)Q, (const T *)q, (C *)c.z_pages, (C *)c.r_pages,
+                     (C *)c.k_pages, c.block_table, q_proj, a);
   return hipGetLastError();
 }
 
@@ -69,9 +69,11 @@ hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void
                                 const void *v_new, const int32_t *start_pos, const void *A,
                                 const void *P, const void *Q, const void *E,
                                 const basiskv_cache &c, float *q_proj, hipStream_t s) {
-  return d.dtype == BASISKV_BF16
-             ? prologue_t<uint16_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s)
-             : prologue_t<float>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s);
+  if (cache_fp8(d))
+    return prologue_t<uint16_t, uint8_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s);
+  return act_bf16(d)
+             ? prologue_t<uint16_t, uint16_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s)
+             : prologue_t<float, float>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s);
 }
 
 }  // namespace bkv_host

@@ -19,11 +19,31 @@ from . import api, layout, synth
 
 
 def to_device(arr, storage, device="cuda"):
-    """Stored numpy array (float32, or uint16 bf16 bits) -> device tensor."""
+    """Stored numpy array (float32, uint16 bf16 bits or uint8 E4M3 codes) ->
+    device tensor (E4M3 codes stay uint8: the library reads raw bytes)."""
     a = np.ascontiguousarray(arr)
     if storage == "bf16":
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(a).to(device)
+
+
+def dims_dtype(storage, cache_storage):
+    """The library's dims.dtype for activation and cache formats."""
+    if cache_storage == "fp8":
+        assert storage == "bf16", "E4M3 pages go with bf16 activations"
+        return api.BF16_FP8
+    assert cache_storage == storage
+    return api.BF16 if storage == "bf16" else api.F32
+
+
+def random_pool(shape, storage, gen, device):
+    """Seeded N(0, 1) draws on the device in a storage format (timing-only
+    state); E4M3 codes via torch's float8_e4m3fn cast."""
+    if storage == "fp8":
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+    tdt = torch.bfloat16 if storage == "bf16" else torch.float32
+    return torch.randn(shape, generator=gen, device=device, dtype=tdt)
 
 
 def to_host_storage(t, storage):
@@ -50,6 +70,7 @@ class DecodeProblem:
         self.wl = wl
         self.storage = inp["storage"]
         st = self.storage
+        self.cache_storage = cst = inp.get("cache_storage") or wl.cache
         if device_random is None:
             q = inp["q"]
             B, Hq, dh = q.shape
@@ -68,8 +89,7 @@ class DecodeProblem:
                                   hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                   page_size=S, max_pages_per_seq=self.max_pages,
                                   num_phys_pages=self.num_phys,
-                                  dtype=api.BF16 if st == "bf16" else api.F32,
-                                  recent_tokens=recent_tokens)
+                                  dtype=dims_dtype(st, cst), recent_tokens=recent_tokens)
         self.recent_tokens = int(recent_tokens)
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         dev = device
@@ -78,7 +98,7 @@ class DecodeProblem:
         if device_random is None:
             self.seq_lens_host = np.asarray(inp["seq_lens"], dtype=np.int32)
             pack = lambda a: to_device(layout.pack_pages(a, self.block_table_host, S, self.num_phys),
-                                       st, dev)
+                                       cst, dev)
             self.z_pages, self.r_pages, self.k_pages = pack(inp["z"]), pack(inp["r"]), pack(inp["kc"])
             self.q = to_device(q, st, dev)
             # appended token of the step: [B, 1, Hkv, dh], written at seq_len - 1
@@ -86,12 +106,11 @@ class DecodeProblem:
             self.v_new = to_device(inp["v_new"][:, None], st, dev)
         else:
             self.seq_lens_host = np.full(B, T, dtype=np.int32)
-            tdt = torch.bfloat16 if st == "bf16" else torch.float32
-            ce = 8 if st == "bf16" else 4
+            ce = {"fp8": 16, "bf16": 8}.get(cst, 4)
             gen = torch.Generator(device=dev)
             gen.manual_seed(seed)
-            rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=tdt)
-            pool = lambda w: rnd(Hkv, self.num_phys, w // ce, S, ce)
+            rnd = lambda *shape: random_pool(shape, st, gen, dev)
+            pool = lambda w: random_pool((Hkv, self.num_phys, w // ce, S, ce), cst, gen, dev)
             self.z_pages, self.r_pages, self.k_pages = pool(wl.r_v), pool(wl.r_q), pool(dh)
             self.q = rnd(B, Hq, dh)
             self.k_new, self.v_new = rnd(B, 1, Hkv, dh), rnd(B, 1, Hkv, dh)
@@ -173,14 +192,17 @@ class DecodeProblem:
                     y=to_host_storage(self.y, self.storage))
 
     def token_codes(self, b, pos):
-        """Stored latent and residual codes of token ``pos`` of sequence b, read
-        back from the pools: (z [Hkv, rV], r [Hkv, rq]) in stored form."""
+        """Stored latent, residual and Key of token ``pos`` of sequence b, read
+        back from the pools: (z [Hkv, rV], r [Hkv, rq], k [Hkv, dh]) in the
+        cache's stored form."""
         S = self.wl.page_size
         phys = int(self.block_table_host[b, pos // S])
         slot = pos % S
-        z = self.z_pages[:, phys, :, slot, :].reshape(self.z_pages.shape[0], -1)
-        r = self.r_pages[:, phys, :, slot, :].reshape(self.r_pages.shape[0], -1)
-        return to_host_storage(z.contiguous(), self.storage), to_host_storage(r.contiguous(), self.storage)
+        rows = []
+        for pool in (self.z_pages, self.r_pages, self.k_pages):
+            t = pool[:, phys, :, slot, :].reshape(pool.shape[0], -1).contiguous()
+            rows.append(to_host_storage(t, self.cache_storage))
+        return tuple(rows)
 
 
 class DenseProblem:
@@ -195,7 +217,7 @@ class DenseProblem:
     """
 
     def __init__(self, prob, v=None, seed=0):
-        wl, st = prob.wl, prob.storage
+        wl, st, cst = prob.wl, prob.storage, prob.cache_storage
         d = prob.dims
         self.prob = prob
         self.dims = api.make_dims(batch=d.batch, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
@@ -204,16 +226,15 @@ class DenseProblem:
                                   max_pages_per_seq=d.max_pages_per_seq,
                                   num_phys_pages=d.num_phys_pages, dtype=d.dtype)
         dev = prob.q.device
-        if v is not None:
+        if v is not None:  # stored in the cache format, as the Key pool
             self.v_pages = to_device(layout.pack_pages(v, prob.block_table_host, wl.page_size,
-                                                       prob.num_phys), st, dev)
+                                                       prob.num_phys), cst, dev)
         else:
             g = torch.Generator(device=dev)
             g.manual_seed(seed)
-            self.v_pages = torch.randn(prob.k_pages.shape, generator=g, device=dev,
-                                       dtype=prob.k_pages.dtype)
+            self.v_pages = random_pool(tuple(prob.k_pages.shape), cst, g, dev)
         dh, hq, hkv = d.head_dim, d.n_q_heads, d.n_kv_heads
-        eye = torch.eye(dh, dtype=prob.k_pages.dtype, device=dev).expand(hkv, dh, dh).contiguous()
+        eye = torch.eye(dh, dtype=prob.M.dtype, device=dev).expand(hkv, dh, dh).contiguous()
         self.M = torch.empty((wl.hidden, hq * dh), dtype=prob.M.dtype, device=dev)
         api.fuse_output_matrix(self.dims, eye, prob.fac["W_O"], self.M)
         self.workspace = torch.zeros(max(api.dense_workspace_bytes(self.dims), 256),
@@ -243,8 +264,10 @@ class PrefillProblem:
     shuffled) block table.
     """
 
-    def __init__(self, wl, k, v, fac, *, storage, shuffle_seed=54321, device="cuda"):
+    def __init__(self, wl, k, v, fac, *, storage, cache_storage=None, shuffle_seed=54321,
+                 device="cuda"):
         self.wl, self.storage = wl, storage
+        self.cache_storage = cst = cache_storage or storage
         B, T, Hkv, dh = k.shape
         S = wl.page_size
         self.T = T
@@ -254,7 +277,7 @@ class PrefillProblem:
                                   hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                   page_size=S, max_pages_per_seq=self.max_pages,
                                   num_phys_pages=self.num_phys,
-                                  dtype=api.BF16 if storage == "bf16" else api.F32)
+                                  dtype=dims_dtype(storage, cst))
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         self.block_table = torch.from_numpy(self.block_table_host).to(device)
         self.seq_lens = torch.full((B,), T, dtype=torch.int32, device=device)
@@ -262,8 +285,8 @@ class PrefillProblem:
         self.k = to_device(k, storage, device)
         self.v = to_device(v, storage, device)
         self.fac = {n: to_device(fac[n], storage, device) for n in ("A", "P", "E")}
-        tdt = torch.bfloat16 if storage == "bf16" else torch.float32
-        ce = 8 if storage == "bf16" else 4
+        tdt = {"fp8": torch.uint8, "bf16": torch.bfloat16}.get(cst, torch.float32)
+        ce = {"fp8": 16, "bf16": 8}.get(cst, 4)
 
         def pool(w):
             return torch.zeros((Hkv, self.num_phys, w // ce, S, ce), dtype=tdt, device=device)
@@ -281,6 +304,6 @@ class PrefillProblem:
         torch.cuda.synchronize()
         out = {}
         for name, t in (("z", self.z_pages), ("r", self.r_pages), ("k", self.k_pages)):
-            out[name] = layout.unpack_pages(to_host_storage(t, self.storage), self.block_table_host,
-                                            self.wl.page_size, self.T)
+            out[name] = layout.unpack_pages(to_host_storage(t, self.cache_storage),
+                                            self.block_table_host, self.wl.page_size, self.T)
         return out

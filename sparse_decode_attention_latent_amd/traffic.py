@@ -26,8 +26,13 @@ class StepShape:
     page_size: int
     max_pages: int
     top_k: int
-    elem: int  # bytes per stored element: 2 (bf16) or 4 (float32)
+    elem: int  # bytes per stored activation element: 2 (bf16) or 4 (float32)
     recent_tokens: int = 0  # recent window: its pages are attended besides the routed ones
+    cache_elem: int = 0  # bytes per cached element (1 for E4M3 pages); 0: same as elem
+
+    @property
+    def ce(self):
+        return self.cache_elem or self.elem
 
 
 def _pages(seq_len, page_size):
@@ -39,7 +44,7 @@ def append_bytes(s: StepShape):
     factors; write one z, r and Key row per (sequence, KV head)."""
     e = s.elem
     fac = s.n_kv_heads * s.head_dim * (s.r_v + s.r_b + s.r_q) * e
-    io = s.batch * s.n_kv_heads * (2 * s.head_dim + s.r_v + s.r_q + s.head_dim) * e
+    io = s.batch * s.n_kv_heads * (2 * s.head_dim * e + (s.r_v + s.r_q + s.head_dim) * s.ce)
     return fac + io
 
 
@@ -55,7 +60,7 @@ def score_bytes(s: StepShape, seq_lens):
     plus projected queries, block-table entries and the page scores."""
     tok = sum(max(0, int(L)) for L in seq_lens)
     pages = sum(_pages(L, s.page_size) for L in seq_lens)
-    stream = tok * s.n_kv_heads * (s.r_b + s.r_q) * s.elem
+    stream = tok * s.n_kv_heads * (s.r_b + s.r_q) * s.ce
     small = (s.batch * s.n_q_heads * (s.r_b + s.r_q) * 4 + pages * 4
              + s.batch * s.n_kv_heads * s.max_pages * 4)
     return stream + small
@@ -64,7 +69,7 @@ def score_bytes(s: StepShape, seq_lens):
 def score_stream_bytes(s: StepShape, seq_lens):
     """The per-token latent + residual stream alone (Table 4 routing widths)."""
     tok = sum(max(0, int(L)) for L in seq_lens)
-    return tok * s.n_kv_heads * (s.r_b + s.r_q) * s.elem
+    return tok * s.n_kv_heads * (s.r_b + s.r_q) * s.ce
 
 
 def select_bytes(s: StepShape, seq_lens):
@@ -90,7 +95,7 @@ def attend_bytes(s: StepShape, seq_lens):
             toks = L
         else:
             toks = s.top_k * s.page_size
-        total += toks * s.n_kv_heads * (s.head_dim + s.r_v) * e
+        total += toks * s.n_kv_heads * (s.head_dim + s.r_v) * s.ce
     total += s.batch * s.n_q_heads * s.head_dim * e          # queries
     total += s.batch * s.n_kv_heads * s.top_k * 4            # selection
     total += s.batch * s.n_q_heads * s.r_v * 4               # u
@@ -115,10 +120,11 @@ def step_bytes(s: StepShape, seq_lens, append=True):
     return parts
 
 
-def prefill_bytes(batch, tokens, n_kv_heads, head_dim, r_v, r_b, r_q, elem):
+def prefill_bytes(batch, tokens, n_kv_heads, head_dim, r_v, r_b, r_q, elem, cache_elem=0):
     """compress_prefill of ``tokens`` tokens per sequence: read K and V and
     the three factors once; write one latent, residual and Key row per
-    (token, KV head)."""
+    (token, KV head) (cache_elem bytes each; 0: elem)."""
     rows = batch * tokens * n_kv_heads
     fac = n_kv_heads * head_dim * (r_v + r_b + r_q) * elem
-    return rows * (2 * head_dim) * elem + fac + rows * (r_v + r_q + head_dim) * elem
+    return (rows * (2 * head_dim) * elem + fac
+            + rows * (r_v + r_q + head_dim) * (cache_elem or elem))

@@ -31,6 +31,19 @@ Tolerances (stated once, used by every GPU test):
                legitimately flip).  The residual code has no unit bound: it
                is computed from the stored latent, and a legitimate one-unit
                difference there moves r by about |P| |E| units of z.
+  E4M3 pages   (BASISKV_BF16_FP8_E4M3: z, r and Key pages as E4M3 codes) every
+               stored code of the appended token is a valid rounding: the
+               nearest-even E4M3 value of the exact (float64) latent, or the
+               other neighbour when the exact value lies within
+               E4M3_TIE_RTOL of the row's largest magnitude of a rounding
+               boundary (float32 accumulation may land on either side; 1e-4
+               is far above that error, ~1e-6 for these 128-term sums); the
+               residual the same way, its exact value formed from the
+               library's own stored latent; the Key code bit-exact (one
+               rounding of a bf16 input).  When a valid code differs from
+               the oracle's, the oracle continues from the library's codes
+               (several roundings are correct).  Scores, selection and u keep
+               the bars above: every page is decoded exactly on both sides.
 """
 
 import math
@@ -44,6 +57,7 @@ BAND = 1e-3
 U_RTOL = 1e-4
 Y_RTOL = {"f32": 1e-4, "bf16": 2e-2}
 CODE_RTOL = {"f32": 1e-5, "bf16": 2e-2}
+E4M3_TIE_RTOL = 1e-4
 
 
 def f64(a, storage):
@@ -51,16 +65,19 @@ def f64(a, storage):
 
 
 def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_pages_out=None,
-                    scale=None, recent_tokens=0):
+                    scale=None, recent_tokens=0, codes_override=None):
     """The oracle's decode step for sequence b of a workload's stored inputs.
 
     Returns scores [Hkv, NPout], sel [Hkv, k], u [Hq, rV], y [D], y_stored,
-    and the appended token's stored codes (z_new, r_new: [Hkv, w]).
-    sel_override [Hkv, k] replaces the oracle's own selection for attention.
-    With a recent window the routed candidates are the pages before it
-    (n_candidates) and its pages are attended as well.
+    the appended token's stored codes (z_new, r_new: [Hkv, w]; k_new) and
+    its unrounded latent z_exact.  sel_override [Hkv, k] replaces the
+    oracle's own selection for attention; codes_override (z, r as float64)
+    replaces its appended latent and residual codes.  With a recent window
+    the routed candidates are the pages before it (n_candidates) and its
+    pages are attended as well.
     """
     st = inp["storage"]
+    cst = inp.get("cache_storage", st)
     G, hkv, S = wl.group, wl.n_kv_heads, wl.page_size
     T = inp["z"].shape[2]
     if n_pages_out is None:
@@ -75,20 +92,27 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
     u = np.zeros((wl.n_q_heads, wl.r_v))
     z_new = np.zeros((hkv, wl.r_v))
     r_new = np.zeros((hkv, wl.r_q))
+    z_exact = np.zeros((hkv, wl.r_v))
+    k_new = np.zeros((hkv, wl.head_dim))
     n_cand = ref.recent_window_first_page(L, S, recent_tokens)
     if L > 0:
         n_pages = -(-L // S)
         recent = np.arange(n_cand, n_pages, dtype=np.int64)
         if append:
-            zs, rs, _ = ref.compress_tokens(f64(inp["k_new"][b:b + 1], st), f64(inp["v_new"][b:b + 1], st),
-                                            fac["A"], fac["P"], fac["E"], wl.r_b, st)
-            z_new, r_new = zs[0], rs[0]
+            zs, rs, ks = ref.compress_tokens(f64(inp["k_new"][b:b + 1], st),
+                                             f64(inp["v_new"][b:b + 1], st),
+                                             fac["A"], fac["P"], fac["E"], wl.r_b, cst)
+            z_new, r_new, k_new = zs[0], rs[0], ks[0]
+            z_exact = np.stack([ref.latent_code(f64(inp["v_new"][b, g], st), fac["A"][g])
+                                for g in range(hkv)])
+            if codes_override is not None:
+                z_new, r_new = codes_override
         for g in range(hkv):
-            z = f64(inp["z"][b, g, :L], st)
-            r = f64(inp["r"][b, g, :L], st)
-            kc = f64(inp["kc"][b, g, :L], st)
+            z = f64(inp["z"][b, g, :L], cst)
+            r = f64(inp["r"][b, g, :L], cst)
+            kc = f64(inp["kc"][b, g, :L], cst)
             if append:
-                z[L - 1], r[L - 1], kc[L - 1] = z_new[g], r_new[g], f64(inp["k_new"][b, g], st)
+                z[L - 1], r[L - 1], kc[L - 1] = z_new[g], r_new[g], k_new[g]
             qg = q[g * G:(g + 1) * G]
             scores[g] = ref.route_page_scores(qg, z, r, fac["P"][g], fac["Q"][g], wl.r_b, L, S,
                                               n_pages_out)
@@ -98,8 +122,44 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
                                                     L, S, scale)
     y = ref.reconstruct(u, fac["Bf"], fac["W_O"], G) if L > 0 else np.zeros(wl.hidden)
     return dict(scores=scores, sel=sel, u=u, y=y, y_stored=ref.round_to_storage(y, st),
-                z_new=z_new, r_new=r_new, n_pages=(-(-L // S) if L > 0 else 0),
-                n_candidates=n_cand)
+                z_new=z_new, r_new=r_new, k_new=k_new, z_exact=z_exact,
+                n_pages=(-(-L // S) if L > 0 else 0), n_candidates=n_cand)
+
+
+def e4m3_valid(gpu_codes, exact):
+    """Mask of stored E4M3 codes that are valid roundings of the float64 values
+    ``exact`` (last axis = row): the nearest-even rounding of some value within
+    E4M3_TIE_RTOL * max|row| of the exact one.  Rounding is monotone and the
+    band is an interval, so those roundings are exactly the E4M3 values
+    between the roundings of the band's two ends."""
+    exact = np.asarray(exact, dtype=np.float64)
+    g = ref.storage_to_f64(gpu_codes, "fp8")
+    tol = E4M3_TIE_RTOL * np.abs(exact).max(axis=-1, keepdims=True)
+    lo = ref.round_to_storage(exact - tol, "fp8")
+    hi = ref.round_to_storage(exact + tol, "fp8")
+    return (g >= lo) & (g <= hi)
+
+
+def check_e4m3_token(wl, inp, b, want, gpu_z, gpu_r, gpu_k, where=""):
+    """Appended E4M3 codes of sequence b (rules in the module docstring).
+    Returns the library's latent and residual as float64 when they differ
+    from the oracle's (for codes_override), else None."""
+    st = inp["storage"]
+    fac = {k: f64(inp[k], st) for k in ("P", "E")}
+    ok_z = e4m3_valid(gpu_z, want["z_exact"])
+    assert ok_z.all(), f"{where}: appended latent codes not a valid rounding at {np.argwhere(~ok_z)[:4]}"
+    zg = f64(gpu_z, "fp8")
+    k = f64(inp["k_new"][b], st)
+    r_exact = np.concatenate([ref.residual_code(k[g][None], zg[g][None], fac["P"][g], fac["E"][g],
+                                                wl.r_b) for g in range(wl.n_kv_heads)])
+    ok_r = e4m3_valid(gpu_r, r_exact)
+    assert ok_r.all(), f"{where}: appended residual codes not a valid rounding at {np.argwhere(~ok_r)[:4]}"
+    np.testing.assert_array_equal(f64(gpu_k, "fp8"), want["k_new"],
+                                  err_msg=f"{where}: appended Key codes")
+    rg = f64(gpu_r, "fp8")
+    if np.array_equal(zg, want["z_new"]) and np.array_equal(rg, want["r_new"]):
+        return None
+    return zg, rg
 
 
 def check_scores(gpu, want, n_pages, where=""):

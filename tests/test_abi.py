@@ -45,7 +45,8 @@ def dims_of(wl, **over):
     kw = dict(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
               hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q, page_size=wl.page_size,
               max_pages_per_seq=wl.max_pages, num_phys_pages=wl.batch * wl.max_pages,
-              dtype=api.BF16 if wl.storage == "bf16" else api.F32)
+              dtype=(api.BF16_FP8 if wl.cache == "fp8" else
+                     api.BF16 if wl.storage == "bf16" else api.F32))
     kw.update(over)
     return api.make_dims(**kw)
 
@@ -86,6 +87,7 @@ def _cache(**kw):
     (dict(dtype=7), 3),
     (dict(max_pages_per_seq=40000), 3),
     (dict(recent_tokens=-1), 2),
+    (dict(dtype=2, r_q=40), 3),       # E4M3 rows: widths must fill 16-byte chunks (16 codes)
 ])
 def test_dims_validation(over, code):
     lib = api.lib()
@@ -132,6 +134,20 @@ def test_null_and_shape_and_workspace_errors():
     assert step(dims_of(WORKLOADS[2], batch=40)) == 3
     big = dims_of(WORKLOADS[2], batch=40)
     assert lib.basiskv_reconstruct(ctypes.byref(big), FAKE, FAKE, FAKE, None) == 3
+
+
+@needs_lib
+def test_fp8_cache_dims():
+    """BASISKV_BF16_FP8_E4M3 (bf16 activations, E4M3 pages) is a valid dtype
+    for the FP8 workloads; the workspace does not depend on the page format
+    (it holds float32 partials and bf16 operand tiles)."""
+    from sparse_decode_attention_latent_amd.configs import workload
+    for name in ("llama8b-ctx32k-fp8", "llama8b-ctx32k-b16r16-page4-fp8"):
+        wl = workload(name)
+        d = dims_of(wl)
+        assert d.dtype == api.BF16_FP8
+        assert api.workspace_bytes(d, wl.top_k) == api.workspace_bytes(
+            dims_of(wl, dtype=api.BF16), wl.top_k) > 0
 
 
 @needs_lib

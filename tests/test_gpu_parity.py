@@ -33,10 +33,24 @@ def _say(msg):
 def compare_step(wl, inp, prob, out, seqs):
     """Check scores, selection, u, y and the appended codes for sequences seqs."""
     st = inp["storage"]
+    cst = inp.get("cache_storage", st)
     rw = prob.recent_tokens
     for b in seqs:
-        want = parity.oracle_sequence(wl, inp, b, top_k=prob.top_k, n_pages_out=prob.max_pages,
-                                      recent_tokens=rw)
+        kw = dict(top_k=prob.top_k, n_pages_out=prob.max_pages, recent_tokens=rw)
+        want = parity.oracle_sequence(wl, inp, b, **kw)
+        L = int(inp["seq_lens"][b])
+        codes = None
+        if L > 0:  # the appended token's stored codes first: the rest is computed from them
+            zg, rg, kg = prob.token_codes(b, L - 1)
+            if cst == "fp8":
+                codes = parity.check_e4m3_token(wl, inp, b, want, zg, rg, kg, f"{wl.name} b={b}")
+                if codes is not None:  # another valid rounding: continue from the library's
+                    want = parity.oracle_sequence(wl, inp, b, codes_override=codes, **kw)
+            else:
+                for name, gv, wv in (("z", zg, want["z_new"]), ("r", rg, want["r_new"])):
+                    e = parity.rel_rows(ref.storage_to_f64(gv, cst), wv)
+                    assert e.max() <= parity.CODE_RTOL[cst], \
+                        f"{wl.name} b={b}: appended {name} err {e.max():.3g}"
         n_pages = want["n_candidates"]  # routed among the pages before any recent window
         for g in range(wl.n_kv_heads):
             where = f"{wl.name} b={b} g={g}"
@@ -45,19 +59,14 @@ def compare_step(wl, inp, prob, out, seqs):
                                    prob.top_k, where)
         same_sel = np.array_equal(out["sel"][b], want["sel"])
         if not same_sel:  # several selections are correct: attend over the library's own
-            want = parity.oracle_sequence(wl, inp, b, top_k=prob.top_k, n_pages_out=prob.max_pages,
-                                          sel_override=out["sel"][b], recent_tokens=rw)
+            want = parity.oracle_sequence(wl, inp, b, sel_override=out["sel"][b],
+                                          codes_override=codes, **kw)
         eu = parity.rel_rows(out["u"][b], want["u"])
         assert eu.max() <= parity.U_RTOL, f"{wl.name} b={b}: u rel err {eu.max():.3g} head {eu.argmax()}"
         ey = parity.rel_rows(ref.storage_to_f64(out["y"][b], st), want["y"])
         assert ey <= parity.Y_RTOL[st], f"{wl.name} b={b}: y rel err {float(ey):.3g}"
-        L = int(inp["seq_lens"][b])
-        if L > 0:
-            zg, rg = prob.token_codes(b, L - 1)
-            for name, gv, wv in (("z", zg, want["z_new"]), ("r", rg, want["r_new"])):
-                e = parity.rel_rows(ref.storage_to_f64(gv, st), wv)
-                assert e.max() <= parity.CODE_RTOL[st], f"{wl.name} b={b}: appended {name} err {e.max():.3g}"
-        _say(f"  {wl.name} b={b} L={L} ok (sel {'=' if same_sel else 'band'}; u {eu.max():.2e}; y {float(ey):.2e})")
+        _say(f"  {wl.name} b={b} L={L} ok (sel {'=' if same_sel else 'band'}; u {eu.max():.2e}; "
+             f"y {float(ey):.2e}{'; codes: library rounding' if codes is not None else ''})")
 
 
 def run_case(wl, *, batch=None, ctx=None, seq_lens=None, seqs=None, top_k=None, shuffle_seed=12345,
@@ -366,6 +375,130 @@ def test_all_scores_tied_selects_lowest_pages(wl_index, ctx):
         for g in range(wl.n_kv_heads):
             np.testing.assert_array_equal(out["sel"][b, g], np.arange(24))
     compare_step(wl, inp, prob, out, range(2))
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 cache pages (appendix Table 13: BasisKV under an E4M3 KV cache);
+# bf16 queries, factors, inputs and output; rules in tests/parity.py
+# ---------------------------------------------------------------------------
+
+FP8 = "llama8b-ctx32k-fp8"
+FP8_ADOPTED = "llama8b-ctx32k-b16r16-page4-fp8"
+
+
+def test_fp8_headline_full_sampled():
+    run_case(workload(FP8), seqs=(0, 4, 7))
+
+
+def test_fp8_adopted_router_full_sampled():
+    run_case(workload(FP8_ADOPTED), seqs=(0, 5))
+
+
+def test_fp8_ragged_lengths():
+    run_case(workload(FP8), batch=6, ctx=1000, seq_lens=[1000, 999, 33, 1, 0, 517], top_k=16)
+
+
+def test_fp8_adopted_router_ragged():
+    run_case(workload(FP8_ADOPTED), batch=4, ctx=8192, seq_lens=[8192, 8191, 2100, 63])
+
+
+@pytest.mark.parametrize("wl_index", [1, 3])
+def test_fp8_other_shapes(wl_index):
+    """Latent 96 / residual 48, groups of 4 and of 8 (the 8-head group runs as
+    two 4-head subgroups), E4M3 pages."""
+    wl = workload(wl_index).with_(cache_storage="fp8")
+    run_case(wl, batch=3, ctx=4096, seq_lens=[4096, 2500, 77], top_k=16)
+
+
+def test_fp8_combined_calls_equal_the_separate_calls():
+    wl = workload(FP8)
+    inp = synth.decode_inputs(wl, batch=3, ctx=8192, seq_lens=[8192, 5000, 40])
+    prob = DecodeProblem(wl, inp, top_k=32)
+    prob.step_unfused(append=True)
+    base = prob.outputs()
+    prob.u.fill_(float("nan"))
+    prob.decode_step()
+    got = prob.outputs()
+    for key in ("scores", "sel", "u", "y"):
+        np.testing.assert_array_equal(got[key], base[key], err_msg=key)
+    compare_step(wl, inp, prob, got, range(3))
+
+
+def test_fp8_append_saturates():
+    """A new token whose Key and Value are far beyond the E4M3 range: the
+    stored codes saturate at +-448 (no NaN code), as the oracle's rounding."""
+    wl = workload(FP8)
+    inp = synth.decode_inputs(wl, batch=2, ctx=2048, seq_lens=[2048, 999])
+    st = inp["storage"]
+    for key in ("k_new", "v_new"):
+        inp[key] = synth.to_storage(synth.from_storage(inp[key], st) * 2000.0, st)
+    prob = DecodeProblem(wl, inp, top_k=16)
+    prob.step(append=True)
+    out = prob.outputs()
+    for b, L in enumerate((2048, 999)):
+        z, r, k = prob.token_codes(b, L - 1)
+        assert not np.any((k & 0x7F) == 0x7F) and not np.any((z & 0x7F) == 0x7F)
+        assert np.any(k == 0x7E) or np.any(k == 0xFE)
+    compare_step(wl, inp, prob, out, range(2))
+
+
+def test_fp8_compress_prefill():
+    """(a0) compression of ragged prompts into E4M3 pages on the MFMA path:
+    every Key code bit-exact, every latent and residual code a valid rounding
+    (tests/parity.py), on every token."""
+    wl = workload(4).with_(cache_storage="fp8")
+    B, T = 3, 1000
+    k, v = synth.kv_activations(wl, batch=B, tokens=T, stream=0)
+    fac = synth.factors(wl)
+    prob = PrefillProblem(wl, k, v, fac, storage="bf16", cache_storage="fp8")
+    prob.run()
+    got = prob.logical()
+    A, P, E = (ref.storage_to_f64(fac[n], "bf16") for n in ("A", "P", "E"))
+    flips = 0
+    for b in range(B):
+        kb, vb = ref.storage_to_f64(k[b], "bf16"), ref.storage_to_f64(v[b], "bf16")  # [T, Hkv, dh]
+        zs, rs, ks = ref.compress_tokens(kb, vb, A, P, E, wl.r_b, "fp8")
+        zg = got["z"][b].transpose(1, 0, 2)  # codes [T, Hkv, w]
+        rg = got["r"][b].transpose(1, 0, 2)
+        kg = got["k"][b].transpose(1, 0, 2)
+        np.testing.assert_array_equal(ref.storage_to_f64(kg, "fp8"), ks)
+        for g in range(wl.n_kv_heads):
+            z_exact = ref.latent_code(vb[:, g], A[g])
+            assert parity.e4m3_valid(zg[:, g], z_exact).all(), f"b={b} g={g}: latent codes"
+            zgv = ref.storage_to_f64(zg[:, g], "fp8")
+            r_exact = ref.residual_code(kb[:, g], zgv, P[g], E[g], wl.r_b)
+            assert parity.e4m3_valid(rg[:, g], r_exact).all(), f"b={b} g={g}: residual codes"
+        flips += int((ref.storage_to_f64(zg, "fp8") != zs).sum())
+    _say(f"  fp8 compress: latent codes differing from the oracle's rounding: {flips}")
+
+
+@pytest.mark.parametrize("seq_lens", [[4096, 1000, 0, 33]])
+def test_fp8_dense_attend_matches_oracle(seq_lens):
+    """The dense baseline over E4M3 Key and Value pages (Table 13's Full-K
+    FP8 row's data format)."""
+    wl = workload(FP8)
+    B = len(seq_lens)
+    inp = synth.decode_inputs(wl, batch=B, ctx=4096, seq_lens=seq_lens)
+    rng = np.random.default_rng(37)
+    v = synth.to_storage(rng.standard_normal(inp["kc"].shape), "fp8")
+    prob = DecodeProblem(wl, inp)
+    dense = DenseProblem(prob, v=v)
+    dense.step()
+    torch.cuda.synchronize()
+    o = dense.o.double().cpu().numpy()
+    y = ref.storage_to_f64(dense.y.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    q = ref.storage_to_f64(inp["q"], "bf16")
+    kc, vv = ref.storage_to_f64(inp["kc"], "fp8"), ref.storage_to_f64(v, "fp8")
+    W_O = ref.storage_to_f64(inp["W_O"], "bf16")
+    G, scale = wl.group, 1 / math.sqrt(wl.head_dim)
+    for b, L in enumerate(seq_lens):
+        want = np.concatenate([ref.dense_attention(q[b, g * G:(g + 1) * G], kc[b, g], vv[b, g], L, scale)
+                               for g in range(wl.n_kv_heads)])
+        eo = parity.rel_rows(o[b], want)
+        assert eo.max() <= parity.U_RTOL, f"b={b}: o rel err {eo.max():.3g}"
+        ey = parity.rel_rows(y[b], want.reshape(-1) @ W_O)
+        assert ey <= parity.Y_RTOL["bf16"], f"b={b}: y rel err {float(ey):.3g}"
+        _say(f"  dense fp8 b={b} L={L}: o {eo.max():.2e} y {float(ey):.2e}")
 
 
 def untile_output_matrix(flat, hidden, K, itemsize):
