@@ -38,9 +38,19 @@ if ROOT not in sys.path:
 
 METRIC = "decode µs/layer + achieved HBM GB/s vs peak, 8B-shaped GQA at 32K ctx, 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "route_scan_llama8b_ctx32k_pmc.json")
-ROUTE_SOURCES = ("sparse_decode_attention_latent_amd/csrc/route.hip",
-                 "sparse_decode_attention_latent_amd/csrc/common.hpp")
+# sources the route_scan and attend_split kernels are compiled from: counter
+# figures taken with other sources are not reported
+KERNEL_SOURCES = ("sparse_decode_attention_latent_amd/csrc/route.hip",
+                  "sparse_decode_attention_latent_amd/csrc/attend.hip",
+                  "sparse_decode_attention_latent_amd/csrc/common.hpp",
+                  "sparse_decode_attention_latent_amd/csrc/topk.hpp",
+                  "sparse_decode_attention_latent_amd/csrc/decode_bodies.hpp",
+                  "include/basiskv.h")
+PMC_KERNELS = ("route_scan_kernel", "attend_split_kernel")
+
+
+def pmc_summary_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"hbm_counters_{workload_name.replace('-', '_')}.json")
 
 
 def log(msg):
@@ -68,7 +78,8 @@ def parse():
                          "five times, the reference for HBM counter scaling")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
-                         "WRITE_SIZE; --calibration-copy) into " + PMC_SUMMARY)
+                         "WRITE_SIZE; --calibration-copy) into "
+                         "profiles/hbm_counters_<workload>.json")
     return ap.parse_args()
 
 
@@ -86,8 +97,9 @@ def calibration_copy():
 
 
 def pmc_summary(fetch_dir, write_dir, workload_name):
-    """Per-dispatch HBM bytes of route_scan_kernel from two counter runs,
-    scaled by what the same counters read for the calibration kernel."""
+    """Per-dispatch HBM bytes of route_scan_kernel and attend_split_kernel from
+    two counter runs, scaled by what the same counters read for the
+    calibration kernel; written to profiles/hbm_counters_<workload>.json."""
     import csv
     import glob
 
@@ -95,64 +107,69 @@ def pmc_summary(fetch_dir, write_dir, workload_name):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         if not files:
             sys.exit(f"no counter_collection.csv under {d}")
-        vals = {"route": [], "calib": []}
+        vals = {k: [] for k in PMC_KERNELS + ("calib",)}
         for f in files:
             for row in csv.DictReader(open(f)):
                 name = row["Kernel_Name"]
-                if "route_scan_kernel" in name:
-                    vals["route"].append(float(row["Counter_Value"]))
-                elif "neg_kernel" in name:
+                for k in PMC_KERNELS:
+                    if k in name:
+                        vals[k].append(float(row["Counter_Value"]))
+                if "neg_kernel" in name:
                     vals["calib"].append(float(row["Counter_Value"]))
-        if not vals["route"] or not vals["calib"]:
-            sys.exit(f"{d}: route_scan_kernel or calibration dispatches missing")
+        if any(not v for v in vals.values()):
+            sys.exit(f"{d}: a kernel or the calibration dispatches are missing")
         return {k: sum(v) / len(v) for k, v in vals.items()}
 
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     ref_kib = CALIB_BYTES / 1024
     fetch_scale = ref_kib / fetch["calib"]
     write_scale = ref_kib / write["calib"]
-    hbm = (fetch["route"] * fetch_scale + write["route"] * write_scale) * 1024
-    out = {"workload": workload_name, "kernel": "route_scan_kernel",
-           "source_sha256": route_source_sha(),
-           "fetch_size_kib_per_dispatch": round(fetch["route"], 1),
-           "write_size_kib_per_dispatch": round(write["route"], 1),
+    kernels = {}
+    for k in PMC_KERNELS:
+        kernels[k] = {"fetch_size_kib_per_dispatch": round(fetch[k], 1),
+                      "write_size_kib_per_dispatch": round(write[k], 1),
+                      "hbm_bytes_per_launch": round((fetch[k] * fetch_scale
+                                                     + write[k] * write_scale) * 1024)}
+    out = {"workload": workload_name, "source_sha256": kernel_source_sha(),
+           "kernels": kernels,
            "calibration": {"kernel": "torch.neg over 64 MiB float32 (64 MiB read, 64 MiB written)",
                            "fetch_size_kib": round(fetch["calib"], 1),
                            "write_size_kib": round(write["calib"], 1),
                            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
-           "hbm_bytes_per_launch": round(hbm),
            "commands": [f"cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} --output-format csv -d "
                         f"$REPO/{os.path.relpath(d, ROOT)} -o run -- python3 $REPO/bench.py "
-                        f"--workload {workload_name} --steps 5 --warmup 2 --cpu-seconds 0 "
-                        f"--calibration-copy"
+                        f"--workload {workload_name} --steps 5 --warmup 2 --cold-steps 0 "
+                        f"--cpu-seconds 0 --calibration-copy"
                         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))],
            "summary_command": f"python3 bench.py --workload {workload_name} --pmc-summary "
                               f"{os.path.relpath(fetch_dir, ROOT)} {os.path.relpath(write_dir, ROOT)}"}
-    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
-    with open(PMC_SUMMARY, "w") as f:
+    path = pmc_summary_path(workload_name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def route_source_sha():
+def kernel_source_sha():
     h = hashlib.sha256()
-    for rel in ROUTE_SOURCES:
+    for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per route_scan launch from the committed rocprofv3 counter
-    summary, or None when there is none for this workload or the kernel's
-    source changed since the counters were taken."""
-    if not os.path.exists(PMC_SUMMARY):
+def measured_traffic(workload_name, kernel="route_scan_kernel"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, or None when there is none for this workload or the kernels'
+    sources changed since the counters were taken."""
+    path = pmc_summary_path(workload_name)
+    if not os.path.exists(path):
         return None
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         s = json.load(f)
-    if s.get("workload") != workload_name or s.get("source_sha256") != route_source_sha():
+    if s.get("workload") != workload_name or s.get("source_sha256") != kernel_source_sha():
         return None
-    return float(s["hbm_bytes_per_launch"])
+    return float(s["kernels"][kernel]["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(wl, inp, target_seconds):
@@ -468,6 +485,7 @@ def main():
     value = sb["total"] / (ms_per_step * 1e-3) / 1e9
     score_gbs = sb["score"] / (per_stage["score"] * 1e-6) / 1e9
     traffic_bytes = measured_traffic(wl.name)
+    attend_traffic = measured_traffic(wl.name, "attend_split_kernel")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -491,6 +509,7 @@ def main():
         "stages_us": {k: round(v, 3) for k, v in per_stage.items()},
         "stages_host_bound": [k for k in stages if host_bound[k]],
         "stages_gbs": {k: round(sb[k] / (per_stage[k] * 1e-6) / 1e9, 1) for k in stages},
+        "stages_hbm_bytes_measured": {"score": traffic_bytes, "attend": attend_traffic},
         "roofline": {"kernel": "route_scan_kernel (page scoring)", "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4),
