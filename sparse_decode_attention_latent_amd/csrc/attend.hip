@@ -87,8 +87,11 @@ typedef float attend_f4 __attribute__((ext_vector_type(4)));
 
 // T: query elements (float32 or bf16); C: cache elements (float32, bf16, or
 // E4M3 codes beside bf16 queries, whose Key chunks are widened to bf16 -- exact
-// -- for the same matrix instruction).
-template <typename T, typename C, int G, int NVC, int NB>
+// -- for the same matrix instruction).  STREAM: page gathers marked non-temporal
+// (used where every load instruction reads whole 128-byte lines and no other
+// workgroup reads the same pages: pages of 8 or more tokens, one query
+// subgroup per KV head).
+template <typename T, typename C, int G, int NVC, int NB, bool STREAM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<C, G, NVC>())))
 void attend_split_kernel(
     const T *__restrict__ q, const C *__restrict__ kpool, const C *__restrict__ zpool,
@@ -261,12 +264,12 @@ void attend_split_kernel(
     const int64_t ko = k_off(0);
 #pragma unroll
     for (int c = 0; c < NKC; ++c)
-      if (v0) kc[c] = load_chunk(kpool, ko + c * chunk_stride);
+      if (v0) kc[c] = load_page_chunk<STREAM>(kpool, ko + c * chunk_stride);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int64_t zo;
       zv[j] = z_src(0, v0, j, zo);
-      if (zv[j]) zc[j] = load_chunk(zpool, zo);
+      if (zv[j]) zc[j] = load_page_chunk<STREAM>(zpool, zo);
     }
   }
 #pragma unroll
@@ -281,7 +284,7 @@ void attend_split_kernel(
       const int64_t ko = k_off(i);
 #pragma unroll
       for (int c = 0; c < NKC; ++c)
-        if (valid) kc[c] = load_chunk(kpool, ko + c * chunk_stride);
+        if (valid) kc[c] = load_page_chunk<STREAM>(kpool, ko + c * chunk_stride);
     }
 
     // ---- exact scores, one token per lane ----
@@ -299,7 +302,7 @@ void attend_split_kernel(
         if constexpr (kFp8) {
           kb[0] = fp8x8_to_bf16x8(kc[c].x, kc[c].y);
           kb[SUB - 1] = fp8x8_to_bf16x8(kc[c].z, kc[c].w);
-          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
+          if (nxt && vn) kc[c] = load_page_chunk<STREAM>(kpool, ko_next + c * chunk_stride);  // registers free again
         } else {
           kb[0] = kc[c];
         }
@@ -317,7 +320,7 @@ void attend_split_kernel(
           }
         }
         if constexpr (!kFp8)
-          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);  // registers free again
+          if (nxt && vn) kc[c] = load_page_chunk<STREAM>(kpool, ko_next + c * chunk_stride);  // registers free again
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -343,7 +346,7 @@ void attend_split_kernel(
             dot[h] = dot2_bf16(kc[c].z, q4.z, dot[h]);
             dot[h] = dot2_bf16(kc[c].w, q4.w, dot[h]);
           }
-          if (nxt && vn) kc[c] = load_chunk(kpool, ko_next + c * chunk_stride);
+          if (nxt && vn) kc[c] = load_page_chunk<STREAM>(kpool, ko_next + c * chunk_stride);
         } else if (valid) {
           float x[CE];
           unpack_chunk<C>(kc[c], x);
@@ -368,7 +371,7 @@ void attend_split_kernel(
       for (int j = 0; j < NJ; ++j) {
         int64_t zo;
         zv[j] = z_src(i, valid, j, zo);
-        if (zv[j]) zc[j] = load_chunk(zpool, zo);
+        if (zv[j]) zc[j] = load_page_chunk<STREAM>(zpool, zo);
       }
     }
 
@@ -407,7 +410,7 @@ void attend_split_kernel(
       if (nxt) {
         int64_t zo;
         zv[j] = z_src(inx, vn, j, zo);
-        if (zv[j]) zc[j] = load_chunk(zpool, zo);
+        if (zv[j]) zc[j] = load_page_chunk<STREAM>(zpool, zo);
       }
       if (G >= 8) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted probability reads
     }
@@ -545,13 +548,19 @@ void attend_split_kernel(
 struct AttendVariant {
   int dtype, G, rv;
   const void *fn1, *fn;  // one block per wavefront and round; kAttendBlocks
+  const void *fn_nt;     // kAttendBlocks with non-temporal gathers (null: not built)
 };
 
-#define BKV_ATT(T, C, DT, G, RV)                                                                \
-  {DT, G, RV,                                                                                   \
-   reinterpret_cast<const void *>(&attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, 1>),       \
-   reinterpret_cast<const void *>(                                                              \
-       &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks>)}
+// non-temporal variants for the 4-head kernels (the 8B-shaped group, and the
+// halves of split 8-head groups), whose gathers are long streams
+#define BKV_ATT(T, C, DT, G, RV)                                                                 \
+  {DT, G, RV,                                                                                    \
+   reinterpret_cast<const void *>(&attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, 1, false>), \
+   reinterpret_cast<const void *>(                                                               \
+       &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, false>),                 \
+   (G) == 4 ? reinterpret_cast<const void *>(                                                    \
+                  &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, ((G) == 4)>)  \
+            : nullptr}
 #define BKV_ATT_G(T, C, DT, RV)                                                  \
   BKV_ATT(T, C, DT, 1, RV), BKV_ATT(T, C, DT, 2, RV), BKV_ATT(T, C, DT, 4, RV), \
       BKV_ATT(T, C, DT, 8, RV)
@@ -671,9 +680,15 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};
-  // a split of at most one block per wavefront takes the one-block kernel
+  // a split of at most one block per wavefront takes the one-block kernel;
+  // non-temporal gathers when the launch is a long stream (the two-block
+  // kernel: measured slower on the short launches, whose time is latency),
+  // each load instruction reads whole 128-byte lines and no other subgroup
+  // reads the same pages
   const bool one = a.pages_per_split <= kAttendWaves * (64 / d.page_size);
-  return hipLaunchKernel(one ? v->fn1 : v->fn, dim3(a.padded), dim3(256), args, 0, s);
+  const bool nt = v->fn_nt && !one && a.gs == 1 && d.page_size >= 8;
+  const void *fn = nt ? v->fn_nt : (one ? v->fn1 : v->fn);
+  return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
 }
 
 }  // namespace bkv_host

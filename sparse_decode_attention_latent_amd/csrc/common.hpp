@@ -134,6 +134,21 @@ __device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte
   return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
 }
 
+// A 16-byte load marked non-temporal (global_load_dwordx4 ... nt): for page
+// data a launch reads once.  On MI355X a streaming read with these loads
+// reaches about 7.0-7.2 TB/s, against 6.0-6.3 TB/s with ordinary loads
+// (400 MiB, 2K-25K workgroups, 4-16 loads in flight per lane).
+typedef unsigned int bkv_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_chunk_stream(const void *base_bytes, int64_t byte_off) {
+  const bkv_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const bkv_u32x4 *>(
+      reinterpret_cast<const char *>(base_bytes) + byte_off));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 load_page_chunk(const void *base_bytes, int64_t byte_off) {
+  return NT ? load_chunk_stream(base_bytes, byte_off) : load_chunk(base_bytes, byte_off);
+}
+
 // Ordering point for LDS traffic between the lanes of one wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

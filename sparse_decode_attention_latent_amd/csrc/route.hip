@@ -57,7 +57,12 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // so every FMA takes one scalar and one vector operand.  Page maxima are
 // butterfly reductions over the page's lanes.  A workgroup is four such
 // steps: many short workgroups keep more loads in flight than a few long
-// ones walking several steps each.
+// ones walking several steps each.  With STREAM the page loads are marked
+// non-temporal: the launch streams the pages once, and on MI355X such loads
+// read faster when every instruction reads whole 128-byte lines (pages of 8
+// or more tokens) and a lane has many of them in flight (8 or more chunks);
+// with 64-byte runs the other half of each line is fetched again, and with
+// few loads per lane their longer latency is not hidden.
 // ---------------------------------------------------------------------------
 
 struct ScoreArgs {
@@ -65,7 +70,7 @@ struct ScoreArgs {
   int pages_per_wg, chunks_per_bg, total, padded;
 };
 
-template <typename T, int G, int NZ, int NR>
+template <typename T, int G, int NZ, int NR, bool STREAM>
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const float *__restrict__ q_proj, const T *__restrict__ zpool, const T *__restrict__ rpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -108,9 +113,15 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
       const int64_t roff = (zhead + phys) * page_r_bytes + (int64_t)slot * 16;
       uint4 cz[NZ], cr[NR];
 #pragma unroll
-      for (int c = 0; c < NZ; ++c) cz[c] = load_chunk(zpool, zoff + (int64_t)c * a.page_size * 16);
+      for (int c = 0; c < NZ; ++c) {
+        const int64_t o = zoff + (int64_t)c * a.page_size * 16;
+        cz[c] = load_page_chunk<STREAM>(zpool, o);
+      }
 #pragma unroll
-      for (int c = 0; c < NR; ++c) cr[c] = load_chunk(rpool, roff + (int64_t)c * a.page_size * 16);
+      for (int c = 0; c < NR; ++c) {
+        const int64_t o = roff + (int64_t)c * a.page_size * 16;
+        cr[c] = load_page_chunk<STREAM>(rpool, o);
+      }
       float acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = 0.f;
@@ -153,15 +164,22 @@ hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const 
   return hipGetLastError();
 }
 
+constexpr int kStreamMinChunks = 8;  // chunk loads per lane that the non-temporal form needs
+
 struct ScoreVariant {
   int dtype, G, rb, rq;
-  const void *fn;
+  const void *fn, *fn_nt;  // ordinary loads; non-temporal loads (null: not built)
 };
 
-#define BKV_SCORE(T, DT, G, RB, RQ)                                                        \
-  {DT, G, RB, RQ,                                                                           \
-   reinterpret_cast<const void *>(                                                          \
-       &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE>)}
+#define BKV_SCORE(T, DT, G, RB, RQ)                                                                  \
+  {DT, G, RB, RQ,                                                                                     \
+   reinterpret_cast<const void *>(                                                                    \
+       &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE, false>),                      \
+   ((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks                                                    \
+       ? reinterpret_cast<const void *>(                                                              \
+             &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE,                         \
+                                (((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks)>)                   \
+       : nullptr}
 
 #define BKV_SCORE_G(T, DT, RB, RQ) \
   BKV_SCORE(T, DT, 1, RB, RQ), BKV_SCORE(T, DT, 2, RB, RQ), BKV_SCORE(T, DT, 4, RB, RQ), \
@@ -200,7 +218,8 @@ static int ilog2(int x) {
 static const void *find_score(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   for (const auto &v : kScoreVariants)
-    if (v.dtype == d.dtype && v.G == G && v.rb == d.r_b && v.rq == d.r_q) return v.fn;
+    if (v.dtype == d.dtype && v.G == G && v.rb == d.r_b && v.rq == d.r_q)
+      return v.fn_nt && d.page_size >= 8 ? v.fn_nt : v.fn;  // whole 128-byte lines per load
   return nullptr;
 }
 
