@@ -601,15 +601,20 @@ int attend_group_split(const basiskv_dims &d) {
 }
 
 // Pages per split.  Every wavefront takes up to kAttendBlocks 64-token blocks
-// per round; a split is one round when there is work enough for about two
-// workgroups per compute unit at that size, otherwise one block per
-// wavefront (more, smaller workgroups).  A split grows by whole rounds when
-// that would leave more than kMaxSplits splits (the kernel loops over them).
+// per round: kAttendBlocks when one block per wavefront would need more
+// wavefronts than the chip holds at once (two per SIMD: 2048), which would
+// leave a second, partial round of wavefronts waiting for the first; one
+// block otherwise (more, smaller workgroups).  A split grows by whole rounds
+// when that would leave more than kMaxSplits splits (the kernel loops over
+// them).
+#ifndef BKV_ATTEND_RESIDENT_WAVES
+#define BKV_ATTEND_RESIDENT_WAVES 2048
+#endif
 static int pages_per_split(const basiskv_dims &d, int32_t entries) {
   const int ppi = 64 / d.page_size;
   const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * attend_group_split(d) *
                          (((int64_t)entries + ppi - 1) / ppi);
-  const int per_wave = blocks >= (int64_t)kAttendWaves * kAttendBlocks * 512 ? kAttendBlocks : 1;
+  const int per_wave = blocks > BKV_ATTEND_RESIDENT_WAVES ? kAttendBlocks : 1;
   const int per_round = kAttendWaves * per_wave * ppi;
   int rounds = 1;
   const int64_t need = ((int64_t)entries + kMaxSplits - 1) / kMaxSplits;

@@ -10,7 +10,18 @@
 // counts by ballots); a row held by several wavefronts resolves 8 bits per
 // round (a histogram of the next digit over the keys that share the decided
 // bits, by LDS atomics, and a suffix scan over its 256 bins), paying one
-// barrier pair per digit instead of one per bit.  Either way the search stops
+// barrier pair per digit instead of one per bit.  For rows held by 16
+// wavefronts (over 4096 pages) the first digit is
+// not a bit field but one of 256 equal-width buckets of the score range
+// [min, max]: a bucket index is a monotone function of the score, so the k-th
+// largest key lies in one bucket T, every key of a higher bucket is taken and
+// the search goes on over T's keys only, from the highest bit in which they
+// differ.  (The leading bits of a row's keys are sign and exponent: as a
+// first digit they fall in a handful of bins -- most keys in one, its LDS
+// atomics serialised -- when a row holds scores of both signs.  On rows held
+// by four wavefronts the extra phase measured slower.)  Rows whose range is
+// not a finite positive number start with the bit digits.  Either
+// way the search stops
 // as soon as exactly k keys share the decided bits (the top-k set is then
 // decided, whatever the lower bits of the k-th key).  The compaction
 // then hands out, in page order, every page whose key exceeds tau and the
@@ -24,6 +35,10 @@ namespace bkv {
 #define BKV_TOPK_RADIX_WAVES 4
 #endif
 constexpr int kTopkRadixWaves = BKV_TOPK_RADIX_WAVES;  // rows this wide search by digits
+#ifndef BKV_TOPK_BUCKET_WAVES
+#define BKV_TOPK_BUCKET_WAVES 16
+#endif
+constexpr int kTopkBucketWaves = BKV_TOPK_BUCKET_WAVES;  // rows this wide start with value buckets
 
 // Order-preserving key of a score: larger score, larger key.  -0 and +0 are
 // one key; NaN ranks below every number; 0 is left for lanes past the row.
@@ -31,6 +46,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 1u;
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The score of an order key (inverse of order_key; NaN for key 1).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 template <int CTRL>
@@ -107,19 +127,13 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
     // digit holding the k-th largest key by a suffix scan over the bins ----
     const int tid = threadIdx.x;
     constexpr int NT = 64 * NWV;
-    int krem = k;  // rank of the k-th largest key among the keys matching tau so far
-    for (int hi = top; hi >= 0;) {
-      const int lo = hi >= 7 ? hi - 7 : 0;
-      const uint32_t dmask = (2u << (hi - lo)) - 1u;
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
-      __syncthreads();
+    int krem = k;  // rank of the k-th largest key among the keys still searched
+    uint32_t live = 0u;  // bit j: key j takes part in the search
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const bool ok = j < kpt && base + 64 * j < NP;
-        const bool match = hi == 31 || (key[j] >> (hi + 1)) == (tau >> (hi + 1));
-        if (ok && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1);
-      }
-      __syncthreads();
+    for (int j = 0; j < KPT; ++j)
+      if (j < kpt && base + 64 * j < NP) live |= 1u << j;
+    // wavefront 0 finds the bin holding the krem-th largest key; all read found[]
+    auto find_bin = [&]() {
       if (wave == 0) {
         int c[4], s = 0;
 #pragma unroll
@@ -145,6 +159,70 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
         }
       }
       __syncthreads();
+    };
+    int hi = top;
+    // ---- first digit: equal-width buckets of the score range ----
+    const float smax = key_value(kmax), smin = key_value(kmin);
+    const float range = smax - smin;
+    if (NWV >= kTopkBucketWaves && top >= 0 && __builtin_isfinite(range) &&
+        range > 0.f) {  // smin, smax finite too
+      const float scale = 256.f / range;
+      auto bucket = [&](float x) { return min(255, (int)((x - smin) * scale)); };
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if ((live >> j) & 1u) atomicAdd(&hist[bucket(v[j])], 1);
+      __syncthreads();
+      find_bin();
+      const int T = found[0];
+      krem -= found[1];
+      const bool whole = found[2] == krem;  // every key of bucket T is taken
+      // bucket T's keys: the rest of the search, from the highest bit they differ in
+      uint32_t mx = 0u, mn = ~0u;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        if (((live >> j) & 1u) && bucket(v[j]) == T) {
+          mx = max(mx, key[j]);
+          mn = min(mn, key[j]);
+        } else {
+          live &= ~(1u << j);
+        }
+      }
+      wave_max_min_u32(mx, mn);
+      if (lane == 0) {
+        xch[1][wave][0] = (int)mx;
+        xch[1][wave][1] = (int)mn;
+      }
+      __syncthreads();
+      mx = 0u;
+      mn = ~0u;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        mx = max(mx, (uint32_t)xch[1][w][0]);
+        mn = min(mn, (uint32_t)xch[1][w][1]);
+      }
+      const uint32_t d2 = mx ^ mn;
+      hi = d2 ? 31 - __clz(d2) : -1;
+      tau = hi < 0 ? mx : hi == 31 ? 0u : mx & ~((2u << hi) - 1u);
+      if (whole) {  // the k-th largest key is the bucket's least
+        tau = mn;
+        hi = -1;
+      }
+      // (found[] and hist are rewritten only after the next barrier)
+    }
+    for (; hi >= 0;) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool match = hi == 31 || (key[j] >> (hi + 1)) == (tau >> (hi + 1));
+        if (((live >> j) & 1u) && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1);
+      }
+      __syncthreads();
+      find_bin();
       const int digit = found[0];
       krem -= found[1];
       tau |= (uint32_t)digit << lo;

@@ -357,6 +357,61 @@ def test_long_rows_selection(page_size, ctx):
     run_case(wl, batch=1, ctx=ctx, top_k=40)
 
 
+def _crafted_rows(n_rows, n, rng):
+    """Score rows that exercise every path of the selection: both signs (the
+    value-bucket first digit), a tiny range with many ties, -inf entries, one
+    value everywhere, two values, a range too wide for float32 (the bit-digit
+    path), and +0 / -0 ties."""
+    rows = []
+    for r in range(n_rows):
+        kind = r % 8
+        x = rng.standard_normal(n).astype(np.float32)
+        if kind == 1:
+            x = (1.0 + rng.integers(0, 50, n) * 2.0 ** -20).astype(np.float32)
+        elif kind == 2:
+            x[rng.choice(n, n // 10, replace=False)] = -np.inf
+        elif kind == 3:
+            x[:] = 0.25
+        elif kind == 4:
+            x = np.where(rng.random(n) < 0.3, 1.0, 0.0).astype(np.float32)
+        elif kind == 5:
+            x[rng.choice(n, 3, replace=False)] = np.float32([3e38, -3e38, 2e38])
+        elif kind == 6:
+            x = (x * 1e-30).astype(np.float32)
+        elif kind == 7:
+            x = np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)) + \
+                np.where(rng.random(n) < 0.01, np.float32(1.0), np.float32(0.0))
+        rows.append(x.astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("max_pages,top_k", [(2048, 100), (8192, 512), (12000, 640)])
+def test_select_crafted_rows_match_oracle(max_pages, top_k):
+    """basiskv_select_pages on crafted score rows (rows of 2048 pages run on
+    four wavefronts with bit digits; 8192 and 12000 on sixteen, starting with
+    value buckets) is exactly the oracle's selection, including ragged
+    sequence lengths and a recent window."""
+    rng = np.random.default_rng(max_pages)
+    B, hkv, S = 8, 2, 4
+    scores = _crafted_rows(B * hkv, max_pages, rng).reshape(B, hkv, max_pages)
+    seq_lens = np.array([max_pages * S - 3 * i * S - i for i in range(B)], dtype=np.int32)
+    for recent in (0, 64):
+        d = api.make_dims(batch=B, n_q_heads=4 * hkv, n_kv_heads=hkv, head_dim=128, hidden=256,
+                          r_v=64, r_b=64, r_q=32, page_size=S, max_pages_per_seq=max_pages,
+                          num_phys_pages=B * max_pages, dtype=api.BF16, recent_tokens=recent)
+        sc = torch.from_numpy(scores).cuda()
+        sl = torch.from_numpy(seq_lens).cuda()
+        sel = torch.full((B, hkv, top_k), -7, dtype=torch.int32, device="cuda")
+        api.select_pages(d, sc, sl, top_k, sel)
+        got = sel.cpu().numpy()
+        for b in range(B):
+            n_cand = ref.recent_window_first_page(int(seq_lens[b]), S, recent)
+            for g in range(hkv):
+                want = ref.select_pages(scores[b, g].astype(np.float64), n_cand, top_k)
+                np.testing.assert_array_equal(got[b, g], want, err_msg=f"b={b} g={g} recent={recent}")
+    _say(f"  select {max_pages} pages, k={top_k}: all rows exact")
+
+
 @pytest.mark.parametrize("wl_index,ctx", [(2, 4096), (4, 8192 * 8)])
 def test_all_scores_tied_selects_lowest_pages(wl_index, ctx):
     """Zero queries make every page score 0: the k lowest page indices are
