@@ -465,6 +465,23 @@ def test_fp8_other_shapes(wl_index):
     run_case(wl, batch=3, ctx=4096, seq_lens=[4096, 2500, 77], top_k=16)
 
 
+@pytest.mark.parametrize("page_size", [4, 8, 16, 64])
+def test_fp8_page_sizes(page_size):
+    wl = workload(FP8).with_(page_size=page_size)
+    run_case(wl, batch=2, ctx=3000, seq_lens=[3000, 2001], top_k=24)
+
+
+@pytest.mark.parametrize("group", [1, 2, 8])
+def test_fp8_group_sizes(group):
+    wl = workload(1).with_(n_q_heads=8 * group, cache_storage="fp8")
+    run_case(wl, batch=2, ctx=2048, seq_lens=[2048, 1500])
+
+
+def test_fp8_recent_window_ragged():
+    run_case(workload(FP8), batch=5, ctx=1000, seq_lens=[1000, 999, 33, 1, 517], top_k=8,
+             recent_tokens=64)
+
+
 def test_fp8_combined_calls_equal_the_separate_calls():
     wl = workload(FP8)
     inp = synth.decode_inputs(wl, batch=3, ctx=8192, seq_lens=[8192, 5000, 40])
