@@ -126,8 +126,9 @@ size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t top_k);
  *   A [n_kv][head_dim][r_v]   Value encoder:   z = v A            -> z pool
  *   P [n_kv][r_b][head_dim]   latent -> Key predictor
  *   E [n_kv][head_dim][r_q]   residual encoder: r = (k - z_s[:r_b] P) E -> r pool
- *   the Key itself is copied to the k pool.  z_s is the latent as stored
- *   (rounded to dtype).  GEMMs run on MFMA with float32 accumulation.
+ *   the Key itself is stored in the k pool (copied; rounded to E4M3 with
+ *   BASISKV_BF16_FP8_E4M3).  z_s is the latent as stored (rounded to the cache
+ *   format).  GEMMs run on MFMA with float32 accumulation.
  * seq_lens are not read or changed.  Returns ERR_SHAPE for n_tokens < 1. */
 int32_t basiskv_compress_prefill(const basiskv_dims *dims, const void *k, const void *v,
                                  const int32_t *start_pos, int32_t n_tokens, const void *A,
@@ -198,9 +199,11 @@ int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
  * two bf16 terms (hi + lo) so no precision is lost before the product.
  *   u [batch][n_q_heads * r_v] float32;  M: hidden x K (K = n_q_heads * r_v)
  *   elements in the tiled layout written by basiskv_fuse_output_matrix;
- *   y [batch][hidden] out, in dtype.  Needs hidden % 16 == 0 and K % 32 == 0
- *   (bf16) or K % 16 == 0 (float32), ERR_UNSUPPORTED otherwise.
- * batch must be <= 32 for bf16 and <= 64 for float32 (ERR_UNSUPPORTED). */
+ *   y [batch][hidden] out, in dtype (bf16 for BASISKV_BF16_FP8_E4M3).  Needs
+ *   hidden % 16 == 0 and K % 32 == 0 (bf16 activations) or K % 16 == 0
+ *   (float32), ERR_UNSUPPORTED otherwise.
+ * batch must be <= 32 for bf16 activations and <= 64 for float32
+ * (ERR_UNSUPPORTED). */
 int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void *M, void *y,
                             void *stream);
 
@@ -235,7 +238,8 @@ int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void 
  * of the dense path is basiskv_reconstruct with dims.r_v = head_dim and the
  * matrix basiskv_fuse_output_matrix builds from an identity decoder.
  * workspace: basiskv_dense_workspace_bytes, zero-filled once, as for the
- * other calls.  bf16 only (ERR_UNSUPPORTED for float32). */
+ * other calls.  BASISKV_BF16 or BASISKV_BF16_FP8_E4M3 (then both pools hold
+ * E4M3 codes); ERR_UNSUPPORTED for float32. */
 size_t basiskv_dense_workspace_bytes(const basiskv_dims *dims);
 int32_t basiskv_dense_attend(const basiskv_dims *dims, const void *q, const void *k_pages,
                              const void *v_pages, const int32_t *block_table,
@@ -245,7 +249,7 @@ int32_t basiskv_dense_attend(const basiskv_dims *dims, const void *q, const void
 /* Set-up: fuse the Value decoder into the output projection,
  *   M[n][h * r_v + i] = sum_d Bf[h / G][i][d] * W_O[h * head_dim + d][n],
  * i.e. M = (blockdiag_h(Bf_{h/G}) W_O)^T, float32 accumulation, stored in dtype
- * in MFMA tiles: element (n, k) at
+ * (bf16 for BASISKV_BF16_FP8_E4M3) in MFMA tiles: element (n, k) at
  *   ((n / 16 * (K / KS) + k / KS) * 64 + (k % KS) / KL * 16 + n % 16) * KL + k % KL,
  * KL = 16 / element bytes (8 bf16, 4 float32), KS = 4 * KL, K = n_q_heads * r_v;
  * each MFMA step's operand (16 features x KS slots) is one contiguous 1 KB run.
