@@ -44,8 +44,7 @@ KERNEL_SOURCES = ("sparse_decode_attention_latent_amd/csrc/route.hip",
                   "sparse_decode_attention_latent_amd/csrc/attend.hip",
                   "sparse_decode_attention_latent_amd/csrc/common.hpp",
                   "sparse_decode_attention_latent_amd/csrc/topk.hpp",
-                  "sparse_decode_attention_latent_amd/csrc/decode_bodies.hpp",
-                  "include/basiskv.h")
+                  "sparse_decode_attention_latent_amd/csrc/decode_bodies.hpp")
 PMC_KERNELS = ("route_scan_kernel", "attend_split_kernel")
 
 
