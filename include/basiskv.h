@@ -65,7 +65,7 @@ typedef enum {
   BASISKV_OK = 0,
   BASISKV_ERR_NULL = 1,        /* a required pointer is NULL */
   BASISKV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
-  BASISKV_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements */
+  BASISKV_ERR_UNSUPPORTED = 3, /* valid, but outside what this library implements */
   BASISKV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
   BASISKV_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch */
 } basiskv_status;
