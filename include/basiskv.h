@@ -50,6 +50,15 @@
  * one wavefront with a token per lane reads page_size * 16 contiguous bytes per
  * chunk.  Logical page p of sequence b is physical page block_table[b][p].
  * Widths must be multiples of CE.
+ *
+ * Routing-first layout (dims.page_layout = BASISKV_LAYOUT_ROUTING_FIRST): the
+ * latent and residual share one pool, cache.z_pages, whose pages hold
+ * (r_v + r_q) / CE chunks in the order: the latent's first r_b / CE chunks, the
+ * r_q / CE residual chunks, the latent's remaining chunks; cache.r_pages is
+ * not used.  Routing then reads one contiguous run of (r_b + r_q) / CE chunks
+ * per page (appendix Table 4's routing widths), where the separate pools give
+ * two; with small pages and narrow E4M3 rows a separate run fills half of a
+ * 128-byte memory line.  Every call of one cache must use the same layout.
  */
 #ifndef BASISKV_H
 #define BASISKV_H
@@ -71,6 +80,7 @@ typedef enum {
 } basiskv_status;
 
 enum { BASISKV_F32 = 0, BASISKV_BF16 = 1, BASISKV_BF16_FP8_E4M3 = 2 };
+enum { BASISKV_LAYOUT_SEPARATE = 0, BASISKV_LAYOUT_ROUTING_FIRST = 1 };
 
 /* Sizes of one layer's decode problem (host values). */
 typedef struct {
@@ -93,12 +103,16 @@ typedef struct {
                                 their score, and the top_k routed pages are chosen among the
                                 pages before them; sel still holds the routed pages only.
                                 0: no window. */
+  int32_t page_layout;       /* BASISKV_LAYOUT_SEPARATE (three pools) or
+                                BASISKV_LAYOUT_ROUTING_FIRST (see above) */
 } basiskv_dims;
 
 /* The paged cache (device pointers, caller-owned). */
 typedef struct {
-  void *z_pages;              /* Value latents  [n_kv][num_phys][r_v/CE][page_size][CE] */
-  void *r_pages;              /* residual codes [n_kv][num_phys][r_q/CE][page_size][CE] */
+  void *z_pages;              /* Value latents  [n_kv][num_phys][r_v/CE][page_size][CE]
+                                 (routing-first: [n_kv][num_phys][(r_v+r_q)/CE][page_size][CE]) */
+  void *r_pages;              /* residual codes [n_kv][num_phys][r_q/CE][page_size][CE]
+                                 (routing-first: unused, may be NULL) */
   void *k_pages;              /* exact Keys     [n_kv][num_phys][head_dim/CE][page_size][CE] */
   const int32_t *block_table; /* [batch][max_pages_per_seq] logical -> physical page */
   const int32_t *seq_lens;    /* [batch] valid tokens of each sequence */

@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libbasiskv.so")
 
 F32, BF16, BF16_FP8 = 0, 1, 2  # BF16_FP8: bf16 activations, E4M3 cache pages
+LAYOUT_SEPARATE, LAYOUT_ROUTING_FIRST = 0, 1  # page layouts (include/basiskv.h)
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_WORKSPACE",
           5: "ERR_LAUNCH"}
 
@@ -35,7 +36,8 @@ class BasisKVError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "r_v", "r_b", "r_q",
-        "page_size", "max_pages_per_seq", "num_phys_pages", "dtype", "recent_tokens")]
+        "page_size", "max_pages_per_seq", "num_phys_pages", "dtype", "recent_tokens",
+        "page_layout")]
 
 
 class Cache(ctypes.Structure):
@@ -101,9 +103,10 @@ def _check(status, where):
 
 
 def make_dims(*, batch, n_q_heads, n_kv_heads, head_dim, hidden, r_v, r_b, r_q, page_size,
-              max_pages_per_seq, num_phys_pages, dtype, recent_tokens=0):
+              max_pages_per_seq, num_phys_pages, dtype, recent_tokens=0,
+              page_layout=LAYOUT_SEPARATE):
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, hidden, r_v, r_b, r_q, page_size,
-                max_pages_per_seq, num_phys_pages, dtype, recent_tokens)
+                max_pages_per_seq, num_phys_pages, dtype, recent_tokens, page_layout)
 
 
 def make_cache(z_pages, r_pages, k_pages, block_table, seq_lens):

@@ -31,6 +31,7 @@ class Workload:
     seed: int = 1000
     recent_tokens: int = 0  # recent window attended besides the routed pages
     cache_storage: str = ""  # "fp8": z, r and Key pages as E4M3 codes ("" = storage)
+    page_layout: int = 0     # 1: routing-first pages (latent and residual in one pool)
     # prefill + decode workload only
     prefill_batch: int = 0
     prefill_tokens: int = 0
@@ -97,6 +98,11 @@ EXTRA_WORKLOADS = (
              top_k=512, recent_tokens=64, n_planted=8, planted="random",
              latent_norm_sigma=0.5, seed=1007, cache_storage="fp8"),
 )
+# The same configurations with the routing-first page layout (each page's
+# routing dims contiguous; include/basiskv.h).
+EXTRA_WORKLOADS = EXTRA_WORKLOADS + tuple(
+    w.with_(name=w.name + "-routing-first", page_layout=1)
+    for w in (WORKLOADS[2], EXTRA_WORKLOADS[0], EXTRA_WORKLOADS[1], EXTRA_WORKLOADS[2]))
 
 HEADLINE = 2
 

@@ -29,6 +29,8 @@ int32_t check_dims(const basiskv_dims *d) {
     return BASISKV_ERR_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0 || d->r_b > d->r_v) return BASISKV_ERR_SHAPE;
   if (d->recent_tokens < 0) return BASISKV_ERR_SHAPE;
+  if (d->page_layout != BASISKV_LAYOUT_SEPARATE && d->page_layout != BASISKV_LAYOUT_ROUTING_FIRST)
+    return BASISKV_ERR_UNSUPPORTED;
   if (d->head_dim != bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!pow2_page(d->page_size)) return BASISKV_ERR_UNSUPPORTED;
   const int ce = bkv_host::cache_chunk(*d);  // whole 16-byte chunks per cached row
@@ -46,8 +48,14 @@ bool output_tiles_fit(const basiskv_dims &d) {
   return d.hidden % 16 == 0 && (d.n_q_heads * d.r_v) % kstep == 0;
 }
 
-int32_t check_cache(const basiskv_cache *c, bool need_k, bool need_z, bool need_r) {
+// (with the routing-first layout the residual lives in the latent pool)
+int32_t check_cache(const basiskv_dims &d, const basiskv_cache *c, bool need_k, bool need_z,
+                    bool need_r) {
   if (!c || !c->block_table || !c->seq_lens) return BASISKV_ERR_NULL;
+  if (bkv_host::routing_first(d)) {
+    need_z = need_z || need_r;
+    need_r = false;
+  }
   if ((need_k && !c->k_pages) || (need_z && !c->z_pages) || (need_r && !c->r_pages))
     return BASISKV_ERR_NULL;
   return BASISKV_OK;
@@ -128,7 +136,7 @@ int32_t basiskv_compress_prefill(const basiskv_dims *d, const void *k, const voi
   int32_t st = check_dims(d);
   if (st) return st;
   if (!k || !v || !start_pos || !A || !P || !E) return BASISKV_ERR_NULL;
-  if ((st = check_cache(c, true, true, true))) return st;
+  if ((st = check_cache(*d, c, true, true, true))) return st;
   if (n_tokens < 1) return BASISKV_ERR_SHAPE;
   if (d->r_v % 16 || d->r_q % 16) return BASISKV_ERR_UNSUPPORTED;  // 16-wide MFMA output tiles
   if ((int64_t)d->batch * n_tokens > INT32_MAX / 2) return BASISKV_ERR_SHAPE;
@@ -150,7 +158,7 @@ int32_t basiskv_score_pages(const basiskv_dims *d, const float *q_proj, const ba
   int32_t st = check_dims(d);
   if (st) return st;
   if (!q_proj || !page_scores) return BASISKV_ERR_NULL;
-  if ((st = check_cache(c, false, true, true))) return st;
+  if ((st = check_cache(*d, c, false, true, true))) return st;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   bool unsupported = false;
   hipError_t e = bkv_host::launch_score(*d, q_proj, *c, page_scores, as_stream(stream),
@@ -174,7 +182,7 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
   int32_t st = check_dims(d);
   if (st) return st;
   if (!q || !P || !Q || !page_scores || !sel) return BASISKV_ERR_NULL;
-  if ((st = check_cache(c, false, true, true))) return st;
+  if ((st = check_cache(*d, c, false, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!ws || ws_bytes < scratch_offset(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
@@ -194,7 +202,7 @@ int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basisk
   int32_t st = check_dims(d);
   if (st) return st;
   if (!q || !sel || !u) return BASISKV_ERR_NULL;
-  if ((st = check_cache(c, true, true, false))) return st;
+  if ((st = check_cache(*d, c, true, true, false))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!bkv_host::attend_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < scratch_offset(*d) + partial_bytes(*d, top_k))
@@ -228,7 +236,7 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (!q || !k_new || !v_new || !start_pos || !A || !P || !Q || !E || !M || !page_scores ||
       !sel || !u || !y)
     return BASISKV_ERR_NULL;
-  if ((st = check_cache(c, true, true, true))) return st;
+  if ((st = check_cache(*d, c, true, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (d->r_v > bkv::kHeadDim || d->r_q > bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
@@ -261,6 +269,7 @@ static basiskv_dims dense_dims(const basiskv_dims &d) {
   basiskv_dims dd = d;
   dd.r_v = d.head_dim;
   dd.recent_tokens = 0;
+  dd.page_layout = BASISKV_LAYOUT_SEPARATE;  // the Key and Value pools are plain
   return dd;
 }
 

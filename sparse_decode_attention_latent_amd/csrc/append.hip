@@ -33,9 +33,11 @@ static hipError_t append_t(const basiskv_dims &d, const void *k, const void *v,
   a.num_phys = d.num_phys_pages;
   a.page_size = d.page_size;
   a.cap = d.max_pages_per_seq * d.page_size;
+  a.geom = pool_geom(d);
   hipLaunchKernelGGL((append_kernel<T, C>), dim3(d.n_kv_heads, d.batch * n_tokens), dim3(256), 0,
                      s, (const T *)k, (const T *)v, start_pos, (const T *)A, (const T *)P,
-                     (const T *)E, (C *)c.z_pages, (C *)c.r_pages, (C *)c.k_pages, c.block_table, a);
+                     (const T *)E, (C *)c.z_pages, (C *)residual_pool(d, c), (C *)c.k_pages,
+                     c.block_table, a);
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ struct AttendArgs {
   float scale_log2;  // scale * log2(e): exponentials are taken base 2
   int32_t *counters;  // [batch * n_kv * gs], zero between calls (see the merge)
   uint16_t *u_tiles;  // optional: u also written as the reconstruction's A operand (bf16)
+  PoolGeom geom;      // latent chunk positions within a page of the latent pool
 };
 
 // Partial record per (b, h, split): [m, l, u[0..r_v)] with m in base-2 logit
@@ -207,7 +208,7 @@ void attend_split_kernel(
 
   const int64_t head_page0 = (int64_t)g * a.num_phys;
   const int64_t kpage_bytes = (int64_t)NKC * a.page_size * 16;
-  const int64_t zpage_bytes = (int64_t)NVC * a.page_size * 16;
+  const int64_t zpage_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
   const int64_t chunk_stride = (int64_t)a.page_size * 16;
 
   // latent-phase lane roles: chunk vc of tokens t = j * TG + tg
@@ -233,7 +234,7 @@ void attend_split_kernel(
     const int src = role ? t : 0;
     const int phys_t = __shfl(phys[i], src);
     const int valid_t = __shfl((int)v, src);
-    off = (head_page0 + phys_t) * zpage_bytes + vc * chunk_stride +
+    off = (head_page0 + phys_t) * zpage_bytes + z_chunk_slot(a.geom, vc) * chunk_stride +
           (int64_t)(src & (a.page_size - 1)) * 16;
     return role && valid_t != 0;
   };
@@ -682,6 +683,7 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.scale_log2 = scale * kLog2e;
   a.counters = counters;
   a.u_tiles = u_tiles;
+  a.geom = pool_geom(d);
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};

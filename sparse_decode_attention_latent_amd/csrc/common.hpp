@@ -271,6 +271,23 @@ __device__ __forceinline__ int xcd_work_index(int padded) {
   return (bid % kXcds) * per_xcd + bid / kXcds;
 }
 
+// Where a page's latent and residual chunks sit, in 16-byte chunks.  Separate
+// pools: latent chunk c is chunk c of a latent page of z_page_chunks = r_v / CE
+// chunks, residual chunk c is chunk c of a residual page.  Routing-first: one
+// pool whose page holds the first r_b / CE latent chunks, then the residual
+// chunks (from r_first = r_b / CE on), then the other latent chunks (shifted
+// by z_shift = r_q / CE).
+struct PoolGeom {
+  int z_page_chunks;  // chunks per page of the latent pool
+  int r_page_chunks;  // chunks per page of the residual pool
+  int r_first;        // page chunk of residual chunk 0
+  int z_split;        // latent chunks from this one on ...
+  int z_shift;        // ... sit this many chunks further into the page
+};
+__host__ __device__ __forceinline__ int z_chunk_slot(const PoolGeom &g, int c) {
+  return c < g.z_split ? c : c + g.z_shift;
+}
+
 __host__ __device__ __forceinline__ int clamp_len(int L, int cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
@@ -286,6 +303,29 @@ inline bool cache_fp8(const basiskv_dims &d) { return d.dtype == BASISKV_BF16_FP
 // elements per 16-byte chunk of a cache page
 inline int cache_chunk(const basiskv_dims &d) {
   return cache_fp8(d) ? 16 : (act_bf16(d) ? 8 : 4);
+}
+inline bool routing_first(const basiskv_dims &d) {
+  return d.page_layout == BASISKV_LAYOUT_ROUTING_FIRST;
+}
+inline bkv::PoolGeom pool_geom(const basiskv_dims &d) {
+  const int ce = cache_chunk(d);
+  bkv::PoolGeom g;
+  if (routing_first(d)) {
+    g.z_page_chunks = g.r_page_chunks = (d.r_v + d.r_q) / ce;
+    g.r_first = g.z_split = d.r_b / ce;
+    g.z_shift = d.r_q / ce;
+  } else {
+    g.z_page_chunks = d.r_v / ce;
+    g.r_page_chunks = d.r_q / ce;
+    g.r_first = 0;
+    g.z_split = d.r_v / ce;
+    g.z_shift = 0;
+  }
+  return g;
+}
+// the residual pool: a pool of its own, or the latent pool (routing-first)
+inline void *residual_pool(const basiskv_dims &d, const basiskv_cache &c) {
+  return routing_first(d) ? c.z_pages : c.r_pages;
 }
 
 hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, const void *Q,

@@ -23,6 +23,7 @@ namespace bkv {
 // ---------------------------------------------------------------------------
 struct AppendArgs {
   int n_tokens, n_kv, rv, rb, rq, max_pages, num_phys, page_size, cap;
+  PoolGeom geom;  // chunk positions of the latent and residual pages
 };
 
 // Sums over the slices of a phase.  Lane l of a wavefront holds the partial
@@ -191,11 +192,13 @@ __device__ __forceinline__ void append_body(
     char *dst;
     if (tid < zc) {
       val = *reinterpret_cast<const uint4 *>(zst + tid * CC);
-      dst = reinterpret_cast<char *>(zpool) + ((hp * zc + tid) * a.page_size + slot) * 16;
+      dst = reinterpret_cast<char *>(zpool) +
+            ((hp * a.geom.z_page_chunks + z_chunk_slot(a.geom, tid)) * a.page_size + slot) * 16;
     } else if (tid < zc + rc) {
       const int c = tid - zc;
       val = *reinterpret_cast<const uint4 *>(rst + c * CC);
-      dst = reinterpret_cast<char *>(rpool) + ((hp * rc + c) * a.page_size + slot) * 16;
+      dst = reinterpret_cast<char *>(rpool) +
+            ((hp * a.geom.r_page_chunks + a.geom.r_first + c) * a.page_size + slot) * 16;
     } else {
       const int c = tid - zc - rc;
       if constexpr (kRoundKey)

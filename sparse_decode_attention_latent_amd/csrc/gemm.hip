@@ -254,6 +254,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(const T *__restrict__ Bf,
 // ---------------------------------------------------------------------------
 struct CompressArgs {
   int batch, n_tokens, n_kv, rv, rb, rq, rb_pad, max_pages, num_phys, page_size, cap;
+  PoolGeom geom;  // chunk positions of the latent and residual pages
 };
 
 // LDS rows are padded by 16 bytes, so the 16 rows a fragment load touches
@@ -474,7 +475,10 @@ __global__ __launch_bounds__(256) void compress_kernel(
 
     // ---- page stores: latent and residual chunks from LDS, Key chunks from the fragments ----
     const int64_t hp_own = (int64_t)g * a.num_phys + phys;
-    auto store_tile = [&](const T *tile, int stride, int n_chunks, C *pool) {
+    // tile chunk c goes to page chunk first + (c < split ? c : c + shift) of a
+    // pool page of page_chunks chunks
+    auto store_tile = [&](const T *tile, int stride, int n_chunks, C *pool, int page_chunks,
+                          int first, int split, int shift) {
       for (int it = 0; it < (16 * n_chunks + 63) / 64; ++it) {
         const int o = it * 64 + lane;
         const int rr = o < 16 * n_chunks ? o / n_chunks : 0, c = o - rr * n_chunks;
@@ -493,13 +497,15 @@ __global__ __launch_bounds__(256) void compress_kernel(
           } else {
             val = *reinterpret_cast<const uint4 *>(tile + rr * stride + c * CC);
           }
+          const int pc = first + (c < split ? c : c + shift);
           *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(pool) +
-                                     ((hp * n_chunks + c) * a.page_size + sl) * 16) = val;
+                                     ((hp * page_chunks + pc) * a.page_size + sl) * 16) = val;
         }
       }
     };
-    store_tile(Zs, L.zs_stride, zc_total, zpool);
-    store_tile(Rs, a.rq, rc_total, rpool);
+    store_tile(Zs, L.zs_stride, zc_total, zpool, a.geom.z_page_chunks, 0, a.geom.z_split,
+               a.geom.z_shift);
+    store_tile(Rs, a.rq, rc_total, rpool, a.geom.r_page_chunks, a.geom.r_first, rc_total, 0);
     if (phys >= 0) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -607,6 +613,7 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   a.num_phys = d.num_phys_pages;
   a.page_size = d.page_size;
   a.cap = d.max_pages_per_seq * d.page_size;
+  a.geom = pool_geom(d);
   const size_t lds = compress_lds_bytes<T>(d, a.rb_pad);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&compress_kernel<T, C>),
@@ -619,8 +626,8 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   if (wgs > kCompressWgsPerHead) wgs = kCompressWgsPerHead;  // persistent: factors staged once each
   hipLaunchKernelGGL((compress_kernel<T, C>), dim3(wgs, d.n_kv_heads), dim3(256), lds, s,
                      (const T *)k, (const T *)v, start_pos, (const T *)A, (const T *)P,
-                     (const T *)E, (C *)c.z_pages, (C *)c.r_pages, (C *)c.k_pages, c.block_table,
-                     a);
+                     (const T *)E, (C *)c.z_pages, (C *)residual_pool(d, c), (C *)c.k_pages,
+                     c.block_table, a);
   return hipGetLastError();
 }
 

@@ -66,8 +66,9 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // ---------------------------------------------------------------------------
 
 struct ScoreArgs {
-  int n_q, n_kv, max_pages, num_phys, page_size, log2_page, zc_total, cap;
+  int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap;
   int pages_per_wg, chunks_per_bg, total, padded;
+  PoolGeom geom;  // chunk positions of the latent and residual pages
 };
 
 template <typename T, int G, int NZ, int NR, bool STREAM>
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int32_t *bt = block_table + (int64_t)b * a.max_pages;
   float *out = scores + (int64_t)bg * a.max_pages;
   const int64_t zhead = (int64_t)g * a.num_phys;
-  const int64_t page_z_bytes = (int64_t)a.zc_total * a.page_size * 16;
-  const int64_t page_r_bytes = (int64_t)NR * a.page_size * 16;
+  const int64_t page_z_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
+  const int64_t page_r_bytes = (int64_t)a.geom.r_page_chunks * a.page_size * 16;
 
   if (const int step = wave; step < n_steps) {
     const int p = p_begin + step * ppi + (lane >> a.log2_page);
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     float best = -INFINITY;
     if (valid) {
       const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
-      const int64_t roff = (zhead + phys) * page_r_bytes + (int64_t)slot * 16;
+      const int64_t roff =
+          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
       uint4 cz[NZ], cr[NR];
 #pragma unroll
       for (int c = 0; c < NZ; ++c) {
@@ -233,7 +235,6 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
     return hipSuccess;
   }
   *unsupported = false;
-  const int ce = cache_chunk(d);
   ScoreArgs a;
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
@@ -241,7 +242,7 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   a.num_phys = d.num_phys_pages;
   a.page_size = d.page_size;
   a.log2_page = ilog2(d.page_size);
-  a.zc_total = d.r_v / ce;
+  a.geom = pool_geom(d);
   a.cap = d.max_pages_per_seq * d.page_size;
   // 4 wavefronts per workgroup, one step of 64 tokens each
   const int ppi = 64 / d.page_size;
@@ -249,7 +250,8 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   a.chunks_per_bg = (d.max_pages_per_seq + a.pages_per_wg - 1) / a.pages_per_wg;
   a.total = d.batch * d.n_kv_heads * a.chunks_per_bg;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
-  void *args[] = {(void *)&q_proj, (void *)&c.z_pages, (void *)&c.r_pages,
+  void *rpool = residual_pool(d, c);
+  void *args[] = {(void *)&q_proj, (void *)&c.z_pages, (void *)&rpool,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&scores, (void *)&a};
   return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
 }

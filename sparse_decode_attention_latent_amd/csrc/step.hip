@@ -50,6 +50,7 @@ static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k
   a.ap.num_phys = d.num_phys_pages;
   a.ap.page_size = d.page_size;
   a.ap.cap = d.max_pages_per_seq * d.page_size;
+  a.ap.geom = pool_geom(d);
   a.n_append = d.n_kv_heads * d.batch;
   const int G = d.n_q_heads / d.n_kv_heads;
   a.proj_x = (G * (d.r_b + d.r_q) + 255) / 256;
@@ -60,7 +61,7 @@ static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k
   const int grid = a.n_append + a.proj_x * d.n_kv_heads * d.batch;
   hipLaunchKernelGGL((step_prologue_kernel<T, C>), dim3(grid), dim3(256), 0, s,
                      (const T *)k_new, (const T *)v_new, start_pos, (const T *)A, (const T *)P,
-                     (const T *)E, (const T *)Q, (const T *)q, (C *)c.z_pages, (C *)c.r_pages,
+                     (const T *)E, (const T *)Q, (const T *)q, (C *)c.z_pages, (C *)residual_pool(d, c),
                      (C *)c.k_pages, c.block_table, q_proj, a);
   return hipGetLastError();
 }

@@ -46,3 +46,21 @@ def unpack_pages(pool, block_table, page_size, T):
     x = pool[:, block_table.reshape(-1).astype(np.int64)]          # [H, B*NP, nc, S, ce]
     x = x.reshape(H, B, n_pages, nc, S, ce).transpose(1, 0, 2, 4, 3, 5)
     return x.reshape(B, H, n_pages * S, nc * ce)[:, :, :T]
+
+
+def pack_routing_first(z, r, r_b, block_table, page_size, num_phys_pages):
+    """Routing-first layout: logical z [B, Hkv, T, rV] and r [B, Hkv, T, rq]
+    -> one pool [Hkv, num_phys_pages, (rV + rq)/CE, S, CE] whose page chunks are
+    z[:r_b], then r, then z[r_b:] (r_b and rq whole chunks)."""
+    z, r = np.asarray(z), np.asarray(r)
+    ce = chunk_elems(z.dtype.itemsize)
+    assert r_b % ce == 0 and r.shape[-1] % ce == 0
+    rows = np.concatenate([z[..., :r_b], r, z[..., r_b:]], axis=-1)
+    return pack_pages(rows, block_table, page_size, num_phys_pages)
+
+
+def split_routing_first(rows, r_b, r_q):
+    """Rows [..., rV + rq] in routing-first order -> (z [..., rV], r [..., rq])."""
+    rows = np.asarray(rows)
+    z = np.concatenate([rows[..., :r_b], rows[..., r_b + r_q:]], axis=-1)
+    return z, rows[..., r_b:r_b + r_q]

@@ -62,7 +62,7 @@ class DecodeProblem:
     """
 
     def __init__(self, wl, inp, *, top_k=None, shuffle_seed=12345, device="cuda",
-                 max_pages=None, recent_tokens=None, device_random=None):
+                 max_pages=None, recent_tokens=None, device_random=None, page_layout=None):
         """device_random: None, or (batch, ctx, seed) for timing-only state whose
         pools, queries and new token are seeded N(0, 1) draws made on the device
         (inp then only supplies the factors); the selection is then arbitrary
@@ -71,6 +71,8 @@ class DecodeProblem:
         self.storage = inp["storage"]
         st = self.storage
         self.cache_storage = cst = inp.get("cache_storage") or wl.cache
+        self.page_layout = wl.page_layout if page_layout is None else int(page_layout)
+        rf = self.page_layout == api.LAYOUT_ROUTING_FIRST
         if device_random is None:
             q = inp["q"]
             B, Hq, dh = q.shape
@@ -89,7 +91,8 @@ class DecodeProblem:
                                   hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                   page_size=S, max_pages_per_seq=self.max_pages,
                                   num_phys_pages=self.num_phys,
-                                  dtype=dims_dtype(st, cst), recent_tokens=recent_tokens)
+                                  dtype=dims_dtype(st, cst), recent_tokens=recent_tokens,
+                                  page_layout=self.page_layout)
         self.recent_tokens = int(recent_tokens)
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         dev = device
@@ -99,7 +102,13 @@ class DecodeProblem:
             self.seq_lens_host = np.asarray(inp["seq_lens"], dtype=np.int32)
             pack = lambda a: to_device(layout.pack_pages(a, self.block_table_host, S, self.num_phys),
                                        cst, dev)
-            self.z_pages, self.r_pages, self.k_pages = pack(inp["z"]), pack(inp["r"]), pack(inp["kc"])
+            if rf:  # latent and residual in one pool; no residual pool
+                self.z_pages = to_device(layout.pack_routing_first(
+                    inp["z"], inp["r"], wl.r_b, self.block_table_host, S, self.num_phys), cst, dev)
+                self.r_pages = None
+            else:
+                self.z_pages, self.r_pages = pack(inp["z"]), pack(inp["r"])
+            self.k_pages = pack(inp["kc"])
             self.q = to_device(q, st, dev)
             # appended token of the step: [B, 1, Hkv, dh], written at seq_len - 1
             self.k_new = to_device(inp["k_new"][:, None], st, dev)
@@ -111,7 +120,11 @@ class DecodeProblem:
             gen.manual_seed(seed)
             rnd = lambda *shape: random_pool(shape, st, gen, dev)
             pool = lambda w: random_pool((Hkv, self.num_phys, w // ce, S, ce), cst, gen, dev)
-            self.z_pages, self.r_pages, self.k_pages = pool(wl.r_v), pool(wl.r_q), pool(dh)
+            if rf:
+                self.z_pages, self.r_pages = pool(wl.r_v + wl.r_q), None
+            else:
+                self.z_pages, self.r_pages = pool(wl.r_v), pool(wl.r_q)
+            self.k_pages = pool(dh)
             self.q = rnd(B, Hq, dh)
             self.k_new, self.v_new = rnd(B, 1, Hkv, dh), rnd(B, 1, Hkv, dh)
         self.seq_lens = torch.from_numpy(self.seq_lens_host).to(dev)
@@ -198,11 +211,16 @@ class DecodeProblem:
         S = self.wl.page_size
         phys = int(self.block_table_host[b, pos // S])
         slot = pos % S
-        rows = []
-        for pool in (self.z_pages, self.r_pages, self.k_pages):
+
+        def row(pool):
             t = pool[:, phys, :, slot, :].reshape(pool.shape[0], -1).contiguous()
-            rows.append(to_host_storage(t, self.cache_storage))
-        return tuple(rows)
+            return to_host_storage(t, self.cache_storage)
+
+        k = row(self.k_pages)
+        if self.r_pages is None:  # routing-first: one pool
+            z, r = layout.split_routing_first(row(self.z_pages), self.wl.r_b, self.wl.r_q)
+            return np.ascontiguousarray(z), np.ascontiguousarray(r), k
+        return row(self.z_pages), row(self.r_pages), k
 
 
 class DenseProblem:
@@ -265,9 +283,10 @@ class PrefillProblem:
     """
 
     def __init__(self, wl, k, v, fac, *, storage, cache_storage=None, shuffle_seed=54321,
-                 device="cuda"):
+                 device="cuda", page_layout=0):
         self.wl, self.storage = wl, storage
         self.cache_storage = cst = cache_storage or storage
+        self.page_layout = int(page_layout)
         B, T, Hkv, dh = k.shape
         S = wl.page_size
         self.T = T
@@ -277,7 +296,7 @@ class PrefillProblem:
                                   hidden=wl.hidden, r_v=wl.r_v, r_b=wl.r_b, r_q=wl.r_q,
                                   page_size=S, max_pages_per_seq=self.max_pages,
                                   num_phys_pages=self.num_phys,
-                                  dtype=dims_dtype(storage, cst))
+                                  dtype=dims_dtype(storage, cst), page_layout=self.page_layout)
         self.block_table_host = synth.block_table(B, self.max_pages, shuffle_seed=shuffle_seed)
         self.block_table = torch.from_numpy(self.block_table_host).to(device)
         self.seq_lens = torch.full((B,), T, dtype=torch.int32, device=device)
@@ -291,7 +310,11 @@ class PrefillProblem:
         def pool(w):
             return torch.zeros((Hkv, self.num_phys, w // ce, S, ce), dtype=tdt, device=device)
 
-        self.z_pages, self.r_pages, self.k_pages = pool(wl.r_v), pool(wl.r_q), pool(dh)
+        if self.page_layout == api.LAYOUT_ROUTING_FIRST:
+            self.z_pages, self.r_pages = pool(wl.r_v + wl.r_q), None
+        else:
+            self.z_pages, self.r_pages = pool(wl.r_v), pool(wl.r_q)
+        self.k_pages = pool(dh)
         self.cache = api.make_cache(self.z_pages, self.r_pages, self.k_pages, self.block_table,
                                     self.seq_lens)
 
@@ -302,8 +325,14 @@ class PrefillProblem:
     def logical(self):
         """Host copies of the pools as logical [B, Hkv, T, w] stored arrays."""
         torch.cuda.synchronize()
-        out = {}
-        for name, t in (("z", self.z_pages), ("r", self.r_pages), ("k", self.k_pages)):
-            out[name] = layout.unpack_pages(to_host_storage(t, self.cache_storage),
-                                            self.block_table_host, self.wl.page_size, self.T)
+        def logical(t):
+            return layout.unpack_pages(to_host_storage(t, self.cache_storage),
+                                       self.block_table_host, self.wl.page_size, self.T)
+
+        out = {"k": logical(self.k_pages)}
+        if self.r_pages is None:  # routing-first: one pool
+            out["z"], out["r"] = layout.split_routing_first(logical(self.z_pages), self.wl.r_b,
+                                                            self.wl.r_q)
+        else:
+            out["z"], out["r"] = logical(self.z_pages), logical(self.r_pages)
         return out

@@ -26,6 +26,15 @@ def test_header_declares_the_binding_names():
     assert header_functions() == sorted(api.EXPORTED)
 
 
+def test_dims_struct_matches_the_header():
+    """The ctypes mirror of basiskv_dims has the header's fields, in order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} basiskv_dims;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [n for n, _ in api.Dims._fields_]
+    assert ctypes.sizeof(api.Dims) == 4 * len(fields)
+
+
 @needs_lib
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(api.LIB_PATH)
@@ -88,6 +97,7 @@ def _cache(**kw):
     (dict(max_pages_per_seq=40000), 3),
     (dict(recent_tokens=-1), 2),
     (dict(dtype=2, r_q=40), 3),       # E4M3 rows: widths must fill 16-byte chunks (16 codes)
+    (dict(page_layout=2), 3),         # no such page layout
 ])
 def test_dims_validation(over, code):
     lib = api.lib()

@@ -573,6 +573,57 @@ def test_fp8_dense_attend_matches_oracle(seq_lens):
         _say(f"  dense fp8 b={b} L={L}: o {eo.max():.2e} y {float(ey):.2e}")
 
 
+# ---------------------------------------------------------------------------
+# the routing-first page layout (latent and residual in one pool, each page's
+# routing dims first): the same results, bit for bit, as the separate pools
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,batch,ctx,seq_lens,top_k", [
+    ("llama8b-ctx32k", 3, 4096, [4096, 3000, 33], 16),
+    ("llama8b-ctx32k-fp8", 3, 4096, [4096, 2222, 1], 16),
+    ("llama8b-ctx32k-b16r16-page4", 3, 4096, [4096, 4095, 100], None),
+    ("llama8b-ctx32k-b16r16-page4-fp8", 3, 4096, [4096, 1234, 65], None),
+    ("qwen32b-ctx32k", 2, 4096, [4096, 777], 16),
+    ("tiny-fp32", 2, 2048, [2048, 1000], None),
+])
+def test_routing_first_layout_matches_separate_pools(name, batch, ctx, seq_lens, top_k):
+    wl = workload(name)
+    _say(f"routing-first {name}: batch={batch} ctx={ctx} seq_lens={seq_lens}")
+    inp = synth.decode_inputs(wl, batch=batch, ctx=ctx, seq_lens=seq_lens)
+    outs, probs = [], []
+    for lay in (api.LAYOUT_SEPARATE, api.LAYOUT_ROUTING_FIRST):
+        prob = DecodeProblem(wl, inp, top_k=top_k, page_layout=lay)
+        prob.step_unfused(append=True)
+        a = prob.outputs()
+        codes = [prob.token_codes(b, int(L) - 1) for b, L in enumerate(seq_lens) if L > 0]
+        prob.u.fill_(float("nan"))
+        prob.decode_step()  # the one-call step on the same (already appended) cache
+        outs.append((a, codes, prob.outputs()))
+        probs.append(prob)
+    (a0, c0, d0), (a1, c1, d1) = outs
+    for key in ("scores", "sel", "u", "y"):
+        np.testing.assert_array_equal(a1[key], a0[key], err_msg=key)
+        np.testing.assert_array_equal(d1[key], d0[key], err_msg="one-call " + key)
+    for x, y in zip(c0, c1):
+        for u, v in zip(x, y):
+            np.testing.assert_array_equal(v, u)
+    compare_step(wl, inp, probs[1], a1, range(batch))
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_routing_first_prefill_compress_matches_separate_pools(cache):
+    wl = workload(4).with_(cache_storage=cache if cache == "fp8" else "")
+    k, v = synth.kv_activations(wl, batch=2, tokens=700, stream=3)
+    fac = synth.factors(wl)
+    got = []
+    for lay in (api.LAYOUT_SEPARATE, api.LAYOUT_ROUTING_FIRST):
+        prob = PrefillProblem(wl, k, v, fac, storage="bf16", cache_storage=cache, page_layout=lay)
+        prob.run()
+        got.append(prob.logical())
+    for key in ("z", "r", "k"):
+        np.testing.assert_array_equal(got[1][key], got[0][key], err_msg=key)
+
+
 def untile_output_matrix(flat, hidden, K, itemsize):
     """The documented tiled layout of the fused output matrix back to [hidden][K]."""
     kl = 16 // itemsize

@@ -69,6 +69,30 @@ def test_pack_unpack_roundtrip_both_storages():
         np.testing.assert_array_equal(layout.unpack_pages(pool, bt, 16, 61), x)
 
 
+def test_routing_first_pages_hold_routing_dims_first():
+    """Routing-first pool: chunk order z[:r_b], r, z[r_b:] within each page; the
+    scoring chunks of a token are the first (r_b + r_q) / CE of its page; the
+    split recovers both caches."""
+    bt = synth.block_table(2, 3, shuffle_seed=4)
+    rng = np.random.default_rng(5)
+    for dt, rv, rb, rq in ((np.uint8, 96, 16, 16), (np.uint16, 64, 64, 32), (np.float32, 32, 16, 8)):
+        z = rng.integers(0, 200, size=(2, 2, 40, rv)).astype(dt)
+        r = rng.integers(0, 200, size=(2, 2, 40, rq)).astype(dt)
+        pool = layout.pack_routing_first(z, r, rb, bt, 16, 6)
+        ce = 16 // np.dtype(dt).itemsize
+        assert pool.shape == (2, 6, (rv + rq) // ce, 16, ce)
+        rows = layout.unpack_pages(pool, bt, 16, 40)
+        zz, rr = layout.split_routing_first(rows, rb, rq)
+        np.testing.assert_array_equal(zz, z)
+        np.testing.assert_array_equal(rr, r)
+        # token 17 of sequence 1, KV head 1: its page and slot, chunk by chunk
+        phys, slot = bt[1, 17 // 16], 17 % 16
+        page = pool[1, phys, :, slot, :].reshape(-1)
+        np.testing.assert_array_equal(page[:rb], z[1, 1, 17, :rb])
+        np.testing.assert_array_equal(page[rb:rb + rq], r[1, 1, 17])
+        np.testing.assert_array_equal(page[rb + rq:], z[1, 1, 17, rb:])
+
+
 def test_workload_shapes():
     assert [w.name for w in WORKLOADS][2] == "llama8b-ctx32k"
     for w in WORKLOADS:
