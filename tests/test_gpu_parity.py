@@ -349,10 +349,11 @@ def test_repeated_steps_reuse_the_workspace_bit_exact():
     compare_step(wl, inp, prob, outs[-1], range(3))
 
 
-@pytest.mark.parametrize("page_size,ctx", [(8, 100000), (4, 80000)])
+@pytest.mark.parametrize("page_size,ctx", [(8, 100000), (4, 80000), (4, 131072)])
 def test_long_rows_selection(page_size, ctx):
-    """Rows of 12500 and 20000 pages: the selection runs as its own launch
-    with 1024 threads per row; every sequence checked against the oracle."""
+    """Rows of 12500, 20000 and 32768 pages (the largest max_pages_per_seq the
+    library takes): the selection runs as its own launch with 1024 threads per
+    row; every sequence checked against the oracle."""
     wl = workload(0).with_(page_size=page_size)
     run_case(wl, batch=1, ctx=ctx, top_k=40)
 
