@@ -161,6 +161,25 @@ def test_fp8_cache_dims():
 
 
 @needs_lib
+def test_routing_first_needs_no_residual_pool():
+    """Routing-first: the residual lives in the latent pool, so a NULL r_pages
+    passes validation and a NULL z_pages does not; with separate pools a NULL
+    r_pages is an error.  (Only calls that fail validation are made here.)"""
+    lib = api.lib()
+    d_rf = dims_of(WORKLOADS[2], page_layout=api.LAYOUT_ROUTING_FIRST)
+    d_sep = dims_of(WORKLOADS[2])
+    no_r = _cache(r_pages=None)
+    no_z = _cache(z_pages=None)
+    assert lib.basiskv_score_pages(ctypes.byref(d_sep), FAKE, ctypes.byref(no_r), FAKE, None) == 1
+    assert lib.basiskv_score_pages(ctypes.byref(d_rf), FAKE, ctypes.byref(no_z), FAKE, None) == 1
+    # a workspace too small: the routing-first call gets past the pool checks to the workspace one
+    assert lib.basiskv_route_pages(ctypes.byref(d_rf), FAKE, FAKE, FAKE, ctypes.byref(no_r), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 4
+    assert lib.basiskv_route_pages(ctypes.byref(d_sep), FAKE, FAKE, FAKE, ctypes.byref(no_r), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 1
+
+
+@needs_lib
 def test_unsupported_variant_is_reported_before_launch():
     lib = api.lib()
     # group size 3 has no scoring / attention variant
