@@ -53,9 +53,11 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // pages), each lane issuing NZ + NR 16-byte loads (its token's chunks of the
 // latent and residual pages).  With the chunk-major page layout those loads
 // are page_size * 16 contiguous bytes per chunk, i.e. fully coalesced.  The
-// projected queries are wave-uniform and are read through the scalar cache,
-// so every FMA takes one scalar and one vector operand.  Page maxima are
-// butterfly reductions over the page's lanes.  A workgroup is four such
+// logits of bf16 and E4M3 pages for groups of 4 and 8 heads run on the matrix
+// cores (MF below: G x (r_b + r_q) multiply-adds per token were the launch's
+// limit for 8-head groups); float32 pages and groups of 1 or 2 heads use FMAs
+// whose wave-uniform query operand comes through the scalar cache.  Page
+// maxima are butterfly reductions over the page's lanes.  A workgroup is four such
 // steps: many short workgroups keep more loads in flight than a few long
 // ones walking several steps each.  With STREAM the page loads are marked
 // non-temporal: the launch streams the pages once, and on MI355X such loads
@@ -71,13 +73,29 @@ struct ScoreArgs {
   PoolGeom geom;  // chunk positions of the latent and residual pages
 };
 
-template <typename T, int G, int NZ, int NR, bool STREAM>
+typedef short route_s4 __attribute__((ext_vector_type(4)));
+typedef float route_f4 __attribute__((ext_vector_type(4)));
+
+// MF: the logits on the matrix cores (bf16 and E4M3 pages, groups of 4 or 8
+// heads).  v_mfma_f32_4x4x4bf16_1k runs 16 independent 4x4x4 products; in
+// each, lane 4 j + i supplies 4 dims of head i's projected query (A) and 4
+// dims of its own token (B), and receives its token's logits for the 4 heads
+// of the quad -- the one-token-per-lane layout is kept.  The float32
+// projected queries enter as two bf16 terms, hi = bf16(q) and lo = bf16(q -
+// hi) (about 16 significant bits); every product is exact and the sums are
+// float32.  The query operands are staged in LDS once per workgroup.
+template <typename T, int G, int NZ, int NR, bool STREAM, bool MF>
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const float *__restrict__ q_proj, const T *__restrict__ zpool, const T *__restrict__ rpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     float *__restrict__ scores, ScoreArgs a) {
   constexpr int CE = Elem<T>::CE;
   constexpr int W = (NZ + NR) * CE;  // r_b + r_q
+  constexpr int QG = MF ? G / 4 : 1;  // head quads
+  constexpr int NST = W / 4;          // 4-dim steps
+  static_assert(!MF || (G % 4 == 0 && sizeof(T) <= 2), "matrix-core logits: bf16/E4M3, G % 4 == 0");
+  // [quad][step][head in quad]: {hi 4 x bf16, lo 4 x bf16}
+  __shared__ __align__(16) uint4 qf[MF ? QG * NST * 4 : 1];
   const int work = xcd_work_index(a.padded);
   if (work >= a.total) return;
   const int bg = work / a.chunks_per_bg;
@@ -101,6 +119,20 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int64_t page_z_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
   const int64_t page_r_bytes = (int64_t)a.geom.r_page_chunks * a.page_size * 16;
 
+  if constexpr (MF) {
+    for (int i = threadIdx.x; i < QG * NST * 4; i += blockDim.x) {
+      const int hq = i & 3, st = (i >> 2) % NST, qd = i / (NST * 4);
+      const float4 v = *reinterpret_cast<const float4 *>(qp + (qd * 4 + hq) * W + st * 4);
+      const uint32_t h01 = f32x2_to_bf16x2(v.x, v.y), h23 = f32x2_to_bf16x2(v.z, v.w);
+      const uint32_t l01 = f32x2_to_bf16x2(v.x - __uint_as_float(h01 << 16),
+                                           v.y - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = f32x2_to_bf16x2(v.z - __uint_as_float(h23 << 16),
+                                           v.w - __uint_as_float(h23 & 0xffff0000u));
+      qf[i] = make_uint4(h01, h23, l01, l23);
+    }
+    __syncthreads();
+  }
+
   if (const int step = wave; step < n_steps) {
     const int p = p_begin + step * ppi + (lane >> a.log2_page);
     const bool in_range = p < p_end;
@@ -109,7 +141,62 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     if (in_range && p < NP) phys = bt[p];
     const bool valid = in_range && p < NP && tok < L && phys >= 0 && phys < a.num_phys;
     float best = -INFINITY;
-    if (valid) {
+    if constexpr (MF) {
+      // every lane joins the matrix instructions; one without a valid token
+      // scores zeros and is masked
+      uint4 cz[NZ], cr[NR];
+#pragma unroll
+      for (int c = 0; c < NZ; ++c) cz[c] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int c = 0; c < NR; ++c) cr[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (valid) {
+        const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
+        const int64_t roff =
+            (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
+#pragma unroll
+        for (int c = 0; c < NZ; ++c)
+          cz[c] = load_page_chunk<STREAM>(zpool, zoff + (int64_t)c * a.page_size * 16);
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+          cr[c] = load_page_chunk<STREAM>(rpool, roff + (int64_t)c * a.page_size * 16);
+      }
+      route_f4 sc[QG];
+#pragma unroll
+      for (int qd = 0; qd < QG; ++qd) sc[qd] = route_f4{0.f, 0.f, 0.f, 0.f};
+      const int hq = lane & 3;
+      // 8 bf16 dims (one uint4) starting at 4-dim step st0
+      auto mma8 = [&](const uint4 &k8, int st0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const route_s4 kv = __builtin_bit_cast(
+              route_s4, hh ? make_uint2(k8.z, k8.w) : make_uint2(k8.x, k8.y));
+#pragma unroll
+          for (int qd = 0; qd < QG; ++qd) {
+            const uint4 qv = qf[(qd * NST + st0 + hh) * 4 + hq];
+            sc[qd] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                __builtin_bit_cast(route_s4, make_uint2(qv.x, qv.y)), kv, sc[qd], 0, 0, 0);
+            sc[qd] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                __builtin_bit_cast(route_s4, make_uint2(qv.z, qv.w)), kv, sc[qd], 0, 0, 0);
+          }
+        }
+      };
+      auto mma_chunk = [&](const uint4 &ch, int dim0) {
+        if constexpr (sizeof(T) == 1) {  // 16 E4M3 codes: widened to bf16 (exact)
+          mma8(fp8x8_to_bf16x8(ch.x, ch.y), dim0 / 4);
+          mma8(fp8x8_to_bf16x8(ch.z, ch.w), dim0 / 4 + 2);
+        } else {
+          mma8(ch, dim0 / 4);
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < NZ; ++c) mma_chunk(cz[c], c * CE);
+#pragma unroll
+      for (int c = 0; c < NR; ++c) mma_chunk(cr[c], NZ * CE + c * CE);
+      if (valid) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) best = fmaxf(best, sc[h / 4][h % 4]);
+      }
+    } else if (valid) {
       const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
       const int64_t roff =
           (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
@@ -173,14 +260,24 @@ struct ScoreVariant {
   const void *fn, *fn_nt;  // ordinary loads; non-temporal loads (null: not built)
 };
 
+#ifndef BKV_ROUTE_MFMA_MIN_G
+#define BKV_ROUTE_MFMA_MIN_G 4
+#endif
+// groups this wide (of 2-byte or 1-byte pages) take the matrix-core logits
+template <typename T, int G>
+constexpr bool route_mfma() {
+  return sizeof(T) <= 2 && G % 4 == 0 && G >= BKV_ROUTE_MFMA_MIN_G;
+}
+
 #define BKV_SCORE(T, DT, G, RB, RQ)                                                                  \
   {DT, G, RB, RQ,                                                                                     \
-   reinterpret_cast<const void *>(                                                                    \
-       &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE, false>),                      \
+   reinterpret_cast<const void *>(&route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE,   \
+                                                     false, route_mfma<T, G>()>),                     \
    ((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks                                                    \
        ? reinterpret_cast<const void *>(                                                              \
              &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE,                         \
-                                (((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks)>)                   \
+                                (((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks),                    \
+                                route_mfma<T, G>()>)                                                  \
        : nullptr}
 
 #define BKV_SCORE_G(T, DT, RB, RQ) \
