@@ -253,7 +253,10 @@ hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const 
   return hipGetLastError();
 }
 
-constexpr int kStreamMinChunks = 8;  // chunk loads per lane that the non-temporal form needs
+#ifndef BKV_STREAM_MIN_CHUNKS
+#define BKV_STREAM_MIN_CHUNKS 8
+#endif
+constexpr int kStreamMinChunks = BKV_STREAM_MIN_CHUNKS;  // chunk loads per lane the non-temporal form needs
 
 struct ScoreVariant {
   int dtype, G, rb, rq;
