@@ -15,8 +15,10 @@
 // not a bit field but one of 256 equal-width buckets of the score range
 // [min, max]: a bucket index is a monotone function of the score, so the k-th
 // largest key lies in one bucket T, every key of a higher bucket is taken and
-// the search goes on over T's keys only, from the highest bit in which they
-// differ.  (The leading bits of a row's keys are sign and exponent: as a
+// the search goes on over T's keys only: while they are at most 1024, each is
+// ranked against the others in LDS (the k-th largest is the key with fewer
+// than the remaining rank above it and at least that many at or above it),
+// otherwise by bit digits from the highest bit in which they differ.  (The leading bits of a row's keys are sign and exponent: as a
 // first digit they fall in a handful of bins -- most keys in one, its LDS
 // atomics serialised -- when a row holds scores of both signs.  On rows held
 // by four wavefronts the extra phase measured slower.)  Rows whose range is
@@ -89,6 +91,12 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
   constexpr bool kRadix = NWV >= kTopkRadixWaves;
   __shared__ int hist[kRadix ? 256 : 1];
   __shared__ int found[kRadix ? 3 : 1];
+  // bucket rows: bucket T's keys, ranked directly when they are few
+  constexpr bool kBucket = NWV >= kTopkBucketWaves;
+  constexpr int kMaxCand = 1024;
+  __shared__ uint32_t cand[kBucket ? kMaxCand : 1];
+  __shared__ int n_cand;
+  __shared__ uint32_t tau_found;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int base = wave * 64 * kpt + lane;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -169,6 +177,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       const float scale = 256.f / range;
       auto bucket = [&](float x) { return min(255, (int)((x - smin) * scale)); };
       for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      if (tid == 0) n_cand = 0;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
@@ -177,14 +186,16 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       find_bin();
       const int T = found[0];
       krem -= found[1];
-      const bool whole = found[2] == krem;  // every key of bucket T is taken
-      // bucket T's keys: the rest of the search, from the highest bit they differ in
+      // bucket T's keys: gathered into cand[] (while they fit), and their
+      // largest and smallest for the bit digits otherwise
       uint32_t mx = 0u, mn = ~0u;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         if (((live >> j) & 1u) && bucket(v[j]) == T) {
           mx = max(mx, key[j]);
           mn = min(mn, key[j]);
+          const int pos = atomicAdd(&n_cand, 1);
+          if (pos < kMaxCand) cand[pos] = key[j];
         } else {
           live &= ~(1u << j);
         }
@@ -195,19 +206,39 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
         xch[1][wave][1] = (int)mn;
       }
       __syncthreads();
-      mx = 0u;
-      mn = ~0u;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) {
-        mx = max(mx, (uint32_t)xch[1][w][0]);
-        mn = min(mn, (uint32_t)xch[1][w][1]);
-      }
-      const uint32_t d2 = mx ^ mn;
-      hi = d2 ? 31 - __clz(d2) : -1;
-      tau = hi < 0 ? mx : hi == 31 ? 0u : mx & ~((2u << hi) - 1u);
-      if (whole) {  // the k-th largest key is the bucket's least
-        tau = mn;
+      const int nc = n_cand;
+      if (nc <= kMaxCand) {
+        // tau is the krem-th largest of the nc candidates: the key with fewer
+        // than krem candidates above it and at least krem at or above it (any
+        // thread holding that value writes it)
+        for (int i = tid; i < nc; i += NT) {
+          const uint32_t ki = cand[i];
+          int gt = 0, ge = 0;
+          for (int j2 = 0; j2 < nc; ++j2) {
+            const uint32_t kj = cand[j2];
+            gt += kj > ki;
+            ge += kj >= ki;
+          }
+          if (gt < krem && krem <= ge) tau_found = ki;
+        }
+        __syncthreads();
+        tau = tau_found;
         hi = -1;
+      } else {
+        mx = 0u;
+        mn = ~0u;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+          mx = max(mx, (uint32_t)xch[1][w][0]);
+          mn = min(mn, (uint32_t)xch[1][w][1]);
+        }
+        const uint32_t d2 = mx ^ mn;
+        hi = d2 ? 31 - __clz(d2) : -1;
+        tau = hi < 0 ? mx : hi == 31 ? 0u : mx & ~((2u << hi) - 1u);
+        if (found[2] == krem) {  // every key of bucket T is taken: tau is its least
+          tau = mn;
+          hi = -1;
+        }
       }
       // (found[] and hist are rewritten only after the next barrier)
     }
