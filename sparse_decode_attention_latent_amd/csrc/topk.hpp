@@ -116,6 +116,10 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       xch[0][wave][0] = (int)kmax;
       xch[0][wave][1] = (int)kmin;
     }
+    if constexpr (kRadix) {  // the first histogram's bins cleared under the same barrier
+      for (int i = threadIdx.x; i < 256; i += 64 * NWV) hist[i] = 0;
+      if (threadIdx.x == 0) n_cand = 0;
+    }
     __syncthreads();
     kmax = 0u;
     kmin = ~0u;
@@ -124,7 +128,9 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       kmax = max(kmax, (uint32_t)xch[0][w][0]);
       kmin = min(kmin, (uint32_t)xch[0][w][1]);
     }
-    __syncthreads();
+    // the bit search below rewrites xch at once; the digit search touches xch[0]
+    // again only in the compaction, barriers later
+    if constexpr (!kRadix) __syncthreads();
   }
   const uint32_t diff = kmax ^ kmin;
   const int top = diff ? 31 - __clz(diff) : -1;  // -1: every valid key is equal
@@ -169,6 +175,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       __syncthreads();
     };
     int hi = top;
+    bool hist_clear = true;  // hist holds zeros
     // ---- first digit: equal-width buckets of the score range ----
     const float smax = key_value(kmax), smin = key_value(kmin);
     const float range = smax - smin;
@@ -176,14 +183,12 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
         range > 0.f) {  // smin, smax finite too
       const float scale = 256.f / range;
       auto bucket = [&](float x) { return min(255, (int)((x - smin) * scale)); };
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
-      if (tid == 0) n_cand = 0;
-      __syncthreads();
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
         if ((live >> j) & 1u) atomicAdd(&hist[bucket(v[j])], 1);
       __syncthreads();
       find_bin();
+      hist_clear = false;
       const int T = found[0];
       krem -= found[1];
       // bucket T's keys: gathered into cand[] (while they fit), and their
@@ -200,13 +205,8 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
           live &= ~(1u << j);
         }
       }
-      wave_max_min_u32(mx, mn);
-      if (lane == 0) {
-        xch[1][wave][0] = (int)mx;
-        xch[1][wave][1] = (int)mn;
-      }
       __syncthreads();
-      const int nc = n_cand;
+      const int nc = n_cand;  // uniform
       if (nc <= kMaxCand) {
         // tau is the krem-th largest of the nc candidates: the key with fewer
         // than krem candidates above it and at least krem at or above it (any
@@ -225,6 +225,12 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
         tau = tau_found;
         hi = -1;
       } else {
+        wave_max_min_u32(mx, mn);
+        if (lane == 0) {
+          xch[1][wave][0] = (int)mx;
+          xch[1][wave][1] = (int)mn;
+        }
+        __syncthreads();
         mx = 0u;
         mn = ~0u;
 #pragma unroll
@@ -245,8 +251,13 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
     for (; hi >= 0;) {
       const int lo = hi >= 7 ? hi - 7 : 0;
       const uint32_t dmask = (2u << (hi - lo)) - 1u;
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
-      __syncthreads();
+      // (after find_bin's barrier wavefront 0 has read the previous counts, and
+      // found[] is rewritten only after the two barriers below)
+      if (!hist_clear) {
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+      }
+      hist_clear = false;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const bool match = hi == 31 || (key[j] >> (hi + 1)) == (tau >> (hi + 1));
@@ -259,7 +270,6 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
       tau |= (uint32_t)digit << lo;
       if (found[2] == krem) break;  // every key sharing these bits is taken
       hi = lo - 1;
-      __syncthreads();  // found[] and hist are rewritten next pass
     }
   } else {
   // ---- tau, bit by bit (keys past the row are 0 and reach no candidate) ----
@@ -293,7 +303,9 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
         eq_w += __popcll(__ballot(key[j] == tau));
       }
     }
-    __syncthreads();
+    // the last reads of xch[0] (the bit search's, or the range exchange's when
+    // every key is equal and the digit search took no barrier) are complete
+    if (!kRadix || top < 0) __syncthreads();
     if (lane == 0) {
       xch[0][wave][0] = gt_w;
       xch[0][wave][1] = eq_w;
