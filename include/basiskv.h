@@ -143,7 +143,10 @@ size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t top_k);
  *   the Key itself is stored in the k pool (copied; rounded to E4M3 with
  *   BASISKV_BF16_FP8_E4M3).  z_s is the latent as stored (rounded to the cache
  *   format).  GEMMs run on MFMA with float32 accumulation.
- * seq_lens are not read or changed.  Returns ERR_SHAPE for n_tokens < 1. */
+ * seq_lens are not read or changed.  Returns ERR_SHAPE for n_tokens < 1.
+ * No workspace: each token's latent and residual are finished by one
+ * wavefront (the factors are staged in LDS once per workgroup), so nothing
+ * crosses workgroups.  Needs r_v and r_q multiples of 16 (MFMA output tiles). */
 int32_t basiskv_compress_prefill(const basiskv_dims *dims, const void *k, const void *v,
                                  const int32_t *start_pos, int32_t n_tokens, const void *A,
                                  const void *P, const void *E, const basiskv_cache *cache,
@@ -207,19 +210,38 @@ int32_t basiskv_sparse_attend(const basiskv_dims *dims, const void *q,
                               float scale, float *u, void *workspace, size_t workspace_bytes,
                               void *stream);
 
-/* (a5) Output reconstruction y = u M (Figure 1: the complete output is rebuilt
- * from the latents; abstract: Value compression is tied to the output
- * projection).  MFMA GEMM with float32 accumulation; for bf16, u is split into
- * two bf16 terms (hi + lo) so no precision is lost before the product.
- *   u [batch][n_q_heads * r_v] float32;  M: hidden x K (K = n_q_heads * r_v)
- *   elements in the tiled layout written by basiskv_fuse_output_matrix;
- *   y [batch][hidden] out, in dtype (bf16 for BASISKV_BF16_FP8_E4M3).  Needs
- *   hidden % 16 == 0 and K % 32 == 0 (bf16 activations) or K % 16 == 0
- *   (float32), ERR_UNSUPPORTED otherwise.
- * batch must be <= 32 for bf16 activations and <= 64 for float32
- * (ERR_UNSUPPORTED). */
+/* (a5) Output reconstruction y = u M.  Figure 1 of the BasisKV pages: after
+ * the partitions exchange their latents, each one rebuilds the complete
+ * output from them; the abstract: Value compression is tied to the output
+ * projection, so the Value decoder is folded into it,
+ *   M = blockdiag_h(Bf_{h/G}) W_O,   the plain fused matrix [n_q_heads * r_v][hidden]
+ * (row k = h * r_v + i: latent dim i of query head h; column n: output feature).
+ * MFMA GEMM with float32 accumulation; for bf16, u is split into two bf16
+ * terms (hi + lo) so no precision is lost before the product.
+ *   u [batch][n_q_heads * r_v] float32;
+ *   M: the fused matrix in the library's MFMA-tiled layout, written once, at
+ *      set-up, by basiskv_pack_output_matrix (from a caller's plain matrix)
+ *      or basiskv_fuse_output_matrix (from Bf and W_O);
+ *   y [batch][hidden] out, in dtype (bf16 for BASISKV_BF16_FP8_E4M3).
+ * Needs hidden % 16 == 0 and K = n_q_heads * r_v a multiple of 32 (bf16
+ * activations) or 16 (float32), ERR_UNSUPPORTED otherwise.  Any batch.
+ * No workspace: every output column's sum over K is finished inside one
+ * workgroup (its wavefronts' partial tiles are added in LDS). */
 int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void *M, void *y,
                             void *stream);
+
+/* Set-up for (a5): the caller's plain fused matrix M_plain
+ * [n_q_heads * r_v][hidden] (dtype: float32, or bf16 for BASISKV_BF16 and
+ * BASISKV_BF16_FP8_E4M3; row k = h * r_v + i, column n = output feature, as
+ * documented at basiskv_reconstruct) copied into the tiled layout that
+ * basiskv_reconstruct and basiskv_decode_step read (see
+ * basiskv_fuse_output_matrix for the layout).  Pure data movement: the tiled
+ * matrix holds the same values bit for bit.  M_plain and M are device
+ * buffers of n_q_heads * r_v * hidden elements that must not overlap
+ * (ERR_SHAPE when they are the same pointer).  Same size requirements as
+ * basiskv_reconstruct. */
+int32_t basiskv_pack_output_matrix(const basiskv_dims *dims, const void *M_plain, void *M,
+                                   void *stream);
 
 /* A whole decode step of one layer in one call, with the same results as
  *   basiskv_compress_prefill(k_new, v_new, start_pos, n_tokens = 1),
@@ -230,7 +252,7 @@ int32_t basiskv_reconstruct(const basiskv_dims *dims, const float *u, const void
  *     sequence, written at position start_pos[b] (device int32 [batch]);
  *     seq_lens must already count it.
  *   q, P, Q, A, E, M, top_k, scale, page_scores, sel, u, y: as in the calls
- *     above.  Needs r_v, r_q <= 128 and the batch limit of basiskv_reconstruct.
+ *     above.  Needs r_v, r_q <= 128.
  *   workspace: see basiskv_workspace_bytes. */
 int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void *k_new,
                             const void *v_new, const int32_t *start_pos, const void *A,

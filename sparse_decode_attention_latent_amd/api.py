@@ -22,8 +22,8 @@ EXPORTED = (
     "basiskv_status_string", "basiskv_workspace_bytes", "basiskv_compress_prefill",
     "basiskv_project_queries", "basiskv_score_pages", "basiskv_select_pages",
     "basiskv_route_pages", "basiskv_sparse_attend", "basiskv_reconstruct",
-    "basiskv_decode_step", "basiskv_fuse_output_matrix", "basiskv_dense_workspace_bytes",
-    "basiskv_dense_attend",
+    "basiskv_decode_step", "basiskv_fuse_output_matrix", "basiskv_pack_output_matrix",
+    "basiskv_dense_workspace_bytes", "basiskv_dense_attend",
 )
 
 
@@ -71,6 +71,7 @@ def _lib():
             "basiskv_decode_step": (I32, [DP, P, P, P, P, P, P, P, P, P, CP, I32, ctypes.c_float,
                                           P, P, P, P, P, SZ, P]),
             "basiskv_fuse_output_matrix": (I32, [DP, P, P, P, P]),
+            "basiskv_pack_output_matrix": (I32, [DP, P, P, P]),
             "basiskv_dense_workspace_bytes": (SZ, [DP]),
             "basiskv_dense_attend": (I32, [DP, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
         }
@@ -184,6 +185,13 @@ def fuse_output_matrix(dims, Bf, W_O, M, stream=None):
     _check(_lib().basiskv_fuse_output_matrix(ctypes.byref(dims), _ptr(Bf), _ptr(W_O), _ptr(M),
                                              _stream(stream)),
            "basiskv_fuse_output_matrix")
+
+
+def pack_output_matrix(dims, M_plain, M, stream=None):
+    """A plain fused matrix [n_q_heads * r_v][hidden] into the tiled layout."""
+    _check(_lib().basiskv_pack_output_matrix(ctypes.byref(dims), _ptr(M_plain), _ptr(M),
+                                             _stream(stream)),
+           "basiskv_pack_output_matrix")
 
 
 def dense_workspace_bytes(dims):

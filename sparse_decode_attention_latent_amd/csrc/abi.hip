@@ -220,7 +220,6 @@ int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M
   int32_t st = check_dims(d);
   if (st) return st;
   if (!u || !M || !y) return BASISKV_ERR_NULL;
-  if (d->batch > (bkv_host::act_bf16(*d) ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   return launched(bkv_host::launch_reconstruct(*d, u, nullptr, M, y, as_stream(stream)));
 }
@@ -241,7 +240,6 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (d->r_v > bkv::kHeadDim || d->r_q > bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
   if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
     return BASISKV_ERR_UNSUPPORTED;
-  if (d->batch > (bkv_host::act_bf16(*d) ? 32 : 64)) return BASISKV_ERR_UNSUPPORTED;
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
   if (!ws || ws_bytes < scratch_offset(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;
@@ -301,6 +299,16 @@ int32_t basiskv_dense_attend(const basiskv_dims *d, const void *q, const void *k
                                          as_stream(stream), &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
   return launched(e);
+}
+
+int32_t basiskv_pack_output_matrix(const basiskv_dims *d, const void *M_plain, void *M,
+                                   void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!M_plain || !M) return BASISKV_ERR_NULL;
+  if (M_plain == M) return BASISKV_ERR_SHAPE;  // not in place
+  if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
+  return launched(bkv_host::launch_pack_output(*d, M_plain, M, as_stream(stream)));
 }
 
 int32_t basiskv_fuse_output_matrix(const basiskv_dims *d, const void *Bf, const void *W_O, void *M,

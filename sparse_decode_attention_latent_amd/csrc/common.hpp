@@ -343,6 +343,7 @@ hipError_t launch_reconstruct(const basiskv_dims &d, const float *u, const uint1
                               const void *M, void *y, hipStream_t s);
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
                        hipStream_t s);
+hipError_t launch_pack_output(const basiskv_dims &d, const void *M_plain, void *M, hipStream_t s);
 hipError_t launch_append(const basiskv_dims &d, const void *k, const void *v,
                          const int32_t *start_pos, int32_t n_tokens, const void *A, const void *P,
                          const void *E, const basiskv_cache &c, hipStream_t s);

@@ -71,8 +71,9 @@ __host__ __device__ __forceinline__ int64_t mtile_index(int n, int k, int K) {
 
 // ---------------------------------------------------------------------------
 // (a5) y[b][n] = sum_k u[b][k] M[n][k],  K = n_q * r_v, M in the tiled layout.
-// One workgroup of 8 wavefronts per 16 output columns; the wavefronts split K
-// and their 16x16 tiles are summed through LDS.  bf16: the A rows are
+// One workgroup of 8 wavefronts per 16 output columns and group of RT row
+// tiles (blockIdx.y); the wavefronts split K and their 16x16 tiles are summed
+// through LDS.  bf16: the A rows are
 // [hi(u) of 8 sequences ; lo(u) of the same 8], so one MFMA carries both
 // terms and y = C[b] + C[b + 8].  float32: 16 sequences per row tile.
 // ---------------------------------------------------------------------------
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
   __shared__ float red[kReconWaves][RT][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
+  const int rt0 = blockIdx.y * RT;  // this workgroup's first row tile
   const int i = lane & 15, qg = lane >> 4;
   const int n_steps = (K + MF::KS - 1) / MF::KS;
   floatx4 acc[RT];
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           araw[uu][rt] = make_uint4(0, 0, 0, 0);
-          if (ks < n_steps && rt * ROWS + (i & 7) < batch)
-            araw[uu][rt] = reinterpret_cast<const uint4 *>(u_tiles)[((int64_t)rt * n_steps + ks) * 64 + lane];
+          if (ks < n_steps && (rt0 + rt) * ROWS + (i & 7) < batch)
+            araw[uu][rt] = reinterpret_cast<const uint4 *>(u_tiles)[((int64_t)(rt0 + rt) * n_steps + ks) * 64 + lane];
         }
       }
 #pragma unroll
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
           braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int b = rt * ROWS + (i & 7);
+          const int b = (rt0 + rt) * ROWS + (i & 7);
           ux[uu][rt][0] = ux[uu][rt][1] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (b < batch && k < K) {
             const float4 *up = reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
           bq[uu] = reinterpret_cast<const float4 *>(M)[((int64_t)blockIdx.x * n_quads + kq) * 64 + lane];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int b = rt * ROWS + i;
+          const int b = (rt0 + rt) * ROWS + i;
           aq[uu][rt] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (b < batch && k < K) aq[uu][rt] = *reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
         }
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
   for (int o = threadIdx.x; o < RT * ROWS * 16; o += blockDim.x) {
     const int rt = o / (ROWS * 16), rem = o % (ROWS * 16);
     const int br = rem / 16, col = rem % 16;
-    const int b = rt * ROWS + br;
+    const int b = (rt0 + rt) * ROWS + br;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < kReconWaves; ++w) {
@@ -233,6 +235,35 @@ __global__ __launch_bounds__(256) void fuse_kernel(const T *__restrict__ Bf,
     float s = 0.f;
     for (int d = 0; d < kHeadDim; ++d) s = fmaf(to_f32(brow[d]), wt[d][c], s);
     if (n0 + c < N) M[mtile_index<T>(n0 + c, h * rv + i, K)] = from_f32<T>(s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Set-up: a caller's plain fused matrix Mp [K][N] (row k = h * r_v + i, the
+// latent slot; column n, the output feature) -> the tiled layout above.
+// grid (ceil(N/64), ceil(K/64)), 256 threads: a 64 x 64 block is read row by
+// row (coalesced) into LDS and written out as whole 16-byte tile chunks.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const T *__restrict__ Mp, T *__restrict__ Mt,
+                                                   int K, int N) {
+  constexpr int KPL = 16 / (int)sizeof(T);
+  __shared__ T tile[64][64 + KPL];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  for (int o = threadIdx.x; o < 64 * 64; o += blockDim.x) {
+    const int kk = o / 64, nn = o % 64;
+    tile[kk][nn] = (k0 + kk < K && n0 + nn < N) ? Mp[(int64_t)(k0 + kk) * N + n0 + nn] : T(0);
+  }
+  __syncthreads();
+  // thread -> (column nn, run of KPL consecutive k): one 16-byte chunk of the tiled matrix
+  for (int o = threadIdx.x; o < 64 * (64 / KPL); o += blockDim.x) {
+    const int nn = o / (64 / KPL), kk = (o % (64 / KPL)) * KPL;
+    const int n = n0 + nn, k = k0 + kk;
+    if (n >= N || k >= K) continue;  // K % KPL == 0: a chunk is whole or absent
+    T v[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) v[j] = tile[kk + j][nn];
+    *reinterpret_cast<uint4 *>(Mt + mtile_index<T>(n, k, K)) = *reinterpret_cast<const uint4 *>(v);
   }
 }
 
@@ -553,7 +584,8 @@ static hipError_t recon_t(const basiskv_dims &d, const float *u, const uint16_t 
   const int rows = sizeof(T) == 2 ? 8 : 16;
   const int rt = (d.batch + rows - 1) / rows;
   const int K = d.n_q_heads * d.r_v, N = d.hidden;
-  dim3 grid((N + 15) / 16), block(512);
+  // up to 4 row tiles per workgroup; larger batches take more row-tile groups
+  dim3 grid((N + 15) / 16, rt <= 4 ? 1 : (rt + 3) / 4), block(512);
   const T *Mt = (const T *)M;
   T *yt = (T *)y;
 #define BKV_RECON(RTV, UTV)                                                                    \
@@ -589,6 +621,18 @@ static hipError_t fuse_t(const basiskv_dims &d, const void *Bf, const void *W_O,
 hipError_t launch_fuse(const basiskv_dims &d, const void *Bf, const void *W_O, void *M,
                        hipStream_t s) {
   return act_bf16(d) ? fuse_t<uint16_t>(d, Bf, W_O, M, s) : fuse_t<float>(d, Bf, W_O, M, s);
+}
+
+template <typename T>
+static hipError_t pack_t(const basiskv_dims &d, const void *Mp, void *M, hipStream_t s) {
+  const int K = d.n_q_heads * d.r_v, N = d.hidden;
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((N + 63) / 64, (K + 63) / 64), dim3(256), 0, s,
+                     (const T *)Mp, (T *)M, K, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_output(const basiskv_dims &d, const void *M_plain, void *M, hipStream_t s) {
+  return act_bf16(d) ? pack_t<uint16_t>(d, M_plain, M, s) : pack_t<float>(d, M_plain, M, s);
 }
 
 #ifndef BKV_COMPRESS_WGS
@@ -631,13 +675,16 @@ static hipError_t compress_t(const basiskv_dims &d, const void *k, const void *v
   return hipGetLastError();
 }
 
-// Few rows per head (the decode append): matrix-vector kernel; otherwise MFMA.
+// One token per sequence (the decode append, at any batch: the same kernel
+// body as the one-call decode step's, so both give the same bits) or few rows
+// per head: matrix-vector kernel; otherwise MFMA.
 constexpr int kAppendMaxRows = 64;
 
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s) {
-  if ((int64_t)d.batch * n_tokens <= kAppendMaxRows && d.r_v <= kHeadDim && d.r_q <= kHeadDim)
+  const bool few = n_tokens == 1 || (int64_t)d.batch * n_tokens <= kAppendMaxRows;
+  if (few && d.r_v <= kHeadDim && d.r_q <= kHeadDim)
     return launch_append(d, k, v, start_pos, n_tokens, A, P, E, c, s);
   if (cache_fp8(d))
     return compress_t<uint16_t, uint8_t>(d, k, v, start_pos, n_tokens, A, P, E, c, s);

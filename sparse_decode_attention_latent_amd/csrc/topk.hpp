@@ -18,13 +18,14 @@
 // the search goes on over T's keys only: while they are at most 1024, each is
 // ranked against the others in LDS (the k-th largest is the key with fewer
 // than the remaining rank above it and at least that many at or above it),
-// otherwise by bit digits from the highest bit in which they differ.  (The leading bits of a row's keys are sign and exponent: as a
-// first digit they fall in a handful of bins -- most keys in one, its LDS
-// atomics serialised -- when a row holds scores of both signs.  On rows held
-// by four wavefronts the extra phase measured slower.)  Rows whose range is
-// not a finite positive number start with the bit digits.  Either
-// way the search stops
-// as soon as exactly k keys share the decided bits (the top-k set is then
+// otherwise by bit digits from the highest bit in which they differ.  (The
+// leading bits of a row's keys are sign and exponent: as a first digit they
+// fall in a handful of bins -- most keys in one, its LDS atomics serialised --
+// when a row holds scores of both signs.  On rows held by four wavefronts the
+// extra phase measured slower.)  Rows whose range is not a finite positive
+// number, or so small that 256 / range overflows, start with the bit digits.
+// Either way the search stops as soon as exactly k keys share the decided
+// bits (the top-k set is then
 // decided, whatever the lower bits of the k-th key).  The compaction
 // then hands out, in page order, every page whose key exceeds tau and the
 // lowest-index pages equal to it; positions come from ballot popcounts.
@@ -179,9 +180,12 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int kpt, int NP,
     // ---- first digit: equal-width buckets of the score range ----
     const float smax = key_value(kmax), smin = key_value(kmin);
     const float range = smax - smin;
+    // the bucket index (x - smin) * 256 / range needs a finite, positive range
+    // whose reciprocal scale is finite too (a range below 256 / FLT_MAX, about
+    // 7.5e-37, would give an infinite scale): other rows take the bit digits
+    const float scale = range > 0.f ? 256.f / range : 0.f;
     if (NWV >= kTopkBucketWaves && top >= 0 && __builtin_isfinite(range) &&
-        range > 0.f) {  // smin, smax finite too
-      const float scale = 256.f / range;
+        range > 0.f && __builtin_isfinite(scale)) {  // smin, smax finite too
       auto bucket = [&](float x) { return min(255, (int)((x - smin) * scale)); };
 #pragma unroll
       for (int j = 0; j < KPT; ++j)

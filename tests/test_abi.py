@@ -141,9 +141,27 @@ def test_null_and_shape_and_workspace_errors():
     assert step(d, top_k=0) == 2
     assert step(d, ws_bytes=64) == 4
     assert step(d, ws=None) == 4
-    assert step(dims_of(WORKLOADS[2], batch=40)) == 3
+    # no batch limit: a batch of 40 gets past the size checks to the workspace check
+    assert step(dims_of(WORKLOADS[2], batch=40), ws_bytes=64) == 4
     big = dims_of(WORKLOADS[2], batch=40)
-    assert lib.basiskv_reconstruct(ctypes.byref(big), FAKE, FAKE, FAKE, None) == 3
+    assert lib.basiskv_reconstruct(ctypes.byref(big), None, FAKE, FAKE, None) == 1
+
+
+@needs_lib
+def test_pack_output_matrix_validation():
+    """basiskv_pack_output_matrix: null pointers, an in-place call, and sizes
+    the tiled layout cannot hold are refused before any launch."""
+    lib = api.lib()
+    d = dims_of(WORKLOADS[2])
+    assert lib.basiskv_pack_output_matrix(ctypes.byref(d), None, FAKE, None) == 1
+    assert lib.basiskv_pack_output_matrix(ctypes.byref(d), FAKE, None, None) == 1
+    assert lib.basiskv_pack_output_matrix(None, FAKE, FAKE, None) == 1
+    assert lib.basiskv_pack_output_matrix(ctypes.byref(d), FAKE, FAKE, None) == 2  # in place
+    other = ctypes.c_void_p(0x2000)
+    assert lib.basiskv_pack_output_matrix(ctypes.byref(dims_of(WORKLOADS[2], hidden=4100)), FAKE,
+                                          other, None) == 3   # hidden % 16 != 0
+    assert lib.basiskv_pack_output_matrix(ctypes.byref(dims_of(WORKLOADS[2], n_q_heads=3, n_kv_heads=3,
+                                                               r_v=8, r_b=8)), FAKE, other, None) == 3  # K = 24
 
 
 @needs_lib
