@@ -261,6 +261,34 @@ int32_t basiskv_decode_step(const basiskv_dims *dims, const void *q, const void 
                             float *page_scores, int32_t *sel, float *u, void *y,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the library's own scratch, the device memory that
+ * basiskv_decode_step_static uses in place of a workspace. */
+#define BASISKV_STATIC_SCRATCH_BYTES (8u << 20)
+size_t basiskv_static_scratch_bytes(void);
+
+/* basiskv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same launches and results as
+ * basiskv_decode_step, bit for bit; the workspace is a file-scope device
+ * array of the library, BASISKV_STATIC_SCRATCH_BYTES (8 MiB) per GPU, held
+ * from the first call on that GPU until the process ends; its device address
+ * is looked up once per device (hipGetSymbolAddress) on the first call made
+ * with that device current.  Nothing is allocated or freed.
+ * Returns ERR_WORKSPACE when basiskv_workspace_bytes(dims, top_k) exceeds
+ * BASISKV_STATIC_SCRATCH_BYTES (about batch 256 at the 8B shape with r_v 96),
+ * and ERR_LAUNCH if the device address cannot be obtained; all other
+ * arguments and checks as for basiskv_decode_step.  Every call on one GPU
+ * shares that GPU's array and finds what the previous call left in it (the
+ * step zeroes what must start at zero itself): calls that overlap on one GPU
+ * -- on different streams, or from different host threads -- race and must
+ * not be made. */
+int32_t basiskv_decode_step_static(const basiskv_dims *dims, const void *q, const void *k_new,
+                                   const void *v_new, const int32_t *start_pos, const void *A,
+                                   const void *P, const void *Q, const void *E, const void *M,
+                                   const basiskv_cache *cache, int32_t top_k, float scale,
+                                   float *page_scores, int32_t *sel, float *u, void *y,
+                                   void *stream);
+
 /* Dense decode attention over every page, the baseline the pages compare
  * the method against (sparse decoding latency, Table 3: full-context Key and
  * Value reads).  For each query head h of KV head g:

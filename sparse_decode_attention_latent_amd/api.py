@@ -23,7 +23,8 @@ EXPORTED = (
     "basiskv_project_queries", "basiskv_score_pages", "basiskv_select_pages",
     "basiskv_route_pages", "basiskv_sparse_attend", "basiskv_reconstruct",
     "basiskv_decode_step", "basiskv_fuse_output_matrix", "basiskv_pack_output_matrix",
-    "basiskv_dense_workspace_bytes", "basiskv_dense_attend",
+    "basiskv_dense_workspace_bytes", "basiskv_dense_attend", "basiskv_static_scratch_bytes",
+    "basiskv_decode_step_static",
 )
 
 
@@ -74,6 +75,9 @@ def _lib():
             "basiskv_pack_output_matrix": (I32, [DP, P, P, P]),
             "basiskv_dense_workspace_bytes": (SZ, [DP]),
             "basiskv_dense_attend": (I32, [DP, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
+            "basiskv_static_scratch_bytes": (SZ, []),
+            "basiskv_decode_step_static": (I32, [DP, P, P, P, P, P, P, P, P, P, CP, I32,
+                                                 ctypes.c_float, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -206,3 +210,18 @@ def dense_attend(dims, q, k_pages, v_pages, block_table, seq_lens, scale, o, wor
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(stream)),
            "basiskv_dense_attend")
+
+
+def static_scratch_bytes():
+    return int(_lib().basiskv_static_scratch_bytes())
+
+
+def decode_step_static(dims, q, k_new, v_new, start_pos, A, P, Q, E, M, cache, top_k, scale,
+                       page_scores, sel, u, y, stream=None):
+    """basiskv_decode_step with the library's own scratch (no workspace)."""
+    _check(_lib().basiskv_decode_step_static(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                             _ptr(start_pos), _ptr(A), _ptr(P), _ptr(Q), _ptr(E),
+                                             _ptr(M), ctypes.byref(cache), int(top_k), float(scale),
+                                             _ptr(page_scores), _ptr(sel), _ptr(u), _ptr(y),
+                                             _stream(stream)),
+           "basiskv_decode_step_static")

@@ -1,6 +1,7 @@
 // C ABI of libbasiskv: host-side validation, workspace sizing and dispatch.
 // Every entry point validates its arguments before enqueuing anything and
 // returns a basiskv_status; nothing here allocates, frees or synchronises.
+#include <mutex>
 #include <string.h>
 
 #include "common.hpp"
@@ -99,13 +100,39 @@ uint16_t *u_tiles(void *ws, const basiskv_dims &d) {
              ? reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + counter_bytes(d))
              : nullptr;
 }
-float *scratch(void *ws, const basiskv_dims &d) {
+float *scratch_area(void *ws, const basiskv_dims &d) {
   return reinterpret_cast<float *>(static_cast<char *>(ws) + scratch_offset(d));
 }
 
 int32_t launched(hipError_t e) { return e == hipSuccess ? BASISKV_OK : BASISKV_ERR_LAUNCH; }
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---- the no-allocation decode step's scratch ----
+// Device memory of the library itself (one copy per GPU, held until the
+// process ends) standing in for the caller's workspace.  In host code the
+// array's name is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = (size_t)BASISKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // per device, looked up on first use
+
+// Device address of `scratch` on the current device (looked up once per device).
+int32_t static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BASISKV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BASISKV_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BASISKV_OK;
+}
 
 }  // namespace
 
@@ -186,7 +213,7 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!ws || ws_bytes < scratch_offset(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
   if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
-  float *q_proj = scratch(ws, *d);
+  float *q_proj = scratch_area(ws, *d);
   hipStream_t s = as_stream(stream);
   bool unsupported = false;
   hipError_t e = bkv_host::launch_project(*d, q, P, Q, q_proj, s);
@@ -208,7 +235,7 @@ int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basisk
   if (!ws || ws_bytes < scratch_offset(*d) + partial_bytes(*d, top_k))
     return BASISKV_ERR_WORKSPACE;
   bool unsupported = false;
-  hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scratch(ws, *d),
+  hipError_t e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scratch_area(ws, *d),
                                          attend_counters(ws), nullptr, as_stream(stream),
                                          &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
@@ -224,12 +251,16 @@ int32_t basiskv_reconstruct(const basiskv_dims *d, const float *u, const void *M
   return launched(bkv_host::launch_reconstruct(*d, u, nullptr, M, y, as_stream(stream)));
 }
 
-int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
-                            const void *v_new, const int32_t *start_pos, const void *A,
-                            const void *P, const void *Q, const void *E, const void *M,
-                            const basiskv_cache *c, int32_t top_k, float scale,
-                            float *page_scores, int32_t *sel, float *u, void *y, void *ws,
-                            size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a decode step (no HIP call).
+int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
+                          const void *v_new, const int32_t *start_pos, const void *A,
+                          const void *P, const void *Q, const void *E, const void *M,
+                          const basiskv_cache *c, int32_t top_k, float *page_scores, int32_t *sel,
+                          float *u, void *y, const void *ws, size_t ws_bytes) {
   int32_t st = check_dims(d);
   if (st) return st;
   if (!q || !k_new || !v_new || !start_pos || !A || !P || !Q || !E || !M || !page_scores ||
@@ -243,12 +274,22 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
   if (!ws || ws_bytes < scratch_offset(*d) + (a > b ? a : b)) return BASISKV_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
-  float *scr = scratch(ws, *d);
+  return BASISKV_OK;
+}
+
+// The launches of a decode step, after check_decode_step.
+int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
+                           const void *v_new, const int32_t *start_pos, const void *A,
+                           const void *P, const void *Q, const void *E, const void *M,
+                           const basiskv_cache *c, int32_t top_k, float scale, float *page_scores,
+                           int32_t *sel, float *u, void *y, void *ws, hipStream_t s) {
+  float *scr = scratch_area(ws, *d);
   bool unsupported = false;
-  // (a0) + (a1) in one launch, then (a2), (a3), (a4), (a5)
-  if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr, s) !=
-      hipSuccess)
+  // (a0) + (a1) in one launch, which also clears the attention's merge
+  // counters; then (a2), (a3), (a4), (a5)
+  const int n_counters = (int)(counter_bytes(*d) / sizeof(int32_t));
+  if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr,
+                                     attend_counters(ws), n_counters, s) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
   hipError_t e = bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
@@ -259,6 +300,43 @@ int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_
                               &unsupported);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
   return launched(bkv_host::launch_reconstruct(*d, u, ut, M, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t basiskv_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
+                            const void *v_new, const int32_t *start_pos, const void *A,
+                            const void *P, const void *Q, const void *E, const void *M,
+                            const basiskv_cache *c, int32_t top_k, float scale,
+                            float *page_scores, int32_t *sel, float *u, void *y, void *ws,
+                            size_t ws_bytes, void *stream) {
+  const int32_t st = check_decode_step(d, q, k_new, v_new, start_pos, A, P, Q, E, M, c, top_k,
+                                       page_scores, sel, u, y, ws, ws_bytes);
+  if (st) return st;
+  return launch_decode_step(d, q, k_new, v_new, start_pos, A, P, Q, E, M, c, top_k, scale,
+                            page_scores, sel, u, y, ws, as_stream(stream));
+}
+
+size_t basiskv_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int32_t basiskv_decode_step_static(const basiskv_dims *d, const void *q, const void *k_new,
+                                   const void *v_new, const int32_t *start_pos, const void *A,
+                                   const void *P, const void *Q, const void *E, const void *M,
+                                   const basiskv_cache *c, int32_t top_k, float scale,
+                                   float *page_scores, int32_t *sel, float *u, void *y,
+                                   void *stream) {
+  // every host check first, against the scratch's size (a stand-in pointer:
+  // nothing is dereferenced or launched before the real address is known)
+  const void *stand_in = &kStaticScratchBytes;
+  int32_t st = check_decode_step(d, q, k_new, v_new, start_pos, A, P, Q, E, M, c, top_k,
+                                 page_scores, sel, u, y, stand_in, kStaticScratchBytes);
+  if (st) return st;
+  void *ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  return launch_decode_step(d, q, k_new, v_new, start_pos, A, P, Q, E, M, c, top_k, scale,
+                            page_scores, sel, u, y, ws, as_stream(stream));
 }
 
 // The dense baseline's sizes: the attention sums Values (head_dim wide) in the
@@ -295,7 +373,7 @@ int32_t basiskv_dense_attend(const basiskv_dims *d, const void *q, const void *k
   c.seq_lens = seq_lens;
   bool unsupported = false;
   hipError_t e = bkv_host::launch_attend(dd, q, c, nullptr, dd.max_pages_per_seq, scale, o,
-                                         scratch(ws, dd), attend_counters(ws), nullptr,
+                                         scratch_area(ws, dd), attend_counters(ws), nullptr,
                                          as_stream(stream), &unsupported);
   if (unsupported) return BASISKV_ERR_UNSUPPORTED;
   return launched(e);

@@ -350,7 +350,8 @@ hipError_t launch_append(const basiskv_dims &d, const void *k, const void *v,
 hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void *k_new,
                                 const void *v_new, const int32_t *start_pos, const void *A,
                                 const void *P, const void *Q, const void *E,
-                                const basiskv_cache &c, float *q_proj, hipStream_t s);
+                                const basiskv_cache &c, float *q_proj, int32_t *counters,
+                                int n_counters, hipStream_t s);
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s);

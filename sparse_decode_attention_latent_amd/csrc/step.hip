@@ -1,7 +1,11 @@
 // One launch for the start of a decode step: the new token's compression
 // (a0) and the routing projection of the queries (a1) are independent, so
 // their workgroups share one grid (the first n_kv * batch workgroups
-// compress, the rest project).  Bodies in decode_bodies.hpp.
+// compress, the rest project).  The first workgroup also zeroes the counters
+// with which the step's attention launch elects its merging workgroups (they
+// are left at zero by every call; clearing them here makes the step
+// independent of what an earlier call left in the workspace).  Bodies in
+// decode_bodies.hpp.
 #include "decode_bodies.hpp"
 
 namespace bkv {
@@ -9,6 +13,8 @@ namespace bkv {
 struct PrologueArgs {
   AppendArgs ap;
   int n_append, proj_x, n_q, n_kv, rb, rq;
+  int32_t *counters;  // attention merge counters to zero (n_counters of them)
+  int n_counters;
 };
 
 template <typename T, typename C>
@@ -19,6 +25,8 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(
     C *__restrict__ rpool, C *__restrict__ kpool, const int32_t *__restrict__ block_table,
     float *__restrict__ q_proj, PrologueArgs a) {
   const int idx = blockIdx.x;
+  if (idx == 0)
+    for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0;
   if (idx < a.n_append) {
     append_body<T, C>(k_new, v_new, start_pos, A, P, E, zpool, rpool, kpool, block_table, a.ap,
                    idx % a.n_kv, idx / a.n_kv);
@@ -39,8 +47,10 @@ template <typename T, typename C>
 static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k_new,
                              const void *v_new, const int32_t *start_pos, const void *A,
                              const void *P, const void *Q, const void *E, const basiskv_cache &c,
-                             float *q_proj, hipStream_t s) {
+                             float *q_proj, int32_t *counters, int n_counters, hipStream_t s) {
   PrologueArgs a;
+  a.counters = counters;
+  a.n_counters = n_counters;
   a.ap.n_tokens = 1;
   a.ap.n_kv = d.n_kv_heads;
   a.ap.rv = d.r_v;
@@ -69,12 +79,16 @@ static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k
 hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void *k_new,
                                 const void *v_new, const int32_t *start_pos, const void *A,
                                 const void *P, const void *Q, const void *E,
-                                const basiskv_cache &c, float *q_proj, hipStream_t s) {
+                                const basiskv_cache &c, float *q_proj, int32_t *counters,
+                                int n_counters, hipStream_t s) {
   if (cache_fp8(d))
-    return prologue_t<uint16_t, uint8_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s);
+    return prologue_t<uint16_t, uint8_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
+                                         counters, n_counters, s);
   return act_bf16(d)
-             ? prologue_t<uint16_t, uint16_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s)
-             : prologue_t<float, float>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj, s);
+             ? prologue_t<uint16_t, uint16_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
+                                              counters, n_counters, s)
+             : prologue_t<float, float>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
+                                        counters, n_counters, s);
 }
 
 }  // namespace bkv_host

@@ -208,3 +208,25 @@ def test_unsupported_variant_is_reported_before_launch():
                                    FAKE, 1 << 30, None) == 3
     assert lib.basiskv_sparse_attend(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, 8, 0.1, FAKE, FAKE,
                                      1 << 30, None) == 3
+
+
+@needs_lib
+def test_decode_step_static_validation():
+    """The no-allocation decode step: the documented scratch size, and every
+    host check -- including a problem whose workspace would not fit the
+    library's scratch -- answered before any HIP call."""
+    lib = api.lib()
+    assert api.static_scratch_bytes() == 8 << 20
+    c = _cache()
+
+    def step(dd, q=FAKE, top_k=128):
+        return lib.basiskv_decode_step_static(ctypes.byref(dd), q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, FAKE, FAKE, ctypes.byref(c), top_k, 0.1, FAKE,
+                                              FAKE, FAKE, FAKE, None)
+    d = dims_of(WORKLOADS[2])
+    assert step(d, q=None) == 1
+    assert step(d, top_k=0) == 2
+    assert step(dims_of(WORKLOADS[2], n_q_heads=30)) == 2
+    big = dims_of(WORKLOADS[1], batch=512)
+    assert api.workspace_bytes(big, 16) > api.static_scratch_bytes()
+    assert step(big, top_k=16) == 4
