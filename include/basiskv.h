@@ -17,6 +17,11 @@
  *        latent-to-output matrix M = blockdiag(B) W_O (Figure 1: the output is
  *        rebuilt from the latents).
  *
+ * Single-source routers: with dims.r_q = 0 there is no residual: no residual
+ * pool (cache.r_pages may be NULL), and Q and E are not read (may be NULL);
+ * with dims.r_b = 0 nothing is predicted from the latent and P is not read
+ * (may be NULL): the residual code is the Key through E.
+ *
  * Conventions shared by every entry point
  *   - Plain C, no exceptions; every call returns a basiskv_status.  Host-side
  *     validation runs before any launch: on a non-OK status nothing has been
@@ -90,8 +95,11 @@ typedef struct {
   int32_t head_dim;          /* must be 128 */
   int32_t hidden;            /* output width D of W_O (multiple of 16) */
   int32_t r_v;               /* Value-latent width */
-  int32_t r_b;               /* routing base width: leading latent dims, <= r_v */
-  int32_t r_q;               /* Key-residual rank */
+  int32_t r_b;               /* routing base width: leading latent dims, 0 <= r_b <= r_v */
+  int32_t r_q;               /* Key-residual rank, >= 0.  r_b and r_q may not both be 0;
+                                r_q = 0 routes from the latent alone, r_b = 0 from the
+                                residual alone (appendix Table 9's single-source routers
+                                B16, R16, R32, beside the combined B16R16) */
   int32_t page_size;         /* tokens per page: 4, 8, 16, 32 or 64 */
   int32_t max_pages_per_seq; /* columns of block_table, <= 32768 */
   int32_t num_phys_pages;    /* pages per pool and per KV head */

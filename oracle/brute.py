@@ -100,7 +100,8 @@ def compress_token(k_vec, v_vec, A_g, P_g, E_g, rb, round_fn):
     z_s = [round_fn(x) for x in z]
     PE = [_vecmat(list(P_g[i]), E_g) for i in range(rb)]  # rb x rq
     kE = _vecmat(list(k_vec), E_g)
-    zPE = _vecmat(z_s[:rb], PE)
+    # with r_b = 0 (a residual-only router) nothing is predicted from the latent
+    zPE = _vecmat(z_s[:rb], PE) if rb > 0 else [0.0] * len(kE)
     r = [round_fn(a - b) for a, b in zip(kE, zPE)]
     return z_s, r
 

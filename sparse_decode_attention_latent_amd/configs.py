@@ -98,6 +98,16 @@ EXTRA_WORKLOADS = (
              top_k=512, recent_tokens=64, n_planted=8, planted="random",
              latent_norm_sigma=0.5, seed=1007, cache_storage="fp8"),
 )
+# The single-source routers of the pages' router ablation (appendix Table 9,
+# beside B16R16): B16 routes from the latent's leading 16 dims alone (no
+# residual, r_q = 0); R16 and R32 from a residual of rank 16 or 32 alone
+# (r_b = 0).  Same setting as the adopted router (Page4, 512 routed pages +
+# 64 recent tokens, V96).
+EXTRA_WORKLOADS = EXTRA_WORKLOADS + (
+    EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-b16-page4", r_b=16, r_q=0, seed=1008),
+    EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-r16-page4", r_b=0, r_q=16, seed=1009),
+    EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-r32-page4", r_b=0, r_q=32, seed=1010),
+)
 # The same configurations with the routing-first page layout (each page's
 # routing dims contiguous; include/basiskv.h).
 EXTRA_WORKLOADS = EXTRA_WORKLOADS + tuple(

@@ -24,9 +24,11 @@ int32_t check_dims(const basiskv_dims *d) {
   if (!d) return BASISKV_ERR_NULL;
   if (d->dtype != BASISKV_F32 && d->dtype != BASISKV_BF16 && d->dtype != BASISKV_BF16_FP8_E4M3)
     return BASISKV_ERR_UNSUPPORTED;
+  // r_b = 0 (a residual-only router) or r_q = 0 (a latent-only router) is
+  // allowed, not both
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
-      d->hidden < 1 || d->r_v < 1 || d->r_b < 1 || d->r_q < 1 || d->page_size < 1 ||
-      d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
+      d->hidden < 1 || d->r_v < 1 || d->r_b < 0 || d->r_q < 0 || d->r_b + d->r_q < 1 ||
+      d->page_size < 1 || d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
     return BASISKV_ERR_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0 || d->r_b > d->r_v) return BASISKV_ERR_SHAPE;
   if (d->recent_tokens < 0) return BASISKV_ERR_SHAPE;
@@ -53,6 +55,7 @@ bool output_tiles_fit(const basiskv_dims &d) {
 int32_t check_cache(const basiskv_dims &d, const basiskv_cache *c, bool need_k, bool need_z,
                     bool need_r) {
   if (!c || !c->block_table || !c->seq_lens) return BASISKV_ERR_NULL;
+  if (d.r_q == 0) need_r = false;  // no residual codes to read or write
   if (bkv_host::routing_first(d)) {
     need_z = need_z || need_r;
     need_r = false;
@@ -60,6 +63,12 @@ int32_t check_cache(const basiskv_dims &d, const basiskv_cache *c, bool need_k, 
   if ((need_k && !c->k_pages) || (need_z && !c->z_pages) || (need_r && !c->r_pages))
     return BASISKV_ERR_NULL;
   return BASISKV_OK;
+}
+
+// The routing factors a call needs: P when r_b > 0, Q (routing) and E
+// (compression) when r_q > 0.
+bool missing_factor(const basiskv_dims &d, const void *P, const void *QorE) {
+  return (d.r_b > 0 && !P) || (d.r_q > 0 && !QorE);
 }
 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
@@ -162,7 +171,7 @@ int32_t basiskv_compress_prefill(const basiskv_dims *d, const void *k, const voi
                                  void *stream) {
   int32_t st = check_dims(d);
   if (st) return st;
-  if (!k || !v || !start_pos || !A || !P || !E) return BASISKV_ERR_NULL;
+  if (!k || !v || !start_pos || !A || missing_factor(*d, P, E)) return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, true, true, true))) return st;
   if (n_tokens < 1) return BASISKV_ERR_SHAPE;
   if (d->r_v % 16 || d->r_q % 16) return BASISKV_ERR_UNSUPPORTED;  // 16-wide MFMA output tiles
@@ -176,7 +185,7 @@ int32_t basiskv_project_queries(const basiskv_dims *d, const void *q, const void
                                 const void *Q, float *q_proj, void *stream) {
   int32_t st = check_dims(d);
   if (st) return st;
-  if (!q || !P || !Q || !q_proj) return BASISKV_ERR_NULL;
+  if (!q || missing_factor(*d, P, Q) || !q_proj) return BASISKV_ERR_NULL;
   return launched(bkv_host::launch_project(*d, q, P, Q, q_proj, as_stream(stream)));
 }
 
@@ -208,7 +217,7 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
                             int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
   int32_t st = check_dims(d);
   if (st) return st;
-  if (!q || !P || !Q || !page_scores || !sel) return BASISKV_ERR_NULL;
+  if (!q || missing_factor(*d, P, Q) || !page_scores || !sel) return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, false, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (!ws || ws_bytes < scratch_offset(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
@@ -263,8 +272,8 @@ int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_ne
                           float *u, void *y, const void *ws, size_t ws_bytes) {
   int32_t st = check_dims(d);
   if (st) return st;
-  if (!q || !k_new || !v_new || !start_pos || !A || !P || !Q || !E || !M || !page_scores ||
-      !sel || !u || !y)
+  if (!q || !k_new || !v_new || !start_pos || !A || missing_factor(*d, P, Q) ||
+      missing_factor(*d, P, E) || !M || !page_scores || !sel || !u || !y)
     return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, true, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;

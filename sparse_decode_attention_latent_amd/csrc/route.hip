@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     if constexpr (MF) {
       // every lane joins the matrix instructions; one without a valid token
       // scores zeros and is masked
-      uint4 cz[NZ], cr[NR];
+      uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
 #pragma unroll
       for (int c = 0; c < NZ; ++c) cz[c] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
       const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
       const int64_t roff =
           (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
-      uint4 cz[NZ], cr[NR];
+      uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
 #pragma unroll
       for (int c = 0; c < NZ; ++c) {
         const int64_t o = zoff + (int64_t)c * a.page_size * 16;
@@ -298,6 +298,13 @@ static const ScoreVariant kScoreVariants[] = {
     BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 96, 48),
     BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 16, 16),
     BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 32, 16),
+    // single-source routers (appendix Table 9: B16, R16, R32)
+    BKV_SCORE_G(uint16_t, BASISKV_BF16, 16, 0), BKV_SCORE_G(uint16_t, BASISKV_BF16, 0, 16),
+    BKV_SCORE_G(uint16_t, BASISKV_BF16, 0, 32), BKV_SCORE_G(float, BASISKV_F32, 16, 0),
+    BKV_SCORE_G(float, BASISKV_F32, 0, 16), BKV_SCORE_G(float, BASISKV_F32, 0, 32),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 16, 0),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 0, 16),
+    BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 0, 32),
 };
 
 }  // namespace bkv

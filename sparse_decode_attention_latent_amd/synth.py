@@ -18,7 +18,9 @@ Recipe (per workload, see configs.py):
             v = z Bf + noise * N(0, 1).
   planted   pages whose tokens' residual codes are shifted along Q_g qbar
             (qbar = mean query of the KV head's group), with a strength of
-            about twice the largest unplanted logit expected by chance.
+            about twice the largest unplanted logit expected by chance; a
+            router without a residual (rq = 0) shifts the latent's routing
+            dims z[:rb] along P_g qbar instead.
 Every tensor draws from its own numpy SeedSequence keyed by
 (tensor id, sequence, KV head), so a smaller batch reproduces the leading
 sequences of a larger one.
@@ -105,9 +107,9 @@ def factors(wl, storage=None):
     st = storage or wl.storage
     hkv, dh = wl.n_kv_heads, wl.head_dim
     P = np.stack([_rng(wl.seed, _ID["P"], g).standard_normal((wl.r_b, dh)) for g in range(hkv)])
-    P /= math.sqrt(wl.r_b)
+    P /= math.sqrt(max(wl.r_b, 1))
     Q = np.stack([_rng(wl.seed, _ID["Q"], g).standard_normal((wl.r_q, dh)) for g in range(hkv)])
-    Q /= math.sqrt(wl.r_q)
+    Q /= math.sqrt(max(wl.r_q, 1))
     Bf = np.stack([_rng(wl.seed, _ID["B"], g).standard_normal((wl.r_v, dh)) for g in range(hkv)])
     Bf /= math.sqrt(wl.r_v)
     W_O = _rng(wl.seed, _ID["W_O"]).standard_normal((wl.n_q_heads * dh, wl.hidden))
@@ -139,7 +141,8 @@ def _latent_scale_sq(wl):
 
 
 def _plant_shift(wl, qg_stored, Qg, T, st):
-    """Residual-code shift for planted tokens of one KV head (rq vector)."""
+    """Code shift for planted tokens of one KV head along Qg qbar (Qg: the
+    residual decoder Q_g, or the predictor P_g when there is no residual)."""
     qbar = from_storage(qg_stored, st).mean(axis=0)
     w = Qg @ qbar
     nw = float(np.linalg.norm(w))
@@ -203,10 +206,14 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         b, g = bg
         z, r = _codes(wl, (b, g), T)
         shift = None
+        plant_z = wl.r_q == 0  # no residual: plant through the latent's routing dims
         if len(planted[b]):
-            shift = _plant_shift(wl, q_st[b, g * G:(g + 1) * G], Qf[g], T, st)
+            shift = _plant_shift(wl, q_st[b, g * G:(g + 1) * G], Pf[g] if plant_z else Qf[g], T, st)
             for p in planted[b]:
-                r[p * wl.page_size:(p + 1) * wl.page_size] += shift
+                if plant_z:
+                    z[p * wl.page_size:(p + 1) * wl.page_size, :wl.r_b] += shift
+                else:
+                    r[p * wl.page_size:(p + 1) * wl.page_size] += shift
         k = z[:, :wl.r_b] @ Pf[g] + r @ Qf[g]
         if noise:
             k += noise * _rng(wl.seed, _ID["knoise"], b, g).standard_normal((T, dh))
@@ -220,7 +227,11 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         rn = _rng(wl.seed, _ID["rnew"], b, g).standard_normal(wl.r_q)
         last_page = (int(seq_lens[b]) - 1) // wl.page_size
         if shift is not None and last_page in set(planted[b].tolist()):
-            rn = rn + shift
+            if plant_z:
+                zn = zn.copy()
+                zn[:wl.r_b] += shift
+            else:
+                rn = rn + shift
         kn = zn[:wl.r_b] @ Pf[g] + rn @ Qf[g]
         vn = zn @ Bff[g]
         if noise:

@@ -138,6 +138,8 @@ def rounding_valid(gpu_codes, exact, storage):
     the roundings of the band's two ends."""
     exact = np.asarray(exact, dtype=np.float64)
     g = ref.storage_to_f64(gpu_codes, storage)
+    if exact.shape[-1] == 0:  # a zero-width row (no residual): nothing to check
+        return np.ones(exact.shape, dtype=bool)
     tol = TIE_RTOL[storage] * np.abs(exact).max(axis=-1, keepdims=True)
     lo = ref.round_to_storage(exact - tol, storage)
     hi = ref.round_to_storage(exact + tol, storage)
@@ -222,6 +224,8 @@ def rel_rows(gpu, want):
     """max |gpu - want| / max |want| over the last axis, per leading index."""
     gpu = np.asarray(gpu, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
+    if want.shape[-1] == 0:  # zero-width rows agree trivially
+        return np.zeros(want.shape[:-1])
     num = np.abs(gpu - want).max(axis=-1)
     den = np.abs(want).max(axis=-1)
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)

@@ -230,3 +230,32 @@ def test_decode_step_static_validation():
     big = dims_of(WORKLOADS[1], batch=512)
     assert api.workspace_bytes(big, 16) > api.static_scratch_bytes()
     assert step(big, top_k=16) == 4
+
+
+@needs_lib
+def test_single_source_router_dims():
+    """r_b = 0 or r_q = 0 are valid (appendix Table 9's single-source
+    routers), both zero is not; a factor the router does not use may be NULL
+    (the calls below get past the pointer checks to the workspace check)."""
+    lib = api.lib()
+    both = dims_of(WORKLOADS[2], r_b=0, r_q=0)
+    assert lib.basiskv_project_queries(ctypes.byref(both), FAKE, FAKE, FAKE, FAKE, None) == 2
+    b_only = dims_of(WORKLOADS[2], r_q=0)
+    r_only = dims_of(WORKLOADS[2], r_b=0)
+    c_no_r = _cache(r_pages=None)
+    # B-only: Q (and the residual pool) unused
+    assert lib.basiskv_route_pages(ctypes.byref(b_only), FAKE, FAKE, None, ctypes.byref(c_no_r), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 4
+    assert lib.basiskv_route_pages(ctypes.byref(b_only), FAKE, None, None, ctypes.byref(c_no_r), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 1
+    # R-only: P unused, the residual pool and Q needed
+    assert lib.basiskv_route_pages(ctypes.byref(r_only), FAKE, None, FAKE, ctypes.byref(_cache()), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 4
+    assert lib.basiskv_route_pages(ctypes.byref(r_only), FAKE, None, FAKE, ctypes.byref(c_no_r), 8,
+                                   FAKE, FAKE, FAKE, 16, None) == 1
+    assert lib.basiskv_compress_prefill(ctypes.byref(r_only), FAKE, FAKE, FAKE, 0, FAKE, None, FAKE,
+                                        ctypes.byref(_cache()), None) == 2  # n_tokens checked after pointers
+    assert lib.basiskv_compress_prefill(ctypes.byref(b_only), FAKE, FAKE, FAKE, 1, FAKE, None, None,
+                                        ctypes.byref(c_no_r), None) == 1  # P needed when r_b > 0
+    for d in (b_only, r_only):
+        assert api.workspace_bytes(d, 16) > 0

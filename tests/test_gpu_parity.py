@@ -106,7 +106,9 @@ def test_prefill_decode_128k_decode_step_full():
 
 @pytest.mark.parametrize("name", ["tiny-fp32", "llama8b-ctx4k", "llama8b-ctx32k", "qwen32b-ctx32k",
                                   "llama8b-prefill-decode-128k", "llama8b-ctx32k-b16r16-page4",
-                                  "llama8b-ctx32k-fp8", "llama8b-ctx32k-b16r16-page4-fp8"])
+                                  "llama8b-ctx32k-fp8", "llama8b-ctx32k-b16r16-page4-fp8",
+                                  "llama8b-ctx32k-b16-page4", "llama8b-ctx32k-r16-page4",
+                                  "llama8b-ctx32k-r32-page4"])
 def test_decode_step_full_size_every_sequence(name):
     """The call bench.py times, basiskv_decode_step, at the workload's full
     size and in the launch configuration the benchmark uses (the same seeded
@@ -352,6 +354,64 @@ def test_recent_window_one_call_step_equals_separate_calls():
     for key in ("scores", "sel", "u", "y"):
         np.testing.assert_array_equal(got[key], base[key], err_msg=key)
     compare_step(wl, inp, prob, got, range(3))
+
+
+# ---------------------------------------------------------------------------
+# single-source routers (appendix Table 9: B16 from the latent's leading 16
+# dims alone, R16 / R32 from the residual alone)
+# ---------------------------------------------------------------------------
+
+SINGLE_SOURCE = ("llama8b-ctx32k-b16-page4", "llama8b-ctx32k-r16-page4", "llama8b-ctx32k-r32-page4")
+
+
+@pytest.mark.parametrize("name", SINGLE_SOURCE)
+def test_single_source_router_ragged(name):
+    run_case(workload(name), batch=4, ctx=4096, seq_lens=[4096, 4095, 700, 63])
+
+
+@pytest.mark.parametrize("name", SINGLE_SOURCE)
+@pytest.mark.parametrize("fmt", ["fp8", "f32", "page32"])
+def test_single_source_router_formats(name, fmt):
+    """E4M3 pages; float32 (latent width 64); 32-token pages without a recent
+    window."""
+    wl = workload(name)
+    if fmt == "fp8":
+        wl = wl.with_(cache_storage="fp8")
+    elif fmt == "f32":
+        wl = wl.with_(storage="f32", r_v=64)
+    else:
+        wl = wl.with_(page_size=32, recent_tokens=0)
+    top_k = 64 if wl.page_size == 4 else 16
+    run_case(wl, batch=2, ctx=2048, seq_lens=[2048, 999], top_k=top_k)
+
+
+@pytest.mark.parametrize("rb,rq", [(16, 0), (0, 32)])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_compress_prefill_single_source(rb, rq, cache):
+    """(a0) on the MFMA path without a residual (r_q = 0: latents only) and
+    without latent prediction (r_b = 0: the residual is the Key through E),
+    every token checked under the rounding rules of tests/parity.py."""
+    wl = workload(4).with_(r_b=rb, r_q=rq, cache_storage="fp8" if cache == "fp8" else "")
+    B, T = 2, 700
+    k, v = synth.kv_activations(wl, batch=B, tokens=T, stream=5)
+    fac = synth.factors(wl)
+    prob = PrefillProblem(wl, k, v, fac, storage="bf16", cache_storage=cache)
+    prob.run()
+    got = prob.logical()
+    A, P, E = (ref.storage_to_f64(fac[n], "bf16") for n in ("A", "P", "E"))
+    for b in range(B):
+        kb, vb = ref.storage_to_f64(k[b], "bf16"), ref.storage_to_f64(v[b], "bf16")
+        np.testing.assert_array_equal(ref.storage_to_f64(got["k"][b], cache),
+                                      ref.round_to_storage(kb, cache).transpose(1, 0, 2))
+        assert got["r"][b].shape[-1] == rq
+        for g in range(wl.n_kv_heads):
+            okz = parity.rounding_valid(got["z"][b, g], ref.latent_code(vb[:, g], A[g]), cache)
+            assert okz.all(), f"b={b} g={g}: latent codes"
+            if rq:
+                zgv = ref.storage_to_f64(got["z"][b, g], cache)
+                r_exact = ref.residual_code(kb[:, g], zgv, P[g], E[g], rb)
+                assert parity.rounding_valid(got["r"][b, g], r_exact, cache).all(), f"b={b} g={g}: residual"
+    _say(f"  compress r_b={rb} r_q={rq} {cache}: every token valid")
 
 
 # ---------------------------------------------------------------------------

@@ -247,6 +247,90 @@ def test_route_uses_only_leading_rb_latent_dims():
 
 
 # ---------------------------------------------------------------------------
+# single-source routers (appendix Table 9: B16 routes from the latent's leading
+# dims alone, R16 / R32 from the residual alone)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rb,rq", [(3, 0), (0, 2)])
+def test_single_source_router_matches_brute(rb, rq):
+    """Routing and compression with r_q = 0 or r_b = 0 agree with the brute
+    force (projected queries; residual as k E - z_s (P E))."""
+    wl = tiny_workload(r_b=rb, r_q=rq)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    G, n_out = wl.group, wl.max_pages
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            qg = d["q"][b, g * G:(g + 1) * G]
+            mine = ref.route_page_scores(qg, d["z"][b, g], d["r"][b, g], d["P"][g], d["Q"][g],
+                                         wl.r_b, 11, wl.page_size, n_out)
+            other = brute.route_page_scores(qg.tolist(), d["z"][b, g].tolist(), d["r"][b, g].tolist(),
+                                            d["P"][g].tolist(), d["Q"][g].tolist(), wl.r_b, 11,
+                                            wl.page_size, n_out)
+            np.testing.assert_allclose(mine, other, rtol=1e-12, atol=1e-12)
+    z_s, r_s, _ = ref.compress_tokens(d["k_new"], d["v_new"], d["A"], d["P"], d["E"], wl.r_b, "f64")
+    assert r_s.shape[-1] == rq and z_s.shape[-1] == wl.r_v
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            zb, rb_ = brute.compress_token(d["k_new"][b, g], d["v_new"][b, g], d["A"][g].tolist(),
+                                           d["P"][g].tolist(), d["E"][g].tolist(), wl.r_b, float)
+            np.testing.assert_allclose(z_s[b, g], zb, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(r_s[b, g], rb_, rtol=0, atol=1e-12)
+
+
+def test_b_only_router_is_the_full_router_with_zero_residual():
+    """Special case: routing without a residual (r_q = 0) gives exactly the
+    scores of the combined router whose residual codes are all zero, for any
+    residual decoder."""
+    wl = tiny_workload(r_q=0)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    rng = np.random.default_rng(9)
+    Q_any = rng.standard_normal((5, wl.head_dim))
+    qg = d["q"][0, :wl.group]
+    mine = ref.route_page_scores(qg, d["z"][0, 0], d["r"][0, 0], d["P"][0], d["Q"][0], wl.r_b,
+                                 11, wl.page_size, wl.max_pages)
+    full = ref.route_page_scores(qg, d["z"][0, 0], np.zeros((wl.ctx, 5)), d["P"][0], Q_any, wl.r_b,
+                                 11, wl.page_size, wl.max_pages)
+    np.testing.assert_array_equal(mine, full)
+
+
+def test_r_only_residual_is_the_key_encoded():
+    """With r_b = 0 nothing is predicted from the latent: the residual code is
+    the Key through the residual encoder, r = k E (closed form), and a
+    noise-free Key k = r Q (E = pinv(Q)) gives its code back exactly."""
+    wl = workload("llama8b-ctx32k-r32-page4").with_(storage="f64")
+    fac = synth.factors(wl)
+    A, P, Q, E = (ref.storage_to_f64(fac[k], "f64") for k in ("A", "P", "Q", "E"))
+    assert P.shape[1] == 0
+    rng = np.random.default_rng(21)
+    r = rng.standard_normal((30, wl.n_kv_heads, wl.r_q))
+    k = np.einsum("ngj,gjd->ngd", r, Q)
+    v = rng.standard_normal((30, wl.n_kv_heads, wl.head_dim))
+    _, r_s, _ = ref.compress_tokens(k, v, A, P, E, 0, "f64")
+    np.testing.assert_allclose(r_s, np.einsum("ngd,gdj->ngj", k, E), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r_s, r, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("name", ["llama8b-ctx32k-b16-page4", "llama8b-ctx32k-r16-page4"])
+def test_single_source_route_equals_exact_logits_when_keys_are_exact(name):
+    """Noise-free Keys are exactly the single source's prediction (z[:rb] P,
+    or r Q), so the routing logits are the exact q.k logits."""
+    wl = workload(name).with_(storage="f64", ctx=200, batch=1)
+    inp = synth.decode_inputs(wl, exact=True)
+    d = unpack(inp)
+    G, S, L = wl.group, wl.page_size, 200
+    for g in (0, wl.n_kv_heads - 1):
+        qg = d["q"][0, g * G:(g + 1) * G]
+        mine = ref.route_page_scores(qg, d["z"][0, g], d["r"][0, g], d["P"][g], d["Q"][g], wl.r_b,
+                                     L, S, wl.max_pages)
+        exact = qg @ d["kc"][0, g, :L].T
+        n_pages = -(-L // S)
+        want = [exact[:, p * S:min((p + 1) * S, L)].max() for p in range(n_pages)]
+        np.testing.assert_allclose(mine[:n_pages], want, rtol=1e-10, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
 # selection
 # ---------------------------------------------------------------------------
 
@@ -519,7 +603,8 @@ def test_dense_attention_equals_sdpa(L):
 # semantics of the synthetic workloads: planted pages are routed
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("index,batch", [(0, 1), (1, 2), (2, 1), (3, 1)])
+@pytest.mark.parametrize("index,batch", [(0, 1), (1, 2), (2, 1), (3, 1), ("llama8b-ctx32k-b16-page4", 1),
+                                         ("llama8b-ctx32k-r32-page4", 1)])
 def test_planted_pages_are_selected(index, batch):
     wl = workload(index).with_(batch=batch)
     inp = synth.decode_inputs(wl)
