@@ -48,7 +48,15 @@ Readings of points the pages leave open (each used below):
      code of each value with no scale factor (scale 1): exponent bias 7,
      3 mantissa bits, largest finite magnitude 448, subnormal step 2**-9, no
      infinities; writes round to nearest even and saturate to +-448 instead
-     of producing the NaN code.
+     of producing the NaN code;  R13 rotary position embedding (RoPE; the
+     Figure 6 caption of the pages measures how well the latent explains
+     the *pre-RoPE* Key): every cached state is pre-RoPE (latent, residual
+     and exact Key), queries come already rotated at their own position, and
+     both the predicted Key (routing) and the exact Key (attention) of the
+     token at position t (its index in the sequence) are rotated to t before
+     the dot product.  Rotation: rotate-half pairs (i, i + dh/2), angle
+     t * w_i taken exactly, w_i the caller's float32 inverse frequencies
+     (w_i = base**(-2i/dh) for the standard embedding).
 """
 
 import math
@@ -186,6 +194,33 @@ def residual_code(k, z_s, P_g, E_g, rb):
 
 
 # ---------------------------------------------------------------------------
+# rotary position embedding (reading R13)
+# ---------------------------------------------------------------------------
+
+def rope_rotate(x, positions, inv_freq):
+    """Rows x [n, dh] rotated to their positions [n] (R13): for each pair
+    (i, i + dh/2), angle phi = position * w_i (float64: exact for positions
+    below 2**24 and float32 frequencies),
+      x_i' = x_i cos(phi) - x_{i+dh/2} sin(phi),
+      x_{i+dh/2}' = x_i sin(phi) + x_{i+dh/2} cos(phi).
+    inv_freq None: no rotation."""
+    x = np.asarray(x, dtype=np.float64)
+    if inv_freq is None:
+        return x
+    half = x.shape[-1] // 2
+    w = np.asarray(inv_freq, dtype=np.float32).astype(np.float64)
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * w[None, :]
+    c, s_ = np.cos(phi), np.sin(phi)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s_, lo * s_ + hi * c], axis=-1)
+
+
+def rope_inverse_frequencies(head_dim, base):
+    """Standard RoPE frequencies w_i = base**(-2i/dh) as float32."""
+    return (float(base) ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # (a1, a2) routing: predicted keys and page scores
 # ---------------------------------------------------------------------------
 
@@ -200,7 +235,8 @@ def predicted_keys(z, r, P_g, Q_g, rb):
     return z[:, :rb] @ P_g + r @ Q_g
 
 
-def route_page_scores(q_group, z, r, P_g, Q_g, rb, seq_len, page_size, n_pages_out):
+def route_page_scores(q_group, z, r, P_g, Q_g, rb, seq_len, page_size, n_pages_out,
+                      inv_freq=None):
     """Page scores of one (sequence, KV head).
 
     BasisKV abstract: the predicted Key information decides which Key pages
@@ -208,12 +244,15 @@ def route_page_scores(q_group, z, r, P_g, Q_g, rb, seq_len, page_size, n_pages_o
     For every valid token t and query head h of the group, the routing logit
     is q_h . k_hat_t (unscaled, R4); a page's score is the maximum over its
     valid tokens and the group's heads (R1, R2).  Pages at or beyond
-    ceil(seq_len / page_size) get -inf.  Returns [n_pages_out] float64.
+    ceil(seq_len / page_size) get -inf.  With inv_freq the predicted Key of
+    token t is rotated to position t first (R13).  Returns [n_pages_out]
+    float64.
     """
     scores = np.full(n_pages_out, -np.inf)
     if seq_len <= 0:
         return scores
     khat = predicted_keys(z[:seq_len], r[:seq_len], P_g, Q_g, rb)
+    khat = rope_rotate(khat, np.arange(seq_len), inv_freq)
     logits = q_group @ khat.T  # [G, seq_len]
     n_pages = -(-seq_len // page_size)
     for p in range(min(n_pages, n_pages_out)):
@@ -266,7 +305,7 @@ def selected_tokens(sel, seq_len, page_size):
 # (a4) exact attention over the selected pages, summed in latent space
 # ---------------------------------------------------------------------------
 
-def attend_group(q_group, kc, z, sel, seq_len, page_size, scale):
+def attend_group(q_group, kc, z, sel, seq_len, page_size, scale, inv_freq=None):
     """Latent attention output of one KV head's query group.
 
     BasisKV abstract: exact QK scores are computed from the original Keys of
@@ -280,7 +319,8 @@ def attend_group(q_group, kc, z, sel, seq_len, page_size, scale):
     toks = selected_tokens(sel, seq_len, page_size)
     if toks.size == 0:
         return np.zeros((q_group.shape[0], z.shape[1]))
-    s = scale * (q_group @ kc[toks].T)  # [G, n]
+    keys = rope_rotate(kc[toks], toks, inv_freq)  # R13: each Key at its position
+    s = scale * (q_group @ keys.T)  # [G, n]
     s = s - s.max(axis=1, keepdims=True)
     w = np.exp(s)
     w = w / w.sum(axis=1, keepdims=True)
@@ -324,7 +364,7 @@ def reconstruct(u, Bf, W_O, group):
 
 def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
                 top_k, n_pages_out, storage, scale=None, k_new=None, v_new=None,
-                store_output=True, recent_tokens=0, cache_storage=None):
+                store_output=True, recent_tokens=0, cache_storage=None, rope_inv_freq=None):
     """One decode step of one layer for a batch.
 
     Inputs are float64 (decode stored values with storage_to_f64 first);
@@ -335,8 +375,9 @@ def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
     (a0); then it routes (a1, a2), selects (a3), attends (a4) and
     reconstructs (a5).  With recent_tokens > 0 the top-k pages are chosen
     before the recent window and the window's pages are attended as well
-    (R11); ``sel`` holds the routed pages only.  Arrays z, r, kc are copied,
-    not modified.
+    (R11); ``sel`` holds the routed pages only.  With rope_inv_freq the
+    cached Keys are pre-RoPE and rotated to their positions (R13).  Arrays
+    z, r, kc are copied, not modified.
 
     Returns a dict: scores [B, Hkv, n_pages_out], sel [B, Hkv, top_k],
     u [B, Hq, rV], y [B, D] (float64, unrounded), y_stored (y rounded to
@@ -377,11 +418,11 @@ def decode_step(q, z, r, kc, seq_lens, A, Bf, P, Q, E, W_O, *, rb, page_size,
         for g in range(hkv):
             qg = q[b, g * group:(g + 1) * group]
             scores[b, g] = route_page_scores(qg, z[b, g], r[b, g], P[g], Q[g], rb, L,
-                                             page_size, n_pages_out)
+                                             page_size, n_pages_out, rope_inv_freq)
             sel[b, g] = select_pages(scores[b, g], first_recent, top_k)
             pages = np.concatenate([sel[b, g], recent])
             u[b, g * group:(g + 1) * group] = attend_group(qg, kc[b, g], z[b, g], pages,
-                                                           L, page_size, scale)
+                                                           L, page_size, scale, rope_inv_freq)
         y[b] = reconstruct(u[b], Bf, W_O, group)
     out = dict(scores=scores, sel=sel, u=u, y=y, z=z, r=r, kc=kc)
     if store_output:

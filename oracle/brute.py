@@ -12,7 +12,9 @@ head or page index) makes the pins in tests/test_oracle.py disagree:
   attend     explicit token loop with an unshifted softmax;
   compress   residual as k E - z_s (P E), instead of (k - z_s P) E;
   reconstruct  through the fused latent-to-output matrix B W_O, instead of
-             decoding the Value first.
+             decoding the Value first;
+  rope       each pair's rotation as an explicit 2 x 2 matrix, applied to the
+             query (transposed) instead of the Key: q . R(t) k = (R(t)^T q) . k.
 
 Inputs are nested Python lists or numpy arrays of floats; all arithmetic is
 Python float (IEEE double) in explicit loops.
@@ -131,6 +133,61 @@ def attend_tokens(q_group, kc, z, tokens, scale):
         return out
     for h in range(G):
         w = [math.exp(scale * _dot(q_group[h], kc[t])) for t in tokens]
+        tot = sum(w)
+        for wi, t in zip(w, tokens):
+            for d in range(rv):
+                out[h][d] += wi / tot * z[t][d]
+    return out
+
+
+def rotate_pair_matrix(angle):
+    """The 2 x 2 rotation [[cos, -sin], [sin, cos]] by ``angle``."""
+    c, s = math.cos(angle), math.sin(angle)
+    return [[c, -s], [s, c]]
+
+
+def rope_unrotate_query(q, position, inv_freq):
+    """R(t)^T q for a query q (list, dh) and a token position t: each pair
+    (i, i + dh/2) multiplied by the transposed 2 x 2 rotation matrix."""
+    half = len(q) // 2
+    out = list(q)
+    for i in range(half):
+        m = rotate_pair_matrix(position * float(inv_freq[i]))
+        a, b = q[i], q[i + half]
+        out[i] = m[0][0] * a + m[1][0] * b
+        out[i + half] = m[0][1] * a + m[1][1] * b
+    return out
+
+
+def route_page_scores_rope(q_group, z, r, P_g, Q_g, rb, seq_len, page_size, n_pages_out, inv_freq):
+    """Page scores with RoPE via projected queries: for token t the query is
+    turned back by t, R(t)^T q, and then projected onto the routing factors:
+    logit = (P R(t)^T q)[:rb] . z[:rb] + (Q R(t)^T q) . r."""
+    scores = [-math.inf] * n_pages_out
+    for t in range(seq_len):
+        p = t // page_size
+        if p >= n_pages_out:
+            continue
+        for qh in q_group:
+            qt = rope_unrotate_query(list(qh), t, inv_freq)
+            logit = (_dot(_matvec(P_g, qt), list(z[t][:rb])) if rb else 0.0) + \
+                (_dot(_matvec(Q_g, qt), list(r[t])) if len(r[t]) else 0.0)
+            if logit > scores[p]:
+                scores[p] = logit
+    return scores
+
+
+def attend_tokens_rope(q_group, kc, z, tokens, scale, inv_freq):
+    """Latent attention over an explicit token list with RoPE: each query
+    turned back by the token's position (R(t)^T q) and dotted with the
+    pre-RoPE Key, explicit loops, an unshifted softmax."""
+    G, rv = len(q_group), len(z[0])
+    out = [[0.0] * rv for _ in range(G)]
+    if not tokens:
+        return out
+    for h in range(G):
+        w = [math.exp(scale * _dot(rope_unrotate_query(list(q_group[h]), t, inv_freq), kc[t]))
+             for t in tokens]
         tot = sum(w)
         for wi, t in zip(w, tokens):
             for d in range(rv):

@@ -32,6 +32,7 @@ class Workload:
     recent_tokens: int = 0  # recent window attended besides the routed pages
     cache_storage: str = ""  # "fp8": z, r and Key pages as E4M3 codes ("" = storage)
     page_layout: int = 0     # 1: routing-first pages (latent and residual in one pool)
+    rope_theta: float = 0.0  # >0: rotary position embedding with this base (pre-RoPE caches)
     # prefill + decode workload only
     prefill_batch: int = 0
     prefill_tokens: int = 0
@@ -107,6 +108,14 @@ EXTRA_WORKLOADS = EXTRA_WORKLOADS + (
     EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-b16-page4", r_b=16, r_q=0, seed=1008),
     EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-r16-page4", r_b=0, r_q=16, seed=1009),
     EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-r32-page4", r_b=0, r_q=32, seed=1010),
+)
+# Rotary position embedding on the predicted pre-RoPE Keys (the pages' Figure 6
+# measures pre-RoPE Key predictability): the adopted router and the headline
+# shape with positions, base 500000 (Llama-3.1's).
+EXTRA_WORKLOADS = EXTRA_WORKLOADS + (
+    EXTRA_WORKLOADS[0].with_(name="llama8b-ctx32k-b16r16-page4-rope", rope_theta=500000.0,
+                             seed=1011),
+    WORKLOADS[2].with_(name="llama8b-ctx32k-rope", rope_theta=500000.0, seed=1012),
 )
 # The same configurations with the routing-first page layout (each page's
 # routing dims contiguous; include/basiskv.h).

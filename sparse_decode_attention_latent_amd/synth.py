@@ -20,7 +20,12 @@ Recipe (per workload, see configs.py):
             (qbar = mean query of the KV head's group), with a strength of
             about twice the largest unplanted logit expected by chance; a
             router without a residual (rq = 0) shifts the latent's routing
-            dims z[:rb] along P_g qbar instead.
+            dims z[:rb] along P_g qbar instead.  With rotary positions the
+            cached Keys are pre-RoPE, so qbar is first turned back by each
+            planted token's position.
+  rope      (workloads with rope_theta > 0) the inverse frequencies
+            base**(-2i/dh), i < dh/2, as float32: an input table of the
+            step, like the factors.
 Every tensor draws from its own numpy SeedSequence keyed by
 (tensor id, sequence, KV head), so a smaller batch reproduces the leading
 sequences of a larger one.
@@ -140,10 +145,32 @@ def _latent_scale_sq(wl):
     return math.exp(2.0 * s * s) if s > 0 else 1.0
 
 
-def _plant_shift(wl, qg_stored, Qg, T, st):
+def rope_frequencies(wl):
+    """The workload's RoPE inverse frequencies (float32 [dh/2]), or None."""
+    if not wl.rope_theta:
+        return None
+    i = np.arange(0, wl.head_dim, 2, dtype=np.float64)
+    return (float(wl.rope_theta) ** (-i / wl.head_dim)).astype(np.float32)
+
+
+def _turn_back(x, pos, freqs):
+    """x rotated by -pos * freqs in rotate-half pairs (i, i + dh/2): the
+    direction a pre-RoPE Key at position pos must have to align with x."""
+    half = x.shape[-1] // 2
+    phi = pos * freqs.astype(np.float64)
+    c, s = np.cos(phi), np.sin(phi)
+    lo, hi = x[:half], x[half:]
+    return np.concatenate([lo * c + hi * s, -lo * s + hi * c])
+
+
+def _plant_shift(wl, qg_stored, Qg, T, st, pos=None):
     """Code shift for planted tokens of one KV head along Qg qbar (Qg: the
-    residual decoder Q_g, or the predictor P_g when there is no residual)."""
+    residual decoder Q_g, or the predictor P_g when there is no residual);
+    with RoPE, qbar turned back by the token's position pos first."""
     qbar = from_storage(qg_stored, st).mean(axis=0)
+    freqs = rope_frequencies(wl)
+    if freqs is not None and pos is not None:
+        qbar = _turn_back(qbar, pos, freqs)
     w = Qg @ qbar
     nw = float(np.linalg.norm(w))
     if nw == 0.0:
@@ -207,13 +234,17 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         z, r = _codes(wl, (b, g), T)
         shift = None
         plant_z = wl.r_q == 0  # no residual: plant through the latent's routing dims
+        qgb = q_st[b, g * G:(g + 1) * G]
+        Fg = Pf[g] if plant_z else Qf[g]
         if len(planted[b]):
-            shift = _plant_shift(wl, q_st[b, g * G:(g + 1) * G], Pf[g] if plant_z else Qf[g], T, st)
+            shift = _plant_shift(wl, qgb, Fg, T, st)
             for p in planted[b]:
-                if plant_z:
-                    z[p * wl.page_size:(p + 1) * wl.page_size, :wl.r_b] += shift
-                else:
-                    r[p * wl.page_size:(p + 1) * wl.page_size] += shift
+                for t in range(p * wl.page_size, min((p + 1) * wl.page_size, T)):
+                    sh = shift if not wl.rope_theta else _plant_shift(wl, qgb, Fg, T, st, pos=t)
+                    if plant_z:
+                        z[t, :wl.r_b] += sh
+                    else:
+                        r[t] += sh
         k = z[:, :wl.r_b] @ Pf[g] + r @ Qf[g]
         if noise:
             k += noise * _rng(wl.seed, _ID["knoise"], b, g).standard_normal((T, dh))
@@ -226,6 +257,8 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
             zn *= _rng(wl.seed, _ID["znew"], b, g, 1).lognormal(0.0, wl.latent_norm_sigma)
         rn = _rng(wl.seed, _ID["rnew"], b, g).standard_normal(wl.r_q)
         last_page = (int(seq_lens[b]) - 1) // wl.page_size
+        if shift is not None and wl.rope_theta:
+            shift = _plant_shift(wl, qgb, Fg, T, st, pos=int(seq_lens[b]) - 1)
         if shift is not None and last_page in set(planted[b].tolist()):
             if plant_z:
                 zn = zn.copy()
@@ -245,7 +278,7 @@ def decode_inputs(wl, *, batch=None, ctx=None, seq_lens=None, exact=False, stora
         list(ex.map(one, [(b, g) for b in range(B) for g in range(hkv)]))
 
     out = dict(q=q_st, z=z_st, r=r_st, kc=k_st, k_new=kn_st, v_new=vn_st, seq_lens=seq_lens,
-               planted=planted, storage=st, cache_storage=cst)
+               planted=planted, storage=st, cache_storage=cst, rope_inv_freq=rope_frequencies(wl))
     out.update(fac)
     return out
 

@@ -90,6 +90,7 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
     L = int(inp["seq_lens"][b])
     fac = {k: f64(inp[k], st) for k in ("A", "Bf", "P", "Q", "E", "W_O")}
     q = f64(inp["q"][b], st)
+    freqs = inp.get("rope_inv_freq")  # rotary positions (pre-RoPE caches), or None
     scores = np.full((hkv, n_pages_out), -np.inf)
     sel = np.full((hkv, top_k), -1, dtype=np.int64)
     u = np.zeros((wl.n_q_heads, wl.r_v))
@@ -118,11 +119,11 @@ def oracle_sequence(wl, inp, b, *, top_k, append=True, sel_override=None, n_page
                 z[L - 1], r[L - 1], kc[L - 1] = z_new[g], r_new[g], k_new[g]
             qg = q[g * G:(g + 1) * G]
             scores[g] = ref.route_page_scores(qg, z, r, fac["P"][g], fac["Q"][g], wl.r_b, L, S,
-                                              n_pages_out)
+                                              n_pages_out, freqs)
             sel[g] = ref.select_pages(scores[g], n_cand, top_k)
             use = sel[g] if sel_override is None else np.asarray(sel_override[g], dtype=np.int64)
             u[g * G:(g + 1) * G] = ref.attend_group(qg, kc, z, np.concatenate([use, recent]),
-                                                    L, S, scale)
+                                                    L, S, scale, freqs)
     y = ref.reconstruct(u, fac["Bf"], fac["W_O"], G) if L > 0 else np.zeros(wl.hidden)
     return dict(scores=scores, sel=sel, u=u, y=y, y_stored=ref.round_to_storage(y, st),
                 z_new=z_new, r_new=r_new, k_new=k_new, z_exact=z_exact,

@@ -604,7 +604,8 @@ def test_dense_attention_equals_sdpa(L):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("index,batch", [(0, 1), (1, 2), (2, 1), (3, 1), ("llama8b-ctx32k-b16-page4", 1),
-                                         ("llama8b-ctx32k-r32-page4", 1)])
+                                         ("llama8b-ctx32k-r32-page4", 1),
+                                         ("llama8b-ctx32k-b16r16-page4-rope", 1)])
 def test_planted_pages_are_selected(index, batch):
     wl = workload(index).with_(batch=batch)
     inp = synth.decode_inputs(wl)
@@ -617,6 +618,134 @@ def test_planted_pages_are_selected(index, batch):
         assert len(planted) == wl.n_planted
         for g in range(wl.n_kv_heads):
             sc = ref.route_page_scores(q[b, g * G:(g + 1) * G], z[b, g], r[b, g], P[g], Q[g], wl.r_b,
-                                       wl.ctx, wl.page_size, wl.max_pages)
+                                       wl.ctx, wl.page_size, wl.max_pages, inp["rope_inv_freq"])
             sel = set(ref.select_pages(sc, wl.max_pages, wl.top_k).tolist())
             assert planted <= sel, (b, g, sorted(planted - sel))
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding (reading R13: cached states pre-RoPE, predicted and
+# exact Keys rotated to their positions; the pages' Figure 6 caption)
+# ---------------------------------------------------------------------------
+
+def _freqs(dh, base=10000.0):
+    return ref.rope_inverse_frequencies(dh, base)
+
+
+def test_rope_frequencies_closed_form():
+    w = _freqs(128, 500000.0)
+    assert w.dtype == np.float32 and w.shape == (64,) and w[0] == 1.0
+    np.testing.assert_allclose(w[1:], 500000.0 ** (-np.arange(2, 128, 2) / 128.0), rtol=1e-7)
+
+
+def test_rope_rotation_matches_pair_matrix_brute():
+    """q . R(t) k with the oracle's rotate-half rotation of k equals the brute
+    force's transposed 2 x 2 matrices applied to q, (R(t)^T q) . k."""
+    rng = np.random.default_rng(41)
+    w = _freqs(16, 100.0)
+    for t in (0, 1, 7, 1000, 131071):
+        q, k = rng.standard_normal(16), rng.standard_normal(16)
+        mine = q @ ref.rope_rotate(k[None], [t], w)[0]
+        other = brute._dot(brute.rope_unrotate_query(q.tolist(), t, w), k.tolist())
+        assert abs(mine - other) <= 1e-12 * max(1.0, abs(mine))
+
+
+def test_rope_is_a_rotation_of_relative_position():
+    """Norms are kept, and (R(s) q) . (R(t) k) = q . R(t - s) k."""
+    rng = np.random.default_rng(42)
+    w = _freqs(128, 500000.0)
+    x = rng.standard_normal((5, 128))
+    rx = ref.rope_rotate(x, [0, 3, 99, 4096, 70000], w)
+    np.testing.assert_allclose(np.linalg.norm(rx, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for s_, t in ((5, 9), (1000, 37), (65536, 65539)):
+        lhs = ref.rope_rotate(q[None], [s_], w)[0] @ ref.rope_rotate(k[None], [t], w)[0]
+        rhs = q @ ref.rope_rotate(k[None], [t - s_], w)[0]
+        assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+
+
+def test_rope_with_zero_frequencies_is_the_unrotated_path():
+    wl = tiny_workload()
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    zero = np.zeros(wl.head_dim // 2, dtype=np.float32)
+    kw = dict(rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k, n_pages_out=wl.max_pages,
+              storage="f64", k_new=d["k_new"], v_new=d["v_new"])
+    base = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                           d["Q"], d["E"], d["W_O"], **kw)
+    rot = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], inp["seq_lens"], d["A"], d["Bf"], d["P"],
+                          d["Q"], d["E"], d["W_O"], rope_inv_freq=zero, **kw)
+    for key in ("scores", "sel", "u", "y"):
+        np.testing.assert_array_equal(rot[key], base[key])
+
+
+@pytest.mark.parametrize("rb,rq", [(3, 2), (3, 0), (0, 2)])
+def test_rope_route_matches_projected_rotated_query_brute(rb, rq):
+    """Rotated predicted Key . query = the projected-query route with the
+    query turned back by each token's position (brute force, pure Python)."""
+    wl = tiny_workload(r_b=rb, r_q=rq)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    w = _freqs(wl.head_dim, 10.0)
+    G = wl.group
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            qg = d["q"][b, g * G:(g + 1) * G]
+            mine = ref.route_page_scores(qg, d["z"][b, g], d["r"][b, g], d["P"][g], d["Q"][g], rb, 11,
+                                         wl.page_size, wl.max_pages, w)
+            other = brute.route_page_scores_rope(qg.tolist(), d["z"][b, g].tolist(),
+                                                 d["r"][b, g].tolist(), d["P"][g].tolist(),
+                                                 d["Q"][g].tolist(), rb, 11, wl.page_size,
+                                                 wl.max_pages, w)
+            np.testing.assert_allclose(mine, other, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_attend_matches_sdpa_on_rotated_keys_and_brute():
+    """Attention with RoPE = SDPA (library) on the Keys rotated to their
+    positions, and = the brute force's turned-back queries."""
+    wl = workload(0).with_(storage="f64", ctx=300, batch=1)
+    inp = synth.decode_inputs(wl)
+    d = unpack(inp)
+    w = _freqs(wl.head_dim, 500000.0)
+    G, S, L, scale = wl.group, wl.page_size, 290, 1 / math.sqrt(wl.head_dim)
+    sel = np.array([0, 3, 7, 11, 18], dtype=np.int64)
+    toks = ref.selected_tokens(sel, L, S)
+    qg, kc, z = d["q"][0, :G], d["kc"][0, 0], d["z"][0, 0]
+    mine = ref.attend_group(qg, kc, z, sel, L, S, scale, w)
+    krot = ref.rope_rotate(kc[toks], toks, w)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qg)[None, :, None], torch.from_numpy(krot)[None, None].expand(1, G, -1, -1),
+        torch.from_numpy(z[toks])[None, None].expand(1, G, -1, -1), scale=scale)[0, :, 0].numpy()
+    np.testing.assert_allclose(mine, want, rtol=1e-12, atol=1e-12)
+    small = tiny_workload()
+    sinp = synth.decode_inputs(small)
+    sd = unpack(sinp)
+    sw = _freqs(small.head_dim, 10.0)
+    qs = sd["q"][0, :small.group] * 0.3
+    stoks = [0, 1, 4, 5, 8, 9]  # pages 0, 2, 4 of 2-token pages
+    other = brute.attend_tokens_rope(qs.tolist(), sd["kc"][0, 0].tolist(), sd["z"][0, 0].tolist(),
+                                     stoks, 0.5, sw)
+    mine_s = ref.attend_group(qs, sd["kc"][0, 0], sd["z"][0, 0], np.array([0, 2, 4]), 10, 2, 0.5, sw)
+    np.testing.assert_allclose(mine_s, other, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_full_k_invariant_equals_dense_rotated_attention():
+    """Exact factors (V = z B, noise-free) and k = all pages: the RoPE decode
+    step equals dense softmax attention over the rotated Keys and the Values,
+    through W_O (the Full-K reference with positions)."""
+    wl = workload(0).with_(storage="f64", ctx=200, batch=1, top_k=13)
+    inp = synth.decode_inputs(wl, exact=True)
+    d = unpack(inp)
+    w = _freqs(wl.head_dim, 500000.0)
+    L = 200
+    out = ref.decode_step(d["q"], d["z"], d["r"], d["kc"], [L], d["A"], d["Bf"], d["P"], d["Q"],
+                          d["E"], d["W_O"], rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k,
+                          n_pages_out=wl.max_pages, storage="f64", rope_inv_freq=w)
+    G, scale = wl.group, 1 / math.sqrt(wl.head_dim)
+    heads = []
+    for g in range(wl.n_kv_heads):
+        v = d["z"][0, g, :L] @ d["Bf"][g]
+        krot = ref.rope_rotate(d["kc"][0, g, :L], np.arange(L), w)
+        heads.append(ref.dense_attention(d["q"][0, g * G:(g + 1) * G], krot, v, L, scale))
+    y = np.concatenate(heads).reshape(-1) @ d["W_O"]
+    np.testing.assert_allclose(out["y"][0], y, rtol=1e-10, atol=1e-10)
