@@ -199,7 +199,7 @@ def cpu_baseline(wl, inp, target_seconds):
                         f["E"], f["W_O"], rb=wl.r_b, page_size=wl.page_size, top_k=wl.top_k,
                         n_pages_out=-(-x["z"].shape[2] // wl.page_size), storage=st,
                         k_new=x["k_new"], v_new=x["v_new"], recent_tokens=wl.recent_tokens,
-                        cache_storage=cst)
+                        cache_storage=cst, rope_inv_freq=inp.get("rope_inv_freq"))
         elapsed += time.perf_counter() - t0
         nbytes += traffic.step_bytes(one, x["L"])["total"]
         done += 1
@@ -450,6 +450,8 @@ def main():
     # host-side call takes about as long as its launch is marked host-bound
     stages = ("append", "project", "score", "select", "attend", "reconstruct")
     calls = [prob.append, prob.project, prob.score, prob.select, prob.attend, prob.reconstruct]
+    if prob.rope_inv_freq is not None:  # RoPE: scoring reads the raw queries, no projection
+        stages, calls = stages[:1] + stages[2:], calls[:1] + calls[2:]
     for _ in range(2):
         prob.step_unfused()
     torch.cuda.synchronize()
@@ -509,7 +511,9 @@ def main():
         "stages_host_bound": [k for k in stages if host_bound[k]],
         "stages_gbs": {k: round(sb[k] / (per_stage[k] * 1e-6) / 1e9, 1) for k in stages},
         "stages_hbm_bytes_measured": {"score": traffic_bytes, "attend": attend_traffic},
-        "roofline": {"kernel": "route_scan_kernel (page scoring)", "bound": "hbm",
+        "roofline": {"kernel": ("route_rope_kernel (page scoring with rotated predicted Keys)"
+                                if prob.rope_inv_freq is not None
+                                else "route_scan_kernel (page scoring)"), "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": sb["score"],

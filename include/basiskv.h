@@ -124,6 +124,25 @@ typedef struct {
   void *k_pages;              /* exact Keys     [n_kv][num_phys][head_dim/CE][page_size][CE] */
   const int32_t *block_table; /* [batch][max_pages_per_seq] logical -> physical page */
   const int32_t *seq_lens;    /* [batch] valid tokens of each sequence */
+  const float *rope_inv_freq; /* NULL: no positions.  Else rotary position embedding
+                                 (the pages' Figure 6 predicts the pre-RoPE Key): float32
+                                 [head_dim / 2] inverse frequencies w_i (w_i = base^(-2i /
+                                 head_dim) for the standard embedding); every cached state
+                                 is pre-RoPE, the queries are already rotated to their own
+                                 position, and the predicted Key (routing) and the exact
+                                 Key (attention) of the token at position t -- its index
+                                 in the sequence -- are rotated to t before the dot
+                                 product: rotate-half pairs (i, i + head_dim / 2) by the
+                                 angle t * w_i (taken exactly).  Routing then forms each
+                                 token's predicted Key on the matrix cores instead of
+                                 using projected queries, so basiskv_score_pages (which
+                                 takes projected queries) returns ERR_UNSUPPORTED; use
+                                 basiskv_score_pages_rope, basiskv_route_pages or
+                                 basiskv_decode_step.  Supported
+                                 for bf16 activations (bf16 or E4M3 pages), groups of 4
+                                 and 8 heads, routing widths (r_b, r_q) of (16, 16),
+                                 (64, 32), (96, 48), latent widths 64 and 96 (ERR_UNSUPPORTED
+                                 otherwise); not used by basiskv_dense_attend. */
 } basiskv_cache;
 
 /* Human-readable name of a status code (static storage). */
@@ -179,6 +198,22 @@ int32_t basiskv_project_queries(const basiskv_dims *dims, const void *q, const v
  *   page_scores [batch][n_kv_heads][max_pages_per_seq] float32 out. */
 int32_t basiskv_score_pages(const basiskv_dims *dims, const float *q_proj,
                             const basiskv_cache *cache, float *page_scores, void *stream);
+
+/* (a2) Page scores with rotary positions (cache->rope_inv_freq set; the
+ * pages' Figure 6 predicts the pre-RoPE Key): for every valid token t of
+ * page p, its predicted Key k_t = z_t[:r_b] P_g + r_t Q_g is rotated to
+ * position t, and
+ *   logit = q_bh . RoPE_t(k_t),
+ * page_scores[b][g][p] = max over the page's valid tokens and the group's
+ * heads; pages at or past ceil(seq_len / page_size) get -inf.
+ *   q [batch][n_q_heads][head_dim] (already rotated to its own position);
+ *   P [n_kv][r_b][head_dim];  Q [n_kv][r_q][head_dim];
+ *   page_scores [batch][n_kv_heads][max_pages_per_seq] float32 out.
+ * ERR_NULL without a frequency table; ERR_UNSUPPORTED outside the supported
+ * set listed at basiskv_cache.  No workspace. */
+int32_t basiskv_score_pages_rope(const basiskv_dims *dims, const void *q, const void *P,
+                                 const void *Q, const basiskv_cache *cache, float *page_scores,
+                                 void *stream);
 
 /* (a3) Top-k page selection per (sequence, KV head) (BasisKV abstract: only
  * the selected pages' Keys are fetched).  Exact: the top_k largest scores

@@ -24,7 +24,7 @@ EXPORTED = (
     "basiskv_route_pages", "basiskv_sparse_attend", "basiskv_reconstruct",
     "basiskv_decode_step", "basiskv_fuse_output_matrix", "basiskv_pack_output_matrix",
     "basiskv_dense_workspace_bytes", "basiskv_dense_attend", "basiskv_static_scratch_bytes",
-    "basiskv_decode_step_static",
+    "basiskv_decode_step_static", "basiskv_score_pages_rope",
 )
 
 
@@ -44,7 +44,7 @@ class Dims(ctypes.Structure):
 class Cache(ctypes.Structure):
     _fields_ = [("z_pages", ctypes.c_void_p), ("r_pages", ctypes.c_void_p),
                 ("k_pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("rope_inv_freq", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -65,6 +65,7 @@ def _lib():
             "basiskv_compress_prefill": (I32, [DP, P, P, P, I32, P, P, P, CP, P]),
             "basiskv_project_queries": (I32, [DP, P, P, P, P, P]),
             "basiskv_score_pages": (I32, [DP, P, CP, P, P]),
+            "basiskv_score_pages_rope": (I32, [DP, P, P, P, CP, P, P]),
             "basiskv_select_pages": (I32, [DP, P, P, I32, P, P]),
             "basiskv_route_pages": (I32, [DP, P, P, P, CP, I32, P, P, P, SZ, P]),
             "basiskv_sparse_attend": (I32, [DP, P, CP, P, I32, ctypes.c_float, P, P, SZ, P]),
@@ -114,12 +115,9 @@ def make_dims(*, batch, n_q_heads, n_kv_heads, head_dim, hidden, r_v, r_b, r_q, 
                 max_pages_per_seq, num_phys_pages, dtype, recent_tokens, page_layout)
 
 
-def make_cache(z_pages, r_pages, k_pages, block_table, seq_lens):
-    return Cache(_ptr(z_pages).value if z_pages is not None else None,
-                 _ptr(r_pages).value if r_pages is not None else None,
-                 _ptr(k_pages).value if k_pages is not None else None,
-                 _ptr(block_table).value if block_table is not None else None,
-                 _ptr(seq_lens).value if seq_lens is not None else None)
+def make_cache(z_pages, r_pages, k_pages, block_table, seq_lens, rope_inv_freq=None):
+    p = lambda t: _ptr(t).value if t is not None else None
+    return Cache(p(z_pages), p(r_pages), p(k_pages), p(block_table), p(seq_lens), p(rope_inv_freq))
 
 
 def workspace_bytes(dims, top_k):
@@ -143,6 +141,12 @@ def score_pages(dims, q_proj, cache, page_scores, stream=None):
     _check(_lib().basiskv_score_pages(ctypes.byref(dims), _ptr(q_proj), ctypes.byref(cache),
                                       _ptr(page_scores), _stream(stream)),
            "basiskv_score_pages")
+
+
+def score_pages_rope(dims, q, P, Q, cache, page_scores, stream=None):
+    _check(_lib().basiskv_score_pages_rope(ctypes.byref(dims), _ptr(q), _ptr(P), _ptr(Q),
+                                           ctypes.byref(cache), _ptr(page_scores), _stream(stream)),
+           "basiskv_score_pages_rope")
 
 
 def select_pages(dims, page_scores, seq_lens, top_k, sel, stream=None):

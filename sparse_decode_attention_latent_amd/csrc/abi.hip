@@ -9,7 +9,6 @@
 namespace bkv_host {
 size_t compress_lds(const basiskv_dims &d);
 bool score_supported(const basiskv_dims &d);
-bool attend_supported(const basiskv_dims &d);
 }
 
 namespace {
@@ -63,6 +62,14 @@ int32_t check_cache(const basiskv_dims &d, const basiskv_cache *c, bool need_k, 
   if ((need_k && !c->k_pages) || (need_z && !c->z_pages) || (need_r && !c->r_pages))
     return BASISKV_ERR_NULL;
   return BASISKV_OK;
+}
+
+bool has_rope(const basiskv_cache *c) { return c && c->rope_inv_freq; }
+
+// Routing of this cache is supported: projected queries, or (with RoPE) the
+// rotated predicted Keys.
+bool routing_supported(const basiskv_dims &d, const basiskv_cache *c) {
+  return has_rope(c) ? bkv_host::score_rope_supported(d) : bkv_host::score_supported(d);
 }
 
 // The routing factors a call needs: P when r_b > 0, Q (routing) and E
@@ -195,7 +202,9 @@ int32_t basiskv_score_pages(const basiskv_dims *d, const float *q_proj, const ba
   if (st) return st;
   if (!q_proj || !page_scores) return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, false, true, true))) return st;
-  if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  // with RoPE the logits depend on each token's position: projected queries
+  // cannot carry them (route_pages and decode_step take the raw queries)
+  if (has_rope(c) || !bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   bool unsupported = false;
   hipError_t e = bkv_host::launch_score(*d, q_proj, *c, page_scores, as_stream(stream),
                                         &unsupported);
@@ -212,6 +221,21 @@ int32_t basiskv_select_pages(const basiskv_dims *d, const float *page_scores,
   return launched(bkv_host::launch_select(*d, page_scores, seq_lens, top_k, sel, as_stream(stream)));
 }
 
+int32_t basiskv_score_pages_rope(const basiskv_dims *d, const void *q, const void *P,
+                                 const void *Q, const basiskv_cache *c, float *page_scores,
+                                 void *stream) {
+  int32_t st = check_dims(d);
+  if (st) return st;
+  if (!q || missing_factor(*d, P, Q) || !page_scores || !has_rope(c)) return BASISKV_ERR_NULL;
+  if ((st = check_cache(*d, c, false, true, true))) return st;
+  if (!bkv_host::score_rope_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  bool unsupported = false;
+  hipError_t e = bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, as_stream(stream),
+                                             &unsupported);
+  if (unsupported) return BASISKV_ERR_UNSUPPORTED;
+  return launched(e);
+}
+
 int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P, const void *Q,
                             const basiskv_cache *c, int32_t top_k, float *page_scores,
                             int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
@@ -220,14 +244,19 @@ int32_t basiskv_route_pages(const basiskv_dims *d, const void *q, const void *P,
   if (!q || missing_factor(*d, P, Q) || !page_scores || !sel) return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, false, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
+  if (!routing_supported(*d, c)) return BASISKV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < scratch_offset(*d) + qproj_bytes(*d)) return BASISKV_ERR_WORKSPACE;
-  if (!bkv_host::score_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
   float *q_proj = scratch_area(ws, *d);
   hipStream_t s = as_stream(stream);
   bool unsupported = false;
-  hipError_t e = bkv_host::launch_project(*d, q, P, Q, q_proj, s);
-  if (e != hipSuccess) return BASISKV_ERR_LAUNCH;
-  e = bkv_host::launch_score(*d, q_proj, *c, page_scores, s, &unsupported);
+  hipError_t e;
+  if (has_rope(c)) {
+    e = bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, s, &unsupported);
+  } else {
+    e = bkv_host::launch_project(*d, q, P, Q, q_proj, s);
+    if (e != hipSuccess) return BASISKV_ERR_LAUNCH;
+    e = bkv_host::launch_score(*d, q_proj, *c, page_scores, s, &unsupported);
+  }
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
   return launched(bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s));
 }
@@ -240,7 +269,7 @@ int32_t basiskv_sparse_attend(const basiskv_dims *d, const void *q, const basisk
   if (!q || !sel || !u) return BASISKV_ERR_NULL;
   if ((st = check_cache(*d, c, true, true, false))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
-  if (!bkv_host::attend_supported(*d)) return BASISKV_ERR_UNSUPPORTED;
+  if (!bkv_host::attend_supported(*d, has_rope(c))) return BASISKV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < scratch_offset(*d) + partial_bytes(*d, top_k))
     return BASISKV_ERR_WORKSPACE;
   bool unsupported = false;
@@ -278,7 +307,7 @@ int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_ne
   if ((st = check_cache(*d, c, true, true, true))) return st;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
   if (d->r_v > bkv::kHeadDim || d->r_q > bkv::kHeadDim) return BASISKV_ERR_UNSUPPORTED;
-  if (!bkv_host::score_supported(*d) || !bkv_host::attend_supported(*d))
+  if (!routing_supported(*d, c) || !bkv_host::attend_supported(*d, has_rope(c)))
     return BASISKV_ERR_UNSUPPORTED;
   if (!output_tiles_fit(*d)) return BASISKV_ERR_UNSUPPORTED;
   const size_t a = qproj_bytes(*d), b = partial_bytes(*d, top_k);
@@ -300,7 +329,9 @@ int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_n
   if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr,
                                      attend_counters(ws), n_counters, s) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
-  hipError_t e = bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported);
+  hipError_t e = has_rope(c)
+                     ? bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, s, &unsupported)
+                     : bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
   if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
@@ -372,7 +403,7 @@ int32_t basiskv_dense_attend(const basiskv_dims *d, const void *q, const void *k
   if (st) return st;
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return BASISKV_ERR_NULL;
   const basiskv_dims dd = dense_dims(*d);
-  if (!bkv_host::attend_supported(dd)) return BASISKV_ERR_UNSUPPORTED;
+  if (!bkv_host::attend_supported(dd, false)) return BASISKV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < scratch_offset(dd) + partial_bytes(dd, dd.max_pages_per_seq))
     return BASISKV_ERR_WORKSPACE;
   basiskv_cache c{};

@@ -48,6 +48,7 @@ struct AttendArgs {
   int32_t *counters;  // [batch * n_kv * gs], zero between calls (see the merge)
   uint16_t *u_tiles;  // optional: u also written as the reconstruction's A operand (bf16)
   PoolGeom geom;      // latent chunk positions within a page of the latent pool
+  const float *rope;  // RoPE inverse frequencies [head_dim / 2] (ROPE kernels only)
 };
 
 // Partial record per (b, h, split): [m, l, u[0..r_v)] with m in base-2 logit
@@ -75,11 +76,13 @@ struct AttendArgs {
 // leaving too few for the rest, and for float32 (a 128-register Key): these
 // take one wavefront per SIMD and its whole register file.  (E4M3 pages:
 // the Key takes 32 registers, the accumulators 16 per head.)
-template <typename C, int G, int NVC>
+// (RoPE kernels, whose rotation keeps the Key and its angles live, take one
+// wavefront per SIMD too.)
+template <typename C, int G, int NVC, bool ROPE = false>
 constexpr int attend_waves_per_eu() {
   constexpr int nj = (kWave + kWave / NVC - 1) / (kWave / NVC);
   constexpr int ce = Elem<C>::CE;
-  return sizeof(C) == 4 || (kHeadDim / ce) * 4 + 4 * nj + ce * G >= 170
+  return ROPE || sizeof(C) == 4 || (kHeadDim / ce) * 4 + 4 * nj + ce * G >= 170
              ? 1 : BKV_ATTEND_WAVES_PER_EU;
 }
 
@@ -92,8 +95,11 @@ typedef float attend_f4 __attribute__((ext_vector_type(4)));
 // (used where every load instruction reads whole 128-byte lines and no other
 // workgroup reads the same pages: pages of 8 or more tokens, one query
 // subgroup per KV head).
-template <typename T, typename C, int G, int NVC, int NB, bool STREAM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<C, G, NVC>())))
+// ROPE: the cached Keys are pre-RoPE; each is rotated to its token's position
+// (rotate-half pairs d, d + head_dim / 2, which a lane holds in chunks c and
+// c + NKC / 2) before the float32 scores.
+template <typename T, typename C, int G, int NVC, int NB, bool STREAM, bool ROPE = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu<C, G, NVC, ROPE>())))
 void attend_split_kernel(
     const T *__restrict__ q, const C *__restrict__ kpool, const C *__restrict__ zpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -108,8 +114,8 @@ void attend_split_kernel(
   constexpr bool kBf = sizeof(T) == 2;
   constexpr bool kFp8 = sizeof(C) == 1;
   static_assert(sizeof(C) == sizeof(T) || (kBf && kFp8), "E4M3 pages go with bf16 queries");
-  constexpr bool kMfma = kBf;            // scores on the matrix cores
-  constexpr bool kStream = kBf;          // next block's gathers overlap this block
+  constexpr bool kMfma = kBf && !ROPE;   // scores on the matrix cores
+  constexpr bool kStream = kBf && !ROPE; // next block's gathers overlap this block
   constexpr int QG = (G + 3) / 4;        // head quads (matrix-instruction row sets)
   constexpr int NQC = kHeadDim / 8;      // 8-dim bf16 query chunks
 
@@ -117,6 +123,7 @@ void attend_split_kernel(
   // else [head][dims] (float32)
   __shared__ __align__(16) uint4 qa_lds[kMfma ? QG * NQC * 4 : 1];
   __shared__ __align__(16) float q_lds[kMfma ? 1 : G][kMfma ? 4 : kHeadDim];
+  __shared__ float w_lds[ROPE ? kHeadDim / 2 : 1];  // RoPE inverse frequencies
   __shared__ float p_lds[NW][G][kWave];
   __shared__ float m_lds[NW][G];
   __shared__ float l_lds[NW][G];
@@ -186,6 +193,10 @@ void attend_split_kernel(
         qa_lds[i] = h < G ? *reinterpret_cast<const uint4 *>(qg + h * kHeadDim + c * 8)
                           : make_uint4(0u, 0u, 0u, 0u);
       }
+    } else if constexpr (ROPE) {  // float32 queries, and the rotation's frequencies
+      for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x)
+        q_lds[i / kHeadDim][i % kHeadDim] = to_f32(qg[i]);
+      for (int i = threadIdx.x; i < kHeadDim / 2; i += blockDim.x) w_lds[i] = a.rope[i];
     } else {
       constexpr int QW = G * kHeadDim * (int)sizeof(T) / 4;  // 32-bit words
       constexpr int QL = (QW + 255) / 256;
@@ -327,6 +338,35 @@ void attend_split_kernel(
       for (int h = 0; h < G; ++h) {
         const float dot = sc[h / 4][0][h % 4] + sc[h / 4][1][h % 4];
         s[h] = valid ? dot * a.scale_log2 : -INFINITY;
+      }
+    } else if constexpr (ROPE) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = -INFINITY;
+      if (valid) {
+        const int pos = page[i] * a.page_size + slot;  // the token's position in its sequence
+        constexpr int HALF = NKC / 2;
+        float dot[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) dot[h] = 0.f;
+#pragma unroll
+        for (int c = 0; c < HALF; ++c) {
+          float x[CE], y[CE];
+          unpack_chunk<C>(kc[c], x);
+          unpack_chunk<C>(kc[c + HALF], y);
+#pragma unroll
+          for (int e = 0; e < CE; ++e) {
+            const int d = c * CE + e;
+            float sn, cs;
+            rope_sincos(pos, w_lds[d], sn, cs);
+            const float xr = x[e] * cs - y[e] * sn;
+            const float yr = x[e] * sn + y[e] * cs;
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+              dot[h] = fmaf(q_lds[h][d], xr, fmaf(q_lds[h][d + kHeadDim / 2], yr, dot[h]));
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[h] = dot[h] * a.scale_log2;
       }
     } else {
 #pragma unroll
@@ -579,6 +619,22 @@ static const AttendVariant kAttendVariants[] = {
     BKV_ATT_G(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 128),
 };
 
+// RoPE variants: pre-RoPE Keys rotated to their positions (float32 scores)
+#define BKV_ATT_ROPE(T, C, DT, G, RV)                                                                 \
+  {DT, G, RV,                                                                                         \
+   reinterpret_cast<const void *>(&attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, 1, false, true>), \
+   reinterpret_cast<const void *>(                                                                    \
+       &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, false, true>),                \
+   nullptr}
+static const AttendVariant kAttendRopeVariants[] = {
+    BKV_ATT_ROPE(uint16_t, uint16_t, BASISKV_BF16, 4, 64),
+    BKV_ATT_ROPE(uint16_t, uint16_t, BASISKV_BF16, 4, 96),
+    BKV_ATT_ROPE(uint16_t, uint16_t, BASISKV_BF16, 8, 64),
+    BKV_ATT_ROPE(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 4, 64),
+    BKV_ATT_ROPE(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 4, 96),
+    BKV_ATT_ROPE(uint16_t, uint8_t, BASISKV_BF16_FP8_E4M3, 8, 64),
+};
+
 }  // namespace bkv
 
 namespace bkv_host {
@@ -642,20 +698,26 @@ int attend_splits(const basiskv_dims &d, int32_t top_k) {
   return (n + pps - 1) / pps;
 }
 
-static const AttendVariant *find_attend(const basiskv_dims &d) {
+static const AttendVariant *find_attend(const basiskv_dims &d, bool rope) {
   const int G = d.n_q_heads / d.n_kv_heads;
   const int gs = attend_group_split(d);
+  if (rope) {
+    for (const auto &v : kAttendRopeVariants)
+      if (v.dtype == d.dtype && v.G == G / gs && v.rv == d.r_v) return &v;
+    return nullptr;
+  }
   for (const auto &v : kAttendVariants)
     if (v.dtype == d.dtype && v.G == G / gs && v.rv == d.r_v) return &v;
   return nullptr;
 }
 
-bool attend_supported(const basiskv_dims &d) { return find_attend(d) != nullptr; }
+bool attend_supported(const basiskv_dims &d, bool rope) { return find_attend(d, rope) != nullptr; }
 
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
                          const int32_t *sel, int32_t top_k, float scale, float *u, float *part,
                          int32_t *counters, uint16_t *u_tiles, hipStream_t s, bool *unsupported) {
-  const AttendVariant *v = find_attend(d);
+  const bool rope = sel != nullptr && c.rope_inv_freq != nullptr;  // (the dense baseline has none)
+  const AttendVariant *v = find_attend(d, rope);
   if (!v) {
     *unsupported = true;
     return hipSuccess;
@@ -684,6 +746,7 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.counters = counters;
   a.u_tiles = u_tiles;
   a.geom = pool_geom(d);
+  a.rope = rope ? c.rope_inv_freq : nullptr;
   void *args[] = {(void *)&q,           (void *)&c.k_pages,  (void *)&c.z_pages,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&sel,
                   (void *)&part,        (void *)&u,          (void *)&a};

@@ -130,6 +130,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// Rotary position embedding: sin and cos of the angle pos * w.  The product
+// is taken in double precision (exact for positions below 2^24 and float32
+// frequencies), reduced to a fraction of a turn, and evaluated by the
+// hardware sine and cosine, which take turns (v_sin_f32 / v_cos_f32).
+__device__ __forceinline__ void rope_sincos(int pos, float w, float &sn, float &cs) {
+  const double turns = (double)pos * (double)w * 0.15915494309189535;  // 1 / (2 pi)
+  const float f = (float)(turns - floor(turns));
+  sn = __builtin_amdgcn_sinf(f);
+  cs = __builtin_amdgcn_cosf(f);
+}
+
 __device__ __forceinline__ uint4 load_chunk(const void *base_bytes, int64_t byte_off) {
   return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(base_bytes) + byte_off);
 }
@@ -332,6 +343,11 @@ hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, c
                           float *q_proj, hipStream_t s);
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
                         float *scores, hipStream_t s, bool *unsupported);
+bool score_rope_supported(const basiskv_dims &d);
+hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P, const void *Q,
+                             const basiskv_cache &c, float *scores, hipStream_t s,
+                             bool *unsupported);
+bool attend_supported(const basiskv_dims &d, bool rope);
 hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s);
 int attend_splits(const basiskv_dims &d, int32_t top_k);

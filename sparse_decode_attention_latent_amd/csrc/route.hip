@@ -241,6 +241,166 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// (a2) page scores with rotary position embedding.  The cached codes are
+// pre-RoPE, so the projected-query shortcut does not apply: the predicted Key
+// of every token is formed, k_hat = [z[:r_b], r] [P; Q] (dims x 128), rotated
+// to the token's position and dotted with the group's queries.
+//
+// Per wavefront: 64 tokens, taken as four 16-token tiles.  For a tile, one
+// v_mfma_f32_16x16x32_bf16 per 32 codes and 16 Key dims: A = the tokens'
+// codes (lane l: token l % 16, codes 8 (l / 16) .. + 7 of the k step -- one
+// 8-element run of a page chunk, widened from E4M3 when the cache is FP8),
+// B = [P; Q]^T staged in LDS (lane l: dim l % 16, the same 8 codes).  The
+// result puts dim 16 nt + l % 16 of tokens 4 (l / 16) .. + 3 in lane l for
+// Key tile nt, so the rotate-half pair (d, d + 64) -- tiles nt and nt + 4 -- is
+// lane-local.  The query dot products are summed over the 16 lanes of a row;
+// token logits go through LDS to the page maxima.
+// grid and work items as route_scan_kernel; q: the raw (rotated) queries.
+// ---------------------------------------------------------------------------
+template <typename C, int G, int NZ, int NR>
+__global__ __launch_bounds__(256) void route_rope_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ P, const uint16_t *__restrict__ Q,
+    const float *__restrict__ inv_freq, const C *__restrict__ zpool, const C *__restrict__ rpool,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
+    float *__restrict__ scores, ScoreArgs a) {
+  constexpr int CE = Elem<C>::CE;        // cache elements per 16-byte chunk
+  constexpr int RB = NZ * CE, RQ = NR * CE, W = RB + RQ;
+  constexpr int KS = (W + 31) / 32;      // 32-code k steps
+  constexpr int KP = KS * 32;
+  constexpr int FS = KP + 8;             // LDS row stride of [P;Q]^T (16-byte pad)
+  typedef __bf16 rb16x8 __attribute__((ext_vector_type(8)));
+  typedef float rf4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint16_t ft[kHeadDim * FS];   // [dim][code]
+  __shared__ float qs[G][kHeadDim];
+  __shared__ float ws[kHeadDim / 2];
+  __shared__ float tok_score[4][kWave];
+
+  const int work = xcd_work_index(a.padded);
+  if (work >= a.total) return;
+  const int bg = work / a.chunks_per_bg;
+  const int chunk = work - bg * a.chunks_per_bg;
+  const int b = bg / a.n_kv, g = bg - b * a.n_kv;
+  const int L = clamp_len(seq_lens[b], a.cap);
+  const int NP = (L + a.page_size - 1) >> a.log2_page;
+  const int p_begin = chunk * a.pages_per_wg;
+  const int p_end = min(a.max_pages, p_begin + a.pages_per_wg);
+  const int ppi = kWave >> a.log2_page;
+  const int n_steps = (p_end - p_begin + ppi - 1) / ppi;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int slot = lane & (a.page_size - 1);
+  const int64_t zhead = (int64_t)g * a.num_phys;
+  const int64_t page_z_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
+  const int64_t page_r_bytes = (int64_t)a.geom.r_page_chunks * a.page_size * 16;
+
+  // this lane's token (lane = token of the wavefront's 64-token step)
+  const bool has_step = wave < n_steps;
+  const int p = p_begin + wave * ppi + (lane >> a.log2_page);
+  const bool in_range = has_step && p < p_end;
+  int phys = -1;
+  if (in_range && p < NP) phys = block_table[(int64_t)b * a.max_pages + p];
+  const bool valid = in_range && p < NP && p * a.page_size + slot < L && phys >= 0 &&
+                     phys < a.num_phys;
+
+  // ---- stage [P_g; Q_g]^T (bf16, zero past W), the queries and the frequencies ----
+  for (int o = threadIdx.x; o < kHeadDim * KP; o += blockDim.x) {
+    const int k = o / kHeadDim, n = o % kHeadDim;  // consecutive threads: consecutive dims
+    uint16_t v = 0;
+    if (k < RB) v = P[((int64_t)g * RB + k) * kHeadDim + n];
+    else if (k < W) v = Q[((int64_t)g * RQ + (k - RB)) * kHeadDim + n];
+    ft[n * FS + k] = v;
+  }
+  for (int o = threadIdx.x; o < G * kHeadDim; o += blockDim.x)
+    qs[o / kHeadDim][o % kHeadDim] = bf16_to_f32(q[((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim + o]);
+  for (int o = threadIdx.x; o < kHeadDim / 2; o += blockDim.x) ws[o] = inv_freq[o];
+  __syncthreads();
+  if (!has_step) return;  // (no barrier below)
+
+  const int li = lane & 15, lg = lane >> 4;
+  for (int mt = 0; mt < 4; ++mt) {
+    // A fragments: token mt * 16 + li (its page and slot from the lane that owns it)
+    const int tok = mt * 16 + li;
+    const int ph = __shfl(phys, tok);
+    const int tv = __shfl((int)valid, tok);
+    const int tslot = tok & (a.page_size - 1);
+    rb16x8 af[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c8 = ks * 4 + lg;  // 8-code run index
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (tv && c8 * 8 < W) {
+        const int code0 = c8 * 8;
+        const bool in_z = code0 < RB;
+        const int cc = in_z ? code0 / CE : (code0 - RB) / CE;  // chunk of its pool
+        const int half = (code0 % CE) / 8;                      // E4M3: which half of the chunk
+        const int64_t off = in_z
+            ? (zhead + ph) * page_z_bytes + ((int64_t)cc * a.page_size + tslot) * 16
+            : (zhead + ph) * page_r_bytes + ((int64_t)(a.geom.r_first + cc) * a.page_size + tslot) * 16;
+        const char *base = reinterpret_cast<const char *>(in_z ? (const void *)zpool : (const void *)rpool);
+        if constexpr (sizeof(C) == 1) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(base + off + half * 8);
+          v = fp8x8_to_bf16x8(w.x, w.y);
+        } else {
+          v = *reinterpret_cast<const uint4 *>(base + off);
+        }
+      }
+      af[ks] = __builtin_bit_cast(rb16x8, v);
+    }
+    // predicted Keys of the tile: dims 16 nt + li, tokens 4 lg .. 4 lg + 3
+    rf4 kh[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      kh[nt] = rf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 bv = *reinterpret_cast<const uint4 *>(&ft[(nt * 16 + li) * FS + ks * 32 + lg * 8]);
+        kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(rb16x8, bv),
+                                                         kh[nt], 0, 0, 0);
+      }
+    }
+    // rotate each token's pairs to its position, then the query dot products
+    float part[4][G];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = mt * 16 + lg * 4 + r;         // token within the step
+      const int pos = (p_begin + wave * ppi) * a.page_size + t;
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[r][h] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int d = nt * 16 + li;
+        float sn, cs;
+        rope_sincos(pos, ws[d], sn, cs);
+        const float x = kh[nt][r], y = kh[nt + 4][r];
+        const float xr = x * cs - y * sn, yr = x * sn + y * cs;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          part[r][h] = fmaf(qs[h][d], xr, fmaf(qs[h][d + kHeadDim / 2], yr, part[r][h]));
+      }
+    }
+    // sums over the 16 lanes of a row (every lane of the row gets them), and
+    // the maximum over the group's heads
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float best = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float v = part[r][h];
+        v += dpp_move<0xB1>(v);
+        v += dpp_move<0x4E>(v);
+        v += dpp_move<0x141>(v);
+        v += dpp_move<0x140>(v);
+        best = fmaxf(best, v);
+      }
+      if (li == 0) tok_score[wave][mt * 16 + lg * 4 + r] = best;
+    }
+  }
+  wave_lds_sync();
+  float best = valid ? tok_score[wave][lane] : -INFINITY;
+  best = group_max(best, a.page_size);
+  if (in_range && slot == 0) scores[(int64_t)bg * a.max_pages + p] = (p < NP) ? best : -INFINITY;
+}
+
 template <typename T>
 hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                      float *q_proj, hipStream_t s) {
@@ -307,6 +467,25 @@ static const ScoreVariant kScoreVariants[] = {
     BKV_SCORE_G(uint8_t, BASISKV_BF16_FP8_E4M3, 0, 32),
 };
 
+struct ScoreRopeVariant {
+  int dtype, G, rb, rq;
+  const void *fn;
+};
+#define BKV_SCORE_ROPE(C, DT, G, RB, RQ) \
+  {DT, G, RB, RQ,                         \
+   reinterpret_cast<const void *>(&route_rope_kernel<C, G, (RB) / Elem<C>::CE, (RQ) / Elem<C>::CE>)}
+static const ScoreRopeVariant kScoreRopeVariants[] = {
+    BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 4, 16, 16), BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 8, 16, 16),
+    BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 4, 64, 32), BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 8, 64, 32),
+    BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 4, 96, 48), BKV_SCORE_ROPE(uint16_t, BASISKV_BF16, 8, 96, 48),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 4, 16, 16),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 8, 16, 16),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 4, 64, 32),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 8, 64, 32),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 4, 96, 48),
+    BKV_SCORE_ROPE(uint8_t, BASISKV_BF16_FP8_E4M3, 8, 96, 48),
+};
+
 }  // namespace bkv
 
 namespace bkv_host {
@@ -333,6 +512,47 @@ static const void *find_score(const basiskv_dims &d) {
 }
 
 bool score_supported(const basiskv_dims &d) { return find_score(d) != nullptr; }
+
+static const void *find_score_rope(const basiskv_dims &d) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  for (const auto &v : kScoreRopeVariants)
+    if (v.dtype == d.dtype && v.G == G && v.rb == d.r_b && v.rq == d.r_q) return v.fn;
+  return nullptr;
+}
+
+bool score_rope_supported(const basiskv_dims &d) { return find_score_rope(d) != nullptr; }
+
+// Page scores with RoPE from the raw queries and the routing factors.
+hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P, const void *Q,
+                             const basiskv_cache &c, float *scores, hipStream_t s,
+                             bool *unsupported) {
+  const void *fn = find_score_rope(d);
+  if (!fn) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  *unsupported = false;
+  ScoreArgs a;
+  a.n_q = d.n_q_heads;
+  a.n_kv = d.n_kv_heads;
+  a.max_pages = d.max_pages_per_seq;
+  a.num_phys = d.num_phys_pages;
+  a.page_size = d.page_size;
+  a.log2_page = ilog2(d.page_size);
+  a.geom = pool_geom(d);
+  a.cap = d.max_pages_per_seq * d.page_size;
+  const int ppi = 64 / d.page_size;
+  a.pages_per_wg = ppi * 4;
+  a.chunks_per_bg = (d.max_pages_per_seq + a.pages_per_wg - 1) / a.pages_per_wg;
+  a.total = d.batch * d.n_kv_heads * a.chunks_per_bg;
+  a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
+  void *rpool = residual_pool(d, c);
+  const float *w = c.rope_inv_freq;
+  void *args[] = {(void *)&q,         (void *)&P,           (void *)&Q,
+                  (void *)&w,         (void *)&c.z_pages,   (void *)&rpool,
+                  (void *)&c.block_table, (void *)&c.seq_lens, (void *)&scores, (void *)&a};
+  return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
+}
 
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
                         float *scores, hipStream_t s, bool *unsupported) {

@@ -129,8 +129,10 @@ class DecodeProblem:
             self.k_new, self.v_new = rnd(B, 1, Hkv, dh), rnd(B, 1, Hkv, dh)
         self.seq_lens = torch.from_numpy(self.seq_lens_host).to(dev)
         self.start_pos = (self.seq_lens - 1).to(torch.int32)
+        freqs = synth.rope_frequencies(wl)  # rotary positions: pre-RoPE caches
+        self.rope_inv_freq = None if freqs is None else torch.from_numpy(freqs).to(dev)
         self.cache = api.make_cache(self.z_pages, self.r_pages, self.k_pages, self.block_table,
-                                    self.seq_lens)
+                                    self.seq_lens, self.rope_inv_freq)
         tdt = torch.bfloat16 if st == "bf16" else torch.float32
         self.M = torch.empty((wl.hidden, Hq * wl.r_v), dtype=tdt, device=dev)
         api.fuse_output_matrix(self.dims, self.fac["Bf"], self.fac["W_O"], self.M)
@@ -153,7 +155,11 @@ class DecodeProblem:
         api.project_queries(self.dims, self.q, self.fac["P"], self.fac["Q"], self.q_proj)
 
     def score(self):
-        api.score_pages(self.dims, self.q_proj, self.cache, self.page_scores)
+        if self.rope_inv_freq is not None:  # predicted Keys rotated: scored from the raw queries
+            api.score_pages_rope(self.dims, self.q, self.fac["P"], self.fac["Q"], self.cache,
+                                 self.page_scores)
+        else:
+            api.score_pages(self.dims, self.q_proj, self.cache, self.page_scores)
 
     def select(self):
         api.select_pages(self.dims, self.page_scores, self.seq_lens, self.top_k, self.sel)
@@ -187,10 +193,12 @@ class DecodeProblem:
         self.reconstruct()
 
     def step_unfused(self, append=True):
-        """The same step with routing as its three separate calls."""
+        """The same step with routing as its separate calls (three; with RoPE,
+        no projection call: scoring takes the raw queries)."""
         if append:
             self.append()
-        self.project()
+        if self.rope_inv_freq is None:
+            self.project()
         self.score()
         self.select()
         self.attend()

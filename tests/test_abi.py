@@ -240,7 +240,7 @@ def test_single_source_router_dims():
     lib = api.lib()
     both = dims_of(WORKLOADS[2], r_b=0, r_q=0)
     assert lib.basiskv_project_queries(ctypes.byref(both), FAKE, FAKE, FAKE, FAKE, None) == 2
-    b_only = dims_of(WORKLOADS[2], r_q=0)
+    b_only = dims_of(WORKLOADS[2], r_b=16, r_q=0)  # the B16 router of Table 9
     r_only = dims_of(WORKLOADS[2], r_b=0)
     c_no_r = _cache(r_pages=None)
     # B-only: Q (and the residual pool) unused
@@ -259,3 +259,30 @@ def test_single_source_router_dims():
                                         ctypes.byref(c_no_r), None) == 1  # P needed when r_b > 0
     for d in (b_only, r_only):
         assert api.workspace_bytes(d, 16) > 0
+
+
+@needs_lib
+def test_rope_cache_support_is_reported_before_launch():
+    """A cache with a RoPE frequency table: the scores-only call does not take
+    positions (it returns UNSUPPORTED rather than unrotated scores); routing
+    and the whole step accept bf16 and E4M3 pages and refuse float32 ones."""
+    lib = api.lib()
+    rope = _cache(rope_inv_freq=0x1000)
+    d = dims_of(WORKLOADS[2])
+    assert lib.basiskv_score_pages(ctypes.byref(d), FAKE, ctypes.byref(rope), FAKE, None) == 3
+    assert lib.basiskv_score_pages(ctypes.byref(d), FAKE, ctypes.byref(_cache()), FAKE, None) != 3
+    # the scores-only RoPE call: needs the table, P and Q; float32 pages unsupported
+    assert lib.basiskv_score_pages_rope(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(_cache()),
+                                        FAKE, None) == 1
+    assert lib.basiskv_score_pages_rope(ctypes.byref(d), FAKE, None, FAKE, ctypes.byref(rope),
+                                        FAKE, None) == 1
+    assert lib.basiskv_score_pages_rope(ctypes.byref(dims_of(WORKLOADS[0])), FAKE, FAKE, FAKE,
+                                        ctypes.byref(rope), FAKE, None) == 3
+    assert lib.basiskv_score_pages_rope(ctypes.byref(dims_of(WORKLOADS[2], n_q_heads=24)), FAKE, FAKE,
+                                        FAKE, ctypes.byref(rope), FAKE, None) == 3
+    for dd, code in ((d, 4), (dims_of(WORKLOADS[2], dtype=api.BF16_FP8), 4), (dims_of(WORKLOADS[0]), 3)):
+        assert lib.basiskv_route_pages(ctypes.byref(dd), FAKE, FAKE, FAKE, ctypes.byref(rope), 8,
+                                       FAKE, FAKE, FAKE, 16, None) == code
+        assert lib.basiskv_decode_step(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, ctypes.byref(rope), 8, 0.1, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, 64, None) == code

@@ -108,7 +108,8 @@ def test_prefill_decode_128k_decode_step_full():
                                   "llama8b-prefill-decode-128k", "llama8b-ctx32k-b16r16-page4",
                                   "llama8b-ctx32k-fp8", "llama8b-ctx32k-b16r16-page4-fp8",
                                   "llama8b-ctx32k-b16-page4", "llama8b-ctx32k-r16-page4",
-                                  "llama8b-ctx32k-r32-page4"])
+                                  "llama8b-ctx32k-r32-page4", "llama8b-ctx32k-b16r16-page4-rope",
+                                  "llama8b-ctx32k-rope"])
 def test_decode_step_full_size_every_sequence(name):
     """The call bench.py times, basiskv_decode_step, at the workload's full
     size and in the launch configuration the benchmark uses (the same seeded
@@ -412,6 +413,69 @@ def test_compress_prefill_single_source(rb, rq, cache):
                 r_exact = ref.residual_code(kb[:, g], zgv, P[g], E[g], rb)
                 assert parity.rounding_valid(got["r"][b, g], r_exact, cache).all(), f"b={b} g={g}: residual"
     _say(f"  compress r_b={rb} r_q={rq} {cache}: every token valid")
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding: pre-RoPE caches, predicted and exact Keys rotated
+# to their positions (the pages' Figure 6 caption; reading in oracle/basiskv_ref.py)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,cache", [
+    ("llama8b-ctx32k-b16r16-page4-rope", "bf16"), ("llama8b-ctx32k-b16r16-page4-rope", "fp8"),
+    ("llama8b-ctx32k-rope", "bf16"), ("llama8b-ctx32k-rope", "fp8"), ("qwen32b-rope", "bf16")])
+def test_rope_ragged(name, cache):
+    """Ragged lengths (a partial last page, a sequence shorter than one scoring
+    tile, a one-token sequence) with positions up to 4095."""
+    wl = workload(name) if name != "qwen32b-rope" else workload(3).with_(rope_theta=1000000.0)
+    if cache == "fp8":
+        wl = wl.with_(cache_storage="fp8")
+    top_k = None if wl.page_size == 4 else 16
+    run_case(wl, batch=4, ctx=4096, seq_lens=[4096, 4093, 50, 1], top_k=top_k)
+
+
+@pytest.mark.parametrize("name", ["llama8b-ctx32k-b16r16-page4-rope", "llama8b-ctx32k-rope"])
+def test_rope_separate_calls_equal_routing(name):
+    """basiskv_score_pages_rope + basiskv_select_pages give route_pages'
+    scores and selection bit for bit, and the rest of the step follows."""
+    wl = workload(name)
+    inp = synth.decode_inputs(wl, batch=3, ctx=4096, seq_lens=[4096, 2049, 31])
+    prob = DecodeProblem(wl, inp)
+    prob.step(append=True)
+    a = prob.outputs()
+    for t in (prob.page_scores, prob.u):
+        t.fill_(float("nan"))
+    prob.sel.fill_(-7)
+    prob.step_unfused(append=False)
+    b = prob.outputs()
+    for key in ("scores", "sel", "u", "y"):
+        np.testing.assert_array_equal(b[key], a[key], err_msg=key)
+
+
+def test_rope_long_positions():
+    """Positions up to 131071: rotation angles of the highest frequency reach
+    about 1.3e5 radians, where the turn count has to be reduced exactly."""
+    wl = workload(4).with_(rope_theta=500000.0, n_planted=8, planted="random")
+    run_case(wl, seq_lens=[131072, 98305])
+
+
+def test_rope_zero_frequencies_equal_no_rope():
+    """An all-zero frequency table rotates nothing: the RoPE kernels give the
+    position-free kernels' selection, and their scores and u within the parity
+    tolerances (the two sum in different orders)."""
+    wl = workload("llama8b-ctx32k-b16r16-page4")
+    inp = synth.decode_inputs(wl, batch=2, ctx=2048, seq_lens=[2048, 777])
+    plain = DecodeProblem(wl, inp)
+    plain.decode_step()
+    a = plain.outputs()
+    zero = DecodeProblem(wl, inp)
+    zero.rope_inv_freq = torch.zeros(wl.head_dim // 2, dtype=torch.float32, device="cuda")
+    zero.cache = api.make_cache(zero.z_pages, zero.r_pages, zero.k_pages, zero.block_table,
+                                zero.seq_lens, zero.rope_inv_freq)
+    zero.decode_step()
+    b = zero.outputs()
+    np.testing.assert_array_equal(b["sel"], a["sel"])
+    np.testing.assert_allclose(b["scores"], a["scores"], rtol=parity.SCORE_RTOL, atol=0)
+    np.testing.assert_allclose(b["u"], a["u"], rtol=0, atol=parity.U_RTOL * np.abs(a["u"]).max())
 
 
 # ---------------------------------------------------------------------------
