@@ -174,8 +174,9 @@ def measured_traffic(workload_name, kernel="route_scan_kernel"):
 def cpu_baseline(wl, inp, target_seconds):
     """The float64 oracle, as it stands, on whole sequences of the workload,
     cycling over the batch until about target_seconds have passed (at least
-    one sequence)."""
-    from threadpoolctl import threadpool_info
+    one sequence).  BLAS runs with one thread per core this process may use
+    (its CPU affinity set); the CPU model is recorded beside the figure."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import basiskv_ref as ref
     from sparse_decode_attention_latent_amd import traffic
@@ -191,6 +192,8 @@ def cpu_baseline(wl, inp, target_seconds):
              for k in ("q", "z", "r", "kc", "k_new", "v_new")}
         x["L"] = inp["seq_lens"][b:b + 1]
         seqs.append(x)
+    n_cores = len(os.sched_getaffinity(0))
+    limiter = threadpool_limits(limits=n_cores, user_api="blas")
     done, elapsed, nbytes = 0, 0.0, 0
     while elapsed < target_seconds or done == 0:
         x = seqs[done % B]
@@ -204,12 +207,27 @@ def cpu_baseline(wl, inp, target_seconds):
         nbytes += traffic.step_bytes(one, x["L"])["total"]
         done += 1
     threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    limiter.unregister()
     return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s",
-            "cores": max(threads) if threads else 1, "kind": "oracle",
+            "cores": max(threads) if threads else 1, "affinity_cores": n_cores,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} single-sequence decode steps (append, route, select, attend, "
                       f"reconstruct) cycling over the {B} sequences of the same workload, "
                       f"float64 numpy oracle, {elapsed:.1f} s",
             "us_per_layer_equiv": round(elapsed / done * B * 1e6, 1)}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cold_steps(prob, n, flush_bytes=FLUSH_BYTES):

@@ -247,16 +247,26 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 // of every token is formed, k_hat = [z[:r_b], r] [P; Q] (dims x 128), rotated
 // to the token's position and dotted with the group's queries.
 //
-// Per wavefront: 64 tokens, taken as four 16-token tiles.  For a tile, one
-// v_mfma_f32_16x16x32_bf16 per 32 codes and 16 Key dims: A = the tokens'
-// codes (lane l: token l % 16, codes 8 (l / 16) .. + 7 of the k step -- one
-// 8-element run of a page chunk, widened from E4M3 when the cache is FP8),
-// B = [P; Q]^T staged in LDS (lane l: dim l % 16, the same 8 codes).  The
-// result puts dim 16 nt + l % 16 of tokens 4 (l / 16) .. + 3 in lane l for
-// Key tile nt, so the rotate-half pair (d, d + 64) -- tiles nt and nt + 4 -- is
-// lane-local.  The query dot products are summed over the 16 lanes of a row;
-// token logits go through LDS to the page maxima.
-// grid and work items as route_scan_kernel; q: the raw (rotated) queries.
+// A wavefront takes 64-token steps (a page-aligned run of pages), each as
+// four 16-token tiles.  For a tile, one v_mfma_f32_16x16x32_bf16 per 32 codes
+// and 16 Key dims: A = the tokens' codes (lane l: token l % 16, codes
+// 8 (l / 16) .. + 7 of the k step -- one 8-element run of a page chunk, widened
+// from E4M3 when the cache is FP8), B = [P; Q]^T (lane l: dim l % 16, the same
+// 8 codes).  The result puts dim 16 nt + l % 16 of tokens 4 (l / 16) .. + 3 in
+// lane l for Key tile nt, so the rotate-half pair (d, d + 64) -- tiles nt and
+// nt + 4 -- is lane-local.  The query dot products are summed over the 16
+// lanes of a row; token logits go through LDS to the page maxima.
+//
+// [P; Q]^T is staged in LDS once per workgroup and, for up to 96 codes, held
+// in registers by every wave; the queries' dims are held in registers too.  A
+// workgroup covers pages_per_wg pages, i.e. several steps per wave, so the
+// staging is shared by many tokens, and each wave loads the codes of its next
+// step while it computes the current one.  Angles: for every tile and
+// frequency one exact sine / cosine at the lane's first token (turns reduced
+// in double precision), then the next three positions by the one-position
+// rotation (cos w, sin w) -- three products per step, float32 rounding.
+// grid: (batch x n_kv x chunks), XCD-major; 256 threads; q: the raw
+// (rotated) queries.
 // ---------------------------------------------------------------------------
 template <typename C, int G, int NZ, int NR>
 __global__ __launch_bounds__(256) void route_rope_kernel(
@@ -269,11 +279,11 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
   constexpr int KS = (W + 31) / 32;      // 32-code k steps
   constexpr int KP = KS * 32;
   constexpr int FS = KP + 8;             // LDS row stride of [P;Q]^T (16-byte pad)
+  constexpr bool kRegB = KS <= 3;        // factor fragments held in registers
   typedef __bf16 rb16x8 __attribute__((ext_vector_type(8)));
   typedef float rf4 __attribute__((ext_vector_type(4)));
   __shared__ __align__(16) uint16_t ft[kHeadDim * FS];   // [dim][code]
   __shared__ float qs[G][kHeadDim];
-  __shared__ float ws[kHeadDim / 2];
   __shared__ float tok_score[4][kWave];
 
   const int work = xcd_work_index(a.padded);
@@ -285,24 +295,16 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
   const int NP = (L + a.page_size - 1) >> a.log2_page;
   const int p_begin = chunk * a.pages_per_wg;
   const int p_end = min(a.max_pages, p_begin + a.pages_per_wg);
-  const int ppi = kWave >> a.log2_page;
+  const int ppi = kWave >> a.log2_page;  // pages per 64-token step
   const int n_steps = (p_end - p_begin + ppi - 1) / ppi;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int slot = lane & (a.page_size - 1);
   const int64_t zhead = (int64_t)g * a.num_phys;
   const int64_t page_z_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
   const int64_t page_r_bytes = (int64_t)a.geom.r_page_chunks * a.page_size * 16;
+  float *out = scores + (int64_t)bg * a.max_pages;
 
-  // this lane's token (lane = token of the wavefront's 64-token step)
-  const bool has_step = wave < n_steps;
-  const int p = p_begin + wave * ppi + (lane >> a.log2_page);
-  const bool in_range = has_step && p < p_end;
-  int phys = -1;
-  if (in_range && p < NP) phys = block_table[(int64_t)b * a.max_pages + p];
-  const bool valid = in_range && p < NP && p * a.page_size + slot < L && phys >= 0 &&
-                     phys < a.num_phys;
-
-  // ---- stage [P_g; Q_g]^T (bf16, zero past W), the queries and the frequencies ----
+  // ---- stage [P_g; Q_g]^T (bf16, zero past W) and the queries ----
   for (int o = threadIdx.x; o < kHeadDim * KP; o += blockDim.x) {
     const int k = o / kHeadDim, n = o % kHeadDim;  // consecutive threads: consecutive dims
     uint16_t v = 0;
@@ -312,93 +314,180 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
   }
   for (int o = threadIdx.x; o < G * kHeadDim; o += blockDim.x)
     qs[o / kHeadDim][o % kHeadDim] = bf16_to_f32(q[((int64_t)b * a.n_q + (int64_t)g * G) * kHeadDim + o]);
-  for (int o = threadIdx.x; o < kHeadDim / 2; o += blockDim.x) ws[o] = inv_freq[o];
   __syncthreads();
-  if (!has_step) return;  // (no barrier below)
+  if (wave >= n_steps) return;  // (no barrier below)
 
   const int li = lane & 15, lg = lane >> 4;
-  for (int mt = 0; mt < 4; ++mt) {
-    // A fragments: token mt * 16 + li (its page and slot from the lane that owns it)
-    const int tok = mt * 16 + li;
-    const int ph = __shfl(phys, tok);
-    const int tv = __shfl((int)valid, tok);
-    const int tslot = tok & (a.page_size - 1);
-    rb16x8 af[KS];
+  // this lane's Key dims d = 16 nt + li and d + 64 (nt < 4): query values,
+  // frequencies in turns per position, and the one-position rotation
+  float qa[G][4], qb[G][4];
+  double wt[4];
+  float cw[4], sw[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c8 = ks * 4 + lg;  // 8-code run index
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (tv && c8 * 8 < W) {
-        const int code0 = c8 * 8;
+  for (int nt = 0; nt < 4; ++nt) {
+    const int d = nt * 16 + li;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qa[h][nt] = qs[h][d];
+      qb[h][nt] = qs[h][d + kHeadDim / 2];
+    }
+    const float w = inv_freq[d];
+    wt[nt] = (double)w * 0.15915494309189535;  // 1 / (2 pi)
+    rope_sincos(1, w, sw[nt], cw[nt]);
+  }
+  uint4 bf[kRegB ? 8 : 1][kRegB ? KS : 1];
+  if constexpr (kRegB) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bf[nt][ks] = *reinterpret_cast<const uint4 *>(&ft[(nt * 16 + li) * FS + ks * 32 + lg * 8]);
+  }
+
+  // The codes of step st for the four tiles.  Every lane loads (tokens past
+  // the sequence read page 0 of the pool); tmask gets bit mt when the lane's
+  // token of tile mt is valid, and the codes of the others are zeroed at use,
+  // so no load waits on a branch.  Returns whether the lane's own token of the
+  // step is valid.
+  auto load_step = [&](int st, uint4 (&af)[4][KS], uint32_t &tmask) -> bool {
+    const int p = p_begin + st * ppi + (lane >> a.log2_page);
+    int phys = -1;
+    if (p < p_end && p < NP) phys = block_table[(int64_t)b * a.max_pages + p];
+    const bool valid = p < p_end && p < NP && p * a.page_size + slot < L && phys >= 0 &&
+                       phys < a.num_phys;
+    tmask = 0;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int tok = mt * 16 + li;
+      const int tv = __shfl((int)valid, tok);
+      const int ph0 = __shfl(phys, tok);
+      const int ph = tv ? ph0 : 0;
+      tmask |= (uint32_t)(tv != 0) << mt;
+      const int tslot = tok & (a.page_size - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int run = (ks * 4 + lg) * 8;            // this lane's 8-code run
+        const int code0 = run < W ? run : 0;          // (runs past W: zeroed at use)
         const bool in_z = code0 < RB;
         const int cc = in_z ? code0 / CE : (code0 - RB) / CE;  // chunk of its pool
-        const int half = (code0 % CE) / 8;                      // E4M3: which half of the chunk
         const int64_t off = in_z
             ? (zhead + ph) * page_z_bytes + ((int64_t)cc * a.page_size + tslot) * 16
             : (zhead + ph) * page_r_bytes + ((int64_t)(a.geom.r_first + cc) * a.page_size + tslot) * 16;
         const char *base = reinterpret_cast<const char *>(in_z ? (const void *)zpool : (const void *)rpool);
         if constexpr (sizeof(C) == 1) {
-          const uint2 w = *reinterpret_cast<const uint2 *>(base + off + half * 8);
-          v = fp8x8_to_bf16x8(w.x, w.y);
+          const uint2 w = *reinterpret_cast<const uint2 *>(base + off + ((code0 % CE) / 8) * 8);
+          af[mt][ks] = make_uint4(w.x, w.y, 0u, 0u);  // widened at use
         } else {
-          v = *reinterpret_cast<const uint4 *>(base + off);
+          af[mt][ks] = *reinterpret_cast<const uint4 *>(base + off);
         }
       }
-      af[ks] = __builtin_bit_cast(rb16x8, v);
     }
-    // predicted Keys of the tile: dims 16 nt + li, tokens 4 lg .. 4 lg + 3
-    rf4 kh[8];
+    return valid;
+  };
+
+  auto compute_step = [&](int st, const uint4 (&af)[4][KS], uint32_t tmask, bool valid) {
+    const int p0 = p_begin + st * ppi;
+    const int pos0 = p0 * a.page_size;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      kh[nt] = rf4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; ++mt) {
+      rb16x8 av[KS];
+      const bool tv = (tmask >> mt) & 1u;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 bv = *reinterpret_cast<const uint4 *>(&ft[(nt * 16 + li) * FS + ks * 32 + lg * 8]);
-        kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(rb16x8, bv),
-                                                         kh[nt], 0, 0, 0);
+        uint4 v = af[mt][ks];
+        if constexpr (sizeof(C) == 1) v = fp8x8_to_bf16x8(v.x, v.y);
+        if (!tv || (ks * 4 + lg) * 8 >= W) v = make_uint4(0u, 0u, 0u, 0u);
+        av[ks] = __builtin_bit_cast(rb16x8, v);
       }
-    }
-    // rotate each token's pairs to its position, then the query dot products
-    float part[4][G];
+      // predicted Keys of the tile: dims 16 nt + li, tokens 4 lg .. 4 lg + 3
+      rf4 kh[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = mt * 16 + lg * 4 + r;         // token within the step
-      const int pos = (p_begin + wave * ppi) * a.page_size + t;
+      for (int nt = 0; nt < 8; ++nt) {
+        kh[nt] = rf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G; ++h) part[r][h] = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 bv;
+          if constexpr (kRegB) bv = bf[nt][ks];
+          else bv = *reinterpret_cast<const uint4 *>(&ft[(nt * 16 + li) * FS + ks * 32 + lg * 8]);
+          kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], __builtin_bit_cast(rb16x8, bv),
+                                                           kh[nt], 0, 0, 0);
+        }
+      }
+      // rotate each token's pairs to its position, then the query dot products
+      float part[4][G];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[r][h] = 0.f;
+      const int pos = pos0 + mt * 16 + lg * 4;  // the lane's first token of the tile
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int d = nt * 16 + li;
-        float sn, cs;
-        rope_sincos(pos, ws[d], sn, cs);
-        const float x = kh[nt][r], y = kh[nt + 4][r];
-        const float xr = x * cs - y * sn, yr = x * sn + y * cs;
+        const double turns = (double)pos * wt[nt];
+        const float f = (float)(turns - floor(turns));
+        float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          part[r][h] = fmaf(qs[h][d], xr, fmaf(qs[h][d + kHeadDim / 2], yr, part[r][h]));
+        for (int r = 0; r < 4; ++r) {
+          if (r > 0) {  // one position on: angle + w
+            const float c2 = cs * cw[nt] - sn * sw[nt];
+            sn = sn * cw[nt] + cs * sw[nt];
+            cs = c2;
+          }
+          const float x = kh[nt][r], y = kh[nt + 4][r];
+          const float xr = x * cs - y * sn, yr = x * sn + y * cs;
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            part[r][h] = fmaf(qa[h][nt], xr, fmaf(qb[h][nt], yr, part[r][h]));
+        }
+      }
+      // sums over the 16 lanes of a row (every lane of the row gets them), and
+      // the maximum over the group's heads
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float best = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float v = part[r][h];
+          v += dpp_move<0xB1>(v);
+          v += dpp_move<0x4E>(v);
+          v += dpp_move<0x141>(v);
+          v += dpp_move<0x140>(v);
+          best = fmaxf(best, v);
+        }
+        if (li == 0) tok_score[wave][mt * 16 + lg * 4 + r] = best;
       }
     }
-    // sums over the 16 lanes of a row (every lane of the row gets them), and
-    // the maximum over the group's heads
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float best = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float v = part[r][h];
-        v += dpp_move<0xB1>(v);
-        v += dpp_move<0x4E>(v);
-        v += dpp_move<0x141>(v);
-        v += dpp_move<0x140>(v);
-        best = fmaxf(best, v);
-      }
-      if (li == 0) tok_score[wave][mt * 16 + lg * 4 + r] = best;
-    }
+    wave_lds_sync();
+    float best = valid ? tok_score[wave][lane] : -INFINITY;
+    best = group_max(best, a.page_size);
+    const int p = p0 + (lane >> a.log2_page);
+    if (p < p_end && slot == 0) out[p] = (p < NP) ? best : -INFINITY;
+  };
+
+  // Steps wave, wave + 4, ... of the workgroup's range; steps wholly past the
+  // sequence write -inf without loads.  Two code buffers: the next step's
+  // loads are issued before the current step's compute.
+  const int first_dead = (NP - p_begin + ppi - 1) / ppi;  // first step with no valid page
+  const int n_live = max(0, min(n_steps, first_dead));
+  int dead = wave;  // this wave's first step at or past n_live
+  if (dead < n_live) dead += ((n_live - 1 - dead) / 4 + 1) * 4;
+  for (int st = dead; st < n_steps; st += 4) {
+    const int p = p_begin + st * ppi + (lane >> a.log2_page);
+    if (p < p_end && slot == 0) out[p] = -INFINITY;
   }
-  wave_lds_sync();
-  float best = valid ? tok_score[wave][lane] : -INFINITY;
-  best = group_max(best, a.page_size);
-  if (in_range && slot == 0) scores[(int64_t)bg * a.max_pages + p] = (p < NP) ? best : -INFINITY;
+  if (wave >= n_live) return;
+  uint4 fa[4][KS], fb[4][KS];
+  uint32_t ma = 0, mb = 0;
+  bool va = load_step(wave, fa, ma), vb = false;
+  for (int st = wave;; st += 8) {
+    const bool more1 = st + 4 < n_live;
+    if (more1) vb = load_step(st + 4, fb, mb);
+    compute_step(st, fa, ma, va);
+    if (!more1) break;
+    const bool more2 = st + 8 < n_live;
+    if (more2) va = load_step(st + 8, fa, ma);
+    compute_step(st + 4, fb, mb, vb);
+    if (!more2) break;
+  }
 }
 
 template <typename T>
@@ -523,6 +612,12 @@ static const void *find_score_rope(const basiskv_dims &d) {
 bool score_rope_supported(const basiskv_dims &d) { return find_score_rope(d) != nullptr; }
 
 // Page scores with RoPE from the raw queries and the routing factors.
+#ifndef BKV_ROPE_WORKGROUPS
+#define BKV_ROPE_WORKGROUPS 1024
+#endif
+constexpr int kRopeWorkgroups = BKV_ROPE_WORKGROUPS;
+constexpr int kRopeMaxStepsPerWave = 32;
+
 hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                              const basiskv_cache &c, float *scores, hipStream_t s,
                              bool *unsupported) {
@@ -541,8 +636,14 @@ hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P
   a.log2_page = ilog2(d.page_size);
   a.geom = pool_geom(d);
   a.cap = d.max_pages_per_seq * d.page_size;
+  // steps of 64 tokens per wave: enough workgroups to fill the chip
+  // (kRopeWorkgroups), as few as that allows, so the factor staging of a
+  // workgroup serves many tokens
   const int ppi = 64 / d.page_size;
-  a.pages_per_wg = ppi * 4;
+  const int64_t steps = (int64_t)d.batch * d.n_kv_heads * ((d.max_pages_per_seq + ppi - 1) / ppi);
+  const int spw = (int)std::max<int64_t>(1, std::min<int64_t>(kRopeMaxStepsPerWave,
+                                                               steps / (4 * kRopeWorkgroups)));
+  a.pages_per_wg = ppi * 4 * spw;
   a.chunks_per_bg = (d.max_pages_per_seq + a.pages_per_wg - 1) / a.pages_per_wg;
   a.total = d.batch * d.n_kv_heads * a.chunks_per_bg;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
