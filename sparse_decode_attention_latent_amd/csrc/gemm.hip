@@ -77,10 +77,13 @@ __host__ __device__ __forceinline__ int64_t mtile_index(int n, int k, int K) {
 // [hi(u) of 8 sequences ; lo(u) of the same 8], so one MFMA carries both
 // terms and y = C[b] + C[b + 8].  float32: 16 sequences per row tile.
 // ---------------------------------------------------------------------------
-constexpr int kReconWaves = 8;
+#ifndef BKV_RECON_WAVES
+#define BKV_RECON_WAVES 8
+#endif
+constexpr int kReconWaves = BKV_RECON_WAVES;
 
 template <typename T, int RT, bool UT>
-__global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restrict__ u,
+__global__ __launch_bounds__(64 * kReconWaves) void reconstruct_kernel(const float *__restrict__ u,
                                                          const uint16_t *__restrict__ u_tiles,
                                                          const T *__restrict__ M,
                                                          T *__restrict__ y, int batch, int K,
@@ -101,28 +104,47 @@ __global__ __launch_bounds__(512) void reconstruct_kernel(const float *__restric
   if constexpr (kBf) {
   if constexpr (UT) {
     // u already split into its bf16 A operand (utile_index): fragments are
-    // loaded as they are; rows past the batch read as zero
-    constexpr int U = 8;
-    for (int ks0 = wave; ks0 < n_steps; ks0 += kReconWaves * U) {
-      uint4 braw[U], araw[U][RT];
+    // loaded as they are.  Every load is unpredicated: the operand holds whole
+    // row tiles, and a row past the batch only feeds output rows that are not
+    // stored.  Rounds of U k-steps per wavefront, software-pipelined: the next
+    // round's loads are in flight while the current round's MFMAs run.
+    constexpr int U = 4;
+    constexpr int kStride = kReconWaves * U;  // k-steps per round, whole workgroup
+    const int n_tiles = (batch + ROWS - 1) / ROWS;  // row tiles the operand holds
+    uint4 b0[U], a0[U][RT], b1[U], a1[U][RT];
+    auto load = [&](int ks0, uint4 (&braw)[U], uint4 (&araw)[U][RT]) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
-        const int ks = ks0 + uu * kReconWaves;
-        braw[uu] = make_uint4(0, 0, 0, 0);
-        if (ks < n_steps)
-          braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          araw[uu][rt] = make_uint4(0, 0, 0, 0);
-          if (ks < n_steps && (rt0 + rt) * ROWS + (i & 7) < batch)
-            araw[uu][rt] = reinterpret_cast<const uint4 *>(u_tiles)[((int64_t)(rt0 + rt) * n_steps + ks) * 64 + lane];
-        }
-      }
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu)
+        const int ks = min(ks0 + uu * kReconWaves, n_steps - 1);  // (clamped: used only below n_steps)
+        braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          acc[rt] = MF::mma(bits_to_frag(araw[uu][rt]), bits_to_frag(braw[uu]), acc[rt]);
+          araw[uu][rt] = rt0 + rt < n_tiles  // (wavefront-uniform)
+              ? reinterpret_cast<const uint4 *>(u_tiles)[((int64_t)(rt0 + rt) * n_steps + ks) * 64 + lane]
+              : make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    auto mma = [&](int ks0, const uint4 (&braw)[U], const uint4 (&araw)[U][RT]) {
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu)
+        if (ks0 + uu * kReconWaves < n_steps) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            acc[rt] = MF::mma(bits_to_frag(araw[uu][rt]), bits_to_frag(braw[uu]), acc[rt]);
+        }
+    };
+    if (wave < n_steps) {
+      load(wave, b0, a0);
+      for (int ks0 = wave;; ks0 += 2 * kStride) {
+        const bool more1 = ks0 + kStride < n_steps;
+        if (more1) load(ks0 + kStride, b1, a1);
+        mma(ks0, b0, a0);
+        if (!more1) break;
+        const bool more2 = ks0 + 2 * kStride < n_steps;
+        if (more2) load(ks0 + 2 * kStride, b0, a0);
+        mma(ks0 + kStride, b1, a1);
+        if (!more2) break;
+      }
     }
   } else {
     // U k-steps per round: every load of the round is issued before the first MFMA
@@ -585,7 +607,7 @@ static hipError_t recon_t(const basiskv_dims &d, const float *u, const uint16_t 
   const int rt = (d.batch + rows - 1) / rows;
   const int K = d.n_q_heads * d.r_v, N = d.hidden;
   // up to 4 row tiles per workgroup; larger batches take more row-tile groups
-  dim3 grid((N + 15) / 16, rt <= 4 ? 1 : (rt + 3) / 4), block(512);
+  dim3 grid((N + 15) / 16, rt <= 4 ? 1 : (rt + 3) / 4), block(64 * kReconWaves);
   const T *Mt = (const T *)M;
   T *yt = (T *)y;
 #define BKV_RECON(RTV, UTV)                                                                    \
