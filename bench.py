@@ -370,15 +370,17 @@ def context_sweep(steps, warmup):
                                           top_k=wl.top_k, elem=2,
                                           recent_tokens=wl.recent_tokens,
                                           cache_elem=1 if wl.cache == "fp8" else 0)
-                row[name] = {"us": round(us, 2),
-                             "gbs": round(traffic.step_bytes(shape, [T] * B)["total"] / (us * 1e-6) / 1e9, 1)}
+                gbs = traffic.step_bytes(shape, [T] * B)["total"] / (us * 1e-6) / 1e9
+                row[name] = {"us": round(us, 2), "gbs": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
                 if dense_us is None:  # dense baseline on the first workload's pools
                     dense = DenseProblem(prob, seed=11)
                     dense_us = _time_calls(dense.step, steps, warmup)
                     dbytes = (B * wl.n_kv_heads * T * 2 * wl.head_dim * 2
                               + wl.hidden * wl.n_q_heads * wl.head_dim * 2)
-                    row["dense"] = {"us": round(dense_us, 2),
-                                    "gbs": round(dbytes / (dense_us * 1e-6) / 1e9, 1)}
+                    dgbs = dbytes / (dense_us * 1e-6) / 1e9
+                    row["dense"] = {"us": round(dense_us, 2), "gbs": round(dgbs, 1),
+                                    "hbm_frac": round(dgbs / HBM_PEAK_GBS, 4)}
                     del dense
                 row[name]["speedup_vs_dense"] = round(dense_us / us, 3)
                 del prob

@@ -147,40 +147,60 @@ __global__ __launch_bounds__(64 * kReconWaves) void reconstruct_kernel(const flo
       }
     }
   } else {
-    // U k-steps per round: every load of the round is issued before the first MFMA
-    constexpr int U = 8 / RT;
-    for (int ks0 = wave; ks0 < n_steps; ks0 += kReconWaves * U) {
-      uint4 braw[U];
-      float4 ux[U][RT][2];
+    // float32 u, split into bf16 hi + lo at use.  Rounds of U k-steps per
+    // wavefront, software-pipelined as above.  Loads are unpredicated: rows past
+    // the batch read the last row (they feed output rows that are not stored),
+    // slots past K read the row's last 8 and are zeroed at use.
+    constexpr int U = 4 / RT;
+    constexpr int kStride = kReconWaves * U;
+    uint4 b0[U], b1[U];
+    float4 x0[U][RT][2], x1[U][RT][2];
+    auto load = [&](int ks0, uint4 (&braw)[U], float4 (&ux)[U][RT][2]) {
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int ks = min(ks0 + uu * kReconWaves, n_steps - 1);
+        const int k = min(ks * MF::KS + qg * 8, K - 8);
+        braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int b = min((rt0 + rt) * ROWS + (i & 7), batch - 1);
+          const float4 *up = reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
+          ux[uu][rt][0] = up[0];
+          ux[uu][rt][1] = up[1];
+        }
+      }
+    };
+    auto mma = [&](int ks0, const uint4 (&braw)[U], const float4 (&ux)[U][RT][2]) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
         const int ks = ks0 + uu * kReconWaves;
-        const int k = ks * MF::KS + qg * 8;
-        braw[uu] = make_uint4(0, 0, 0, 0);
-        if (ks < n_steps)
-          braw[uu] = reinterpret_cast<const uint4 *>(M)[((int64_t)blockIdx.x * n_steps + ks) * 64 + lane];
+        if (ks < n_steps) {
+          const bool in_k = ks * MF::KS + qg * 8 < K;
+          const bf16x8 bfrag = bits_to_frag(braw[uu]);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int b = (rt0 + rt) * ROWS + (i & 7);
-          ux[uu][rt][0] = ux[uu][rt][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (b < batch && k < K) {
-            const float4 *up = reinterpret_cast<const float4 *>(u + (int64_t)b * K + k);
-            ux[uu][rt][0] = up[0];
-            ux[uu][rt][1] = up[1];
+          for (int rt = 0; rt < RT; ++rt) {
+            const float4 y0 = ux[uu][rt][0], y1 = ux[uu][rt][1];
+            float x[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = in_k ? x[e] : 0.f;
+            bf16x8 hi, lo;
+            split_bf16(x, &hi, &lo);
+            acc[rt] = MF::mma(i < 8 ? hi : lo, bfrag, acc[rt]);
           }
         }
       }
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const bf16x8 bfrag = bits_to_frag(braw[uu]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const float4 x0 = ux[uu][rt][0], x1 = ux[uu][rt][1];
-          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          bf16x8 hi, lo;
-          split_bf16(x, &hi, &lo);
-          acc[rt] = MF::mma(i < 8 ? hi : lo, bfrag, acc[rt]);
-        }
+    };
+    if (wave < n_steps) {
+      load(wave, b0, x0);
+      for (int ks0 = wave;; ks0 += 2 * kStride) {
+        const bool more1 = ks0 + kStride < n_steps;
+        if (more1) load(ks0 + kStride, b1, x1);
+        mma(ks0, b0, x0);
+        if (!more1) break;
+        const bool more2 = ks0 + 2 * kStride < n_steps;
+        if (more2) load(ks0 + 2 * kStride, b0, x0);
+        mma(ks0 + kStride, b1, x1);
+        if (!more2) break;
       }
     }
   }
