@@ -249,27 +249,41 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 //
 // A wavefront takes 64-token steps (a page-aligned run of pages), each as
 // four 16-token tiles.  For a tile, one v_mfma_f32_16x16x32_bf16 per 32 codes
-// and 16 Key dims: A = the tokens' codes (lane l: token l % 16, codes
-// 8 (l / 16) .. + 7 of the k step -- one 8-element run of a page chunk, widened
-// from E4M3 when the cache is FP8), B = [P; Q]^T (lane l: dim l % 16, the same
-// 8 codes).  The result puts dim 16 nt + l % 16 of tokens 4 (l / 16) .. + 3 in
-// lane l for Key tile nt, so the rotate-half pair (d, d + 64) -- tiles nt and
-// nt + 4 -- is lane-local.  The query dot products are summed over the 16
-// lanes of a row; token logits go through LDS to the page maxima.
+// and 16 Key dims forms the predicted Keys transposed: A = [P; Q]^T (lane l:
+// dim l % 16 of the Key tile, codes 8 (l / 16) .. + 7 of the k step), B = the
+// tokens' codes (lane l: token l % 16, the same 8 codes -- one 8-element run
+// of a page chunk, widened from E4M3 when the cache is FP8).  The result puts
+// dims 16 nt + 4 (l / 16) + 0..3 of token l % 16 in lane l for Key tile nt, so
+// the rotate-half pair (d, d + 64) -- tiles nt and nt + 4 -- is lane-local and
+// a lane holds 32 dims of one token.  Each lane rotates its 16 pairs in float32
+// and splits the rotated values into bf16 hi + lo terms (about 16 significant
+// bits); the dot products with the group's bf16 queries then run on the same
+// matrix instruction (A = the queries, heads as rows; B = the rotated Key; k
+// slots map to the lane's dims in the same order on both sides), hi and lo
+// accumulating into one float32 tile that holds the tile's logits.
+//
+// Angles: the token at tile position i sits at t = t0 + i (t0 uniform over
+// the wavefront).  Every tile, lane l takes one exact sine and cosine of
+// t0 w_l (turns reduced in double precision), shared through LDS; each lane
+// combines them with the fixed rotation by i w_d of its own dims (taken once,
+// exactly) -- four products per pair.
 //
 // [P; Q]^T is staged in LDS once per workgroup and, for up to 96 codes, held
-// in registers by every wave; the queries' dims are held in registers too.  A
-// workgroup covers pages_per_wg pages, i.e. several steps per wave, so the
-// staging is shared by many tokens, and each wave loads the codes of its next
-// step while it computes the current one.  Angles: for every tile and
-// frequency one exact sine / cosine at the lane's first token (turns reduced
-// in double precision), then the next three positions by the one-position
-// rotation (cos w, sin w) -- three products per step, float32 rounding.
+// in registers by every wave.  A workgroup covers pages_per_wg pages, i.e.
+// several steps per wave, so the staging is shared by many tokens, and each
+// wave loads the codes of its next step while it computes the current one.
 // grid: (batch x n_kv x chunks), XCD-major; 256 threads; q: the raw
 // (rotated) queries.
 // ---------------------------------------------------------------------------
+// wavefronts per SIMD: two for routing widths up to 32 codes (their factor and
+// code registers leave room), one for the wider ones (whole register file)
+#ifndef BKV_ROPE_WAVES_PER_EU
+#define BKV_ROPE_WAVES_PER_EU 2
+#endif
 template <typename C, int G, int NZ, int NR>
-__global__ __launch_bounds__(256) void route_rope_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu((NZ + NR) * (16 / sizeof(C)) <= 32 ? BKV_ROPE_WAVES_PER_EU : 1)))
+void route_rope_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ P, const uint16_t *__restrict__ Q,
     const float *__restrict__ inv_freq, const C *__restrict__ zpool, const C *__restrict__ rpool,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -285,6 +299,8 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
   __shared__ __align__(16) uint16_t ft[kHeadDim * FS];   // [dim][code]
   __shared__ float qs[G][kHeadDim];
   __shared__ float tok_score[4][kWave];
+  __shared__ __align__(16) float ang[4][2][kHeadDim / 2];  // per wave: cos, sin of t0 w_d
+  static_assert(G <= 16, "heads are the rows of one matrix tile");
 
   const int work = xcd_work_index(a.padded);
   if (work >= a.total) return;
@@ -318,23 +334,27 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
   if (wave >= n_steps) return;  // (no barrier below)
 
   const int li = lane & 15, lg = lane >> 4;
-  // this lane's Key dims d = 16 nt + li and d + 64 (nt < 4): query values,
-  // frequencies in turns per position, and the one-position rotation
-  float qa[G][4], qb[G][4];
-  double wt[4];
-  float cw[4], sw[4];
+  // k slot j of dot step s <-> Key dim 16 (2 s + j / 4) + 4 lg + j % 4 (the
+  // lane's rotated values of Key tiles 2 s and 2 s + 1); the query operand:
+  // head li's values at those dims (zero rows past the group)
+  uint4 qop[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int d = nt * 16 + li;
+  for (int st = 0; st < 4; ++st) {
+    float x[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qa[h][nt] = qs[h][d];
-      qb[h][nt] = qs[h][d + kHeadDim / 2];
-    }
-    const float w = inv_freq[d];
-    wt[nt] = (double)w * 0.15915494309189535;  // 1 / (2 pi)
-    rope_sincos(1, w, sw[nt], cw[nt]);
+    for (int j = 0; j < 8; ++j)
+      x[j] = li < G ? qs[li < G ? li : 0][16 * (2 * st + j / 4) + 4 * lg + j % 4] : 0.f;
+    qop[st] = make_uint4(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]),
+                         f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7]));
   }
+  // this lane's pairs (d, d + 64), d = 16 nt + 4 lg + r: the rotation by li w_d
+  // (its token's offset in a tile); and frequency l in turns per position
+  float cl[4][4], sl[4][4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rope_sincos(li, inv_freq[16 * nt + 4 * lg + r], sl[nt][r], cl[nt][r]);
+  const double wt = (double)inv_freq[lane] * 0.15915494309189535;  // 1 / (2 pi); lane < 64 pairs
   uint4 bf[kRegB ? 8 : 1][kRegB ? KS : 1];
   if constexpr (kRegB) {
 #pragma unroll
@@ -390,6 +410,13 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
     const int pos0 = p0 * a.page_size;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      // the tile's base angles t0 w_l, exact, one frequency per lane
+      {
+        const double turns = (double)(pos0 + mt * 16) * wt;
+        const float f = (float)(turns - floor(turns));
+        ang[wave][0][lane] = __builtin_amdgcn_cosf(f);
+        ang[wave][1][lane] = __builtin_amdgcn_sinf(f);
+      }
       rb16x8 av[KS];
       const bool tv = (tmask >> mt) & 1u;
 #pragma unroll
@@ -399,7 +426,7 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
         if (!tv || (ks * 4 + lg) * 8 >= W) v = make_uint4(0u, 0u, 0u, 0u);
         av[ks] = __builtin_bit_cast(rb16x8, v);
       }
-      // predicted Keys of the tile: dims 16 nt + li, tokens 4 lg .. 4 lg + 3
+      // predicted Keys of the tile, transposed: dims 16 nt + 4 lg + r of token li
       rf4 kh[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -409,52 +436,55 @@ __global__ __launch_bounds__(256) void route_rope_kernel(
           uint4 bv;
           if constexpr (kRegB) bv = bf[nt][ks];
           else bv = *reinterpret_cast<const uint4 *>(&ft[(nt * 16 + li) * FS + ks * 32 + lg * 8]);
-          kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], __builtin_bit_cast(rb16x8, bv),
+          kh[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rb16x8, bv), av[ks],
                                                            kh[nt], 0, 0, 0);
         }
       }
-      // rotate each token's pairs to its position, then the query dot products
-      float part[4][G];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int h = 0; h < G; ++h) part[r][h] = 0.f;
-      const int pos = pos0 + mt * 16 + lg * 4;  // the lane's first token of the tile
+      wave_lds_sync();
+      // rotate each pair to the token's position: angle t0 w_d + li w_d
+      float kr[8][4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const double turns = (double)pos * wt[nt];
-        const float f = (float)(turns - floor(turns));
-        float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+        const float4 c0 = *reinterpret_cast<const float4 *>(&ang[wave][0][16 * nt + 4 * lg]);
+        const float4 s0 = *reinterpret_cast<const float4 *>(&ang[wave][1][16 * nt + 4 * lg]);
+        const float ct[4] = {c0.x, c0.y, c0.z, c0.w}, stt[4] = {s0.x, s0.y, s0.z, s0.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (r > 0) {  // one position on: angle + w
-            const float c2 = cs * cw[nt] - sn * sw[nt];
-            sn = sn * cw[nt] + cs * sw[nt];
-            cs = c2;
-          }
+          const float cs = ct[r] * cl[nt][r] - stt[r] * sl[nt][r];
+          const float sn = stt[r] * cl[nt][r] + ct[r] * sl[nt][r];
           const float x = kh[nt][r], y = kh[nt + 4][r];
-          const float xr = x * cs - y * sn, yr = x * sn + y * cs;
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            part[r][h] = fmaf(qa[h][nt], xr, fmaf(qb[h][nt], yr, part[r][h]));
+          kr[nt][r] = x * cs - y * sn;
+          kr[nt + 4][r] = x * sn + y * cs;
         }
       }
-      // sums over the 16 lanes of a row (every lane of the row gets them), and
-      // the maximum over the group's heads
+      // logits of the tile: heads 4 lg + r of token li, hi and lo terms
+      rf4 lgh = rf4{0.f, 0.f, 0.f, 0.f}, lgl = lgh;  // hi and lo terms: two independent chains
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float best = -INFINITY;
+      for (int ds = 0; ds < 4; ++ds) {
+        float x[8];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float v = part[r][h];
-          v += dpp_move<0xB1>(v);
-          v += dpp_move<0x4E>(v);
-          v += dpp_move<0x141>(v);
-          v += dpp_move<0x140>(v);
-          best = fmaxf(best, v);
+        for (int j = 0; j < 8; ++j) x[j] = kr[2 * ds + j / 4][j % 4];
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = f32x2_to_bf16x2(x[2 * i], x[2 * i + 1]);
+          l[i] = f32x2_to_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16),
+                                 x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
         }
-        if (li == 0) tok_score[wave][mt * 16 + lg * 4 + r] = best;
+        const rb16x8 qv = __builtin_bit_cast(rb16x8, qop[ds]);
+        lgh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qv, __builtin_bit_cast(rb16x8, make_uint4(h[0], h[1], h[2], h[3])), lgh, 0, 0, 0);
+        lgl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qv, __builtin_bit_cast(rb16x8, make_uint4(l[0], l[1], l[2], l[3])), lgl, 0, 0, 0);
       }
+      const rf4 lg4 = lgh + lgl;
+      // maximum over the group's heads (rows 4 lg + r < G)
+      float best = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * lg + r < G) best = fmaxf(best, lg4[r]);
+      if constexpr (G > 4) best = fmaxf(best, __shfl_xor(best, 16));
+      if (lg == 0) tok_score[wave][mt * 16 + li] = best;
     }
     wave_lds_sync();
     float best = valid ? tok_score[wave][lane] : -INFINITY;
@@ -613,7 +643,7 @@ bool score_rope_supported(const basiskv_dims &d) { return find_score_rope(d) != 
 
 // Page scores with RoPE from the raw queries and the routing factors.
 #ifndef BKV_ROPE_WORKGROUPS
-#define BKV_ROPE_WORKGROUPS 1024
+#define BKV_ROPE_WORKGROUPS 512
 #endif
 constexpr int kRopeWorkgroups = BKV_ROPE_WORKGROUPS;
 constexpr int kRopeMaxStepsPerWave = 32;
