@@ -36,6 +36,12 @@ constexpr int kMaxSplits = 64;  // partial records per (sequence, head)
 #define BKV_ATTEND_BLOCKS 2
 #endif
 constexpr int kAttendBlocks = BKV_ATTEND_BLOCKS;  // 64-token blocks per wavefront
+// RoPE kernels hold one wavefront per SIMD (1024 on the chip) and are also
+// built with three blocks per wavefront: rows of a little over one block per
+// SIMD (the adopted router: 2176 blocks) then take three block times instead
+// of a second round of two-block wavefronts (four).  The launch picks the
+// block count (pages_per_split).
+constexpr int kAttendRopeBlocks = 3;
 
 struct AttendArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap, top_k;
@@ -590,6 +596,7 @@ struct AttendVariant {
   int dtype, G, rv;
   const void *fn1, *fn;  // one block per wavefront and round; kAttendBlocks
   const void *fn_nt;     // kAttendBlocks with non-temporal gathers (null: not built)
+  const void *fn3;       // kAttendRopeBlocks (RoPE kernels; null otherwise)
 };
 
 // non-temporal variants for the 4-head kernels (the 8B-shaped group, and the
@@ -601,7 +608,8 @@ struct AttendVariant {
        &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, false>),                 \
    (G) == 4 ? reinterpret_cast<const void *>(                                                    \
                   &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, ((G) == 4)>)  \
-            : nullptr}
+            : nullptr,                                                                           \
+   nullptr}
 #define BKV_ATT_G(T, C, DT, RV)                                                  \
   BKV_ATT(T, C, DT, 1, RV), BKV_ATT(T, C, DT, 2, RV), BKV_ATT(T, C, DT, 4, RV), \
       BKV_ATT(T, C, DT, 8, RV)
@@ -625,7 +633,9 @@ static const AttendVariant kAttendVariants[] = {
    reinterpret_cast<const void *>(&attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, 1, false, true>), \
    reinterpret_cast<const void *>(                                                                    \
        &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendBlocks, false, true>),                \
-   nullptr}
+   nullptr,                                                                                           \
+   reinterpret_cast<const void *>(                                                                    \
+       &attend_split_kernel<T, C, G, (RV) / Elem<C>::CE, kAttendRopeBlocks, false, true>)}
 static const AttendVariant kAttendRopeVariants[] = {
     BKV_ATT_ROPE(uint16_t, uint16_t, BASISKV_BF16, 4, 64),
     BKV_ATT_ROPE(uint16_t, uint16_t, BASISKV_BF16, 4, 96),
@@ -657,30 +667,53 @@ int attend_group_split(const basiskv_dims &d) {
   return act_bf16(d) && G == 8 && d.r_v >= 96 ? 2 : 1;
 }
 
-// Pages per split.  Every wavefront takes up to kAttendBlocks 64-token blocks
-// per round: kAttendBlocks when one block per wavefront would need more
-// wavefronts than the chip holds at once (two per SIMD: 2048), which would
-// leave a second, partial round of wavefronts waiting for the first; one
-// block otherwise (more, smaller workgroups).  A split grows by whole rounds
-// when that would leave more than kMaxSplits splits (the kernel loops over
-// them).
+// Pages per split and 64-token blocks per wavefront and round (nb).  A split
+// is kAttendWaves wavefronts x nb blocks, grown by whole rounds when that would
+// leave more than kMaxSplits splits (the kernel loops over them).  Position-free
+// kernels take kAttendBlocks blocks when one block per wavefront would need more
+// wavefronts than the chip holds at once (two per SIMD: 2048), which would leave
+// a second, partial round waiting for the first, and one block otherwise (more,
+// smaller workgroups).  RoPE kernels (one wavefront per SIMD: 1024) take the
+// block count among 1, kAttendBlocks and kAttendRopeBlocks with the fewest block
+// times -- rounds of resident wavefronts x blocks per wavefront and round x
+// rounds per split -- and, of equals, the fewest splits.
 #ifndef BKV_ATTEND_RESIDENT_WAVES
 #define BKV_ATTEND_RESIDENT_WAVES 2048
 #endif
-static int pages_per_split(const basiskv_dims &d, int32_t entries) {
+struct SplitPlan {
+  int nb, pages;
+};
+static SplitPlan split_plan_for(const basiskv_dims &d, int32_t entries, int nb) {
   const int ppi = 64 / d.page_size;
-  const int64_t blocks = (int64_t)d.batch * d.n_kv_heads * attend_group_split(d) *
-                         (((int64_t)entries + ppi - 1) / ppi);
-  const int per_wave = blocks > BKV_ATTEND_RESIDENT_WAVES ? kAttendBlocks : 1;
-  const int per_round = kAttendWaves * per_wave * ppi;
-  int rounds = 1;
+  const int per_round = kAttendWaves * nb * ppi;
   const int64_t need = ((int64_t)entries + kMaxSplits - 1) / kMaxSplits;
-  if (need > per_round) {
-    const int full = kAttendWaves * kAttendBlocks * ppi;  // several rounds: full rounds
-    rounds = (int)((need + full - 1) / full);
-    return full * rounds;
+  const int rounds = need > per_round ? (int)((need + per_round - 1) / per_round) : 1;
+  return {nb, per_round * rounds};
+}
+static SplitPlan split_plan(const basiskv_dims &d, int32_t entries, bool rope) {
+  const int ppi = 64 / d.page_size;
+  const int64_t rows = (int64_t)d.batch * d.n_kv_heads * attend_group_split(d);
+  const int64_t blocks = rows * (((int64_t)entries + ppi - 1) / ppi);
+  const int64_t need = ((int64_t)entries + kMaxSplits - 1) / kMaxSplits;
+  if (!rope) {
+    const int nb = blocks > BKV_ATTEND_RESIDENT_WAVES || need > kAttendWaves * ppi ? kAttendBlocks : 1;
+    return split_plan_for(d, entries, nb);
   }
-  return per_round;
+  const int64_t resident = BKV_ATTEND_RESIDENT_WAVES / 2;
+  SplitPlan best{0, 0};
+  int64_t best_t = 0, best_s = 0;
+  for (int nb : {1, kAttendBlocks, kAttendRopeBlocks}) {
+    const SplitPlan p = split_plan_for(d, entries, nb);
+    const int64_t splits = ((int64_t)entries + p.pages - 1) / p.pages;
+    const int64_t waves = rows * splits * kAttendWaves;
+    const int64_t t = (waves + resident - 1) / resident * p.pages / (kAttendWaves * ppi);
+    if (best.nb == 0 || t < best_t || (t == best_t && splits < best_s)) {
+      best = p;
+      best_t = t;
+      best_s = splits;
+    }
+  }
+  return best;
 }
 
 // Entries of one row: the top_k routed pages, then room for the recent
@@ -692,10 +725,13 @@ static int attend_entries(const basiskv_dims &d, int32_t top_k) {
   return top_k + (w + d.page_size - 1) / d.page_size + 1;
 }
 
+// Splits per row: the larger of the two kernels' counts (the workspace is
+// sized from dims alone, before it is known whether the cache has positions)
 int attend_splits(const basiskv_dims &d, int32_t top_k) {
   const int n = attend_entries(d, top_k);
-  const int pps = pages_per_split(d, n);
-  return (n + pps - 1) / pps;
+  const int pa = split_plan(d, n, false).pages, pb = split_plan(d, n, true).pages;
+  const int sa = (n + pa - 1) / pa, sb = (n + pb - 1) / pb;
+  return sa > sb ? sa : sb;
 }
 
 static const AttendVariant *find_attend(const basiskv_dims &d, bool rope) {
@@ -738,7 +774,8 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   a.recent = a.all_pages ? 0 : d.recent_tokens;
   a.n_entries = a.all_pages ? top_k : attend_entries(d, top_k);
   a.gs = attend_group_split(d);
-  a.pages_per_split = pages_per_split(d, a.n_entries);
+  const SplitPlan plan = split_plan(d, a.n_entries, rope);
+  a.pages_per_split = plan.pages;
   a.n_split = (a.n_entries + a.pages_per_split - 1) / a.pages_per_split;
   a.total = d.batch * d.n_kv_heads * a.gs * a.n_split;
   a.padded = (a.total + kXcds - 1) / kXcds * kXcds;
@@ -755,9 +792,13 @@ hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cac
   // kernel: measured slower on the short launches, whose time is latency),
   // each load instruction reads whole 128-byte lines and no other subgroup
   // reads the same pages
-  const bool one = a.pages_per_split <= kAttendWaves * (64 / d.page_size);
-  const bool nt = v->fn_nt && !one && a.gs == 1 && d.page_size >= 8;
-  const void *fn = nt ? v->fn_nt : (one ? v->fn1 : v->fn);
+  const bool one = plan.nb == 1;
+  const bool nt = v->fn_nt && plan.nb == kAttendBlocks && a.gs == 1 && d.page_size >= 8;
+  const void *fn = nt ? v->fn_nt : one ? v->fn1 : plan.nb == kAttendBlocks ? v->fn : v->fn3;
+  if (!fn) {
+    *unsupported = true;
+    return hipSuccess;
+  }
   return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
 }
 
