@@ -451,6 +451,17 @@ def test_rope_separate_calls_equal_routing(name):
         np.testing.assert_array_equal(b[key], a[key], err_msg=key)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_rope_routing_first_layout(cache):
+    """RoPE routing and attention over routing-first pages (the RoPE kernels
+    read a page's routing dims and latent chunks through the pool geometry),
+    ragged lengths, against the oracle."""
+    wl = workload("llama8b-ctx32k-b16r16-page4-rope").with_(page_layout=1)
+    if cache == "fp8":
+        wl = wl.with_(cache_storage="fp8")
+    run_case(wl, batch=3, ctx=4096, seq_lens=[4096, 2001, 9])
+
+
 def test_rope_long_positions():
     """Positions up to 131071: rotation angles of the highest frequency reach
     about 1.3e5 radians, where the turn count has to be reduced exactly."""
