@@ -268,21 +268,21 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 // combines them with the fixed rotation by i w_d of its own dims (taken once,
 // exactly) -- four products per pair.
 //
-// [P; Q]^T is staged in LDS once per workgroup and, for up to 96 codes, held
-// in registers by every wave.  A workgroup covers pages_per_wg pages, i.e.
+// [P; Q]^T is staged in LDS once per workgroup and, for 32 codes, held in
+// registers by every wave.  A workgroup covers pages_per_wg pages, i.e.
 // several steps per wave, so the staging is shared by many tokens, and each
 // wave loads the codes of its next step while it computes the current one.
 // grid: (batch x n_kv x chunks), XCD-major; 256 threads; q: the raw
 // (rotated) queries.
 // ---------------------------------------------------------------------------
-// wavefronts per SIMD: two for routing widths up to 32 codes (their factor and
-// code registers leave room), one for the wider ones (whole register file)
+// wavefronts per SIMD: two for routing widths up to 96 codes, one for the
+// wider ones (whole register file)
 #ifndef BKV_ROPE_WAVES_PER_EU
 #define BKV_ROPE_WAVES_PER_EU 2
 #endif
 template <typename C, int G, int NZ, int NR>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((NZ + NR) * (16 / sizeof(C)) <= 32 ? BKV_ROPE_WAVES_PER_EU : 1)))
+__attribute__((amdgpu_waves_per_eu((NZ + NR) * (16 / sizeof(C)) <= 96 ? BKV_ROPE_WAVES_PER_EU : 1)))
 void route_rope_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ P, const uint16_t *__restrict__ Q,
     const float *__restrict__ inv_freq, const C *__restrict__ zpool, const C *__restrict__ rpool,
@@ -293,7 +293,10 @@ void route_rope_kernel(
   constexpr int KS = (W + 31) / 32;      // 32-code k steps
   constexpr int KP = KS * 32;
   constexpr int FS = KP + 8;             // LDS row stride of [P;Q]^T (16-byte pad)
-  constexpr bool kRegB = KS <= 3;        // factor fragments held in registers
+  // factor fragments held in registers for one k step (32 codes); wider
+  // routing reads them from LDS each tile, which leaves room for two
+  // wavefronts per SIMD up to 96 codes (measured 168 -> 142 us at 96)
+  constexpr bool kRegB = KS <= 1;
   typedef __bf16 rb16x8 __attribute__((ext_vector_type(8)));
   typedef float rf4 __attribute__((ext_vector_type(4)));
   __shared__ __align__(16) uint16_t ft[kHeadDim * FS];   // [dim][code]
