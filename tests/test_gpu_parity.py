@@ -462,6 +462,16 @@ def test_rope_routing_first_layout(cache):
     run_case(wl, batch=3, ctx=4096, seq_lens=[4096, 2001, 9])
 
 
+@pytest.mark.parametrize("batch,ctx,top_k", [(2, 32768, 4096), (1, 65536, 12500)])
+def test_rope_long_split_plans(batch, ctx, top_k):
+    """RoPE attention split plans beyond the benchmark's: three-block wavefronts
+    with more splits than the position-free plan would take (top_k 4096), and
+    splits of several rounds each (top_k 12500, over the split cap)."""
+    wl = workload("llama8b-ctx32k-b16r16-page4-rope")
+    lens = [ctx, ctx - 2767][:batch]
+    run_case(wl, batch=batch, ctx=ctx, seq_lens=lens, top_k=top_k)
+
+
 def test_rope_long_positions():
     """Positions up to 131071: rotation angles of the highest frequency reach
     about 1.3e5 radians, where the turn count has to be reduced exactly."""
