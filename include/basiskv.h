@@ -63,7 +63,11 @@
  * not used.  Routing then reads one contiguous run of (r_b + r_q) / CE chunks
  * per page (appendix Table 4's routing widths), where the separate pools give
  * two; with small pages and narrow E4M3 rows a separate run fills half of a
- * 128-byte memory line.  Every call of one cache must use the same layout.
+ * 128-byte memory line.  Pages are whole 128-byte lines: with 4-token pages an
+ * odd chunk count is rounded up to the next even one (the last chunk of each
+ * page is unused), so the pool is [n_kv][num_phys][C][page_size][CE] with
+ * C = (r_v + r_q) / CE, plus one when page_size is 4 and that is odd.  Every
+ * call of one cache must use the same layout.
  */
 #ifndef BASISKV_H
 #define BASISKV_H

@@ -322,7 +322,12 @@ inline bkv::PoolGeom pool_geom(const basiskv_dims &d) {
   const int ce = cache_chunk(d);
   bkv::PoolGeom g;
   if (routing_first(d)) {
-    g.z_page_chunks = g.r_page_chunks = (d.r_v + d.r_q) / ce;
+    // pages of whole 128-byte lines: with 4-token pages (a chunk row of 64
+    // bytes) an odd chunk count is rounded up by one unused chunk, so that every
+    // page -- and its leading routing run -- starts on a line
+    const int chunks = (d.r_v + d.r_q) / ce, row = d.page_size * 16;
+    const int unit = row >= 128 ? 1 : 128 / row;
+    g.z_page_chunks = g.r_page_chunks = (chunks + unit - 1) / unit * unit;
     g.r_first = g.z_split = d.r_b / ce;
     g.z_shift = d.r_q / ce;
   } else {

@@ -48,19 +48,32 @@ def unpack_pages(pool, block_table, page_size, T):
     return x.reshape(B, H, n_pages * S, nc * ce)[:, :, :T]
 
 
+def routing_first_width(r_v, r_q, page_size, ce):
+    """Elements per token of a routing-first page: r_v + r_q, plus one unused
+    chunk where needed to make the page whole 128-byte lines (4-token pages
+    with an odd chunk count)."""
+    chunks = (r_v + r_q) // ce
+    unit = 1 if page_size * 16 >= 128 else 128 // (page_size * 16)
+    return -(-chunks // unit) * unit * ce
+
+
 def pack_routing_first(z, r, r_b, block_table, page_size, num_phys_pages):
     """Routing-first layout: logical z [B, Hkv, T, rV] and r [B, Hkv, T, rq]
-    -> one pool [Hkv, num_phys_pages, (rV + rq)/CE, S, CE] whose page chunks are
-    z[:r_b], then r, then z[r_b:] (r_b and rq whole chunks)."""
+    -> one pool [Hkv, num_phys_pages, width/CE, S, CE] whose page chunks are
+    z[:r_b], then r, then z[r_b:] (r_b and rq whole chunks), then zeros up to
+    routing_first_width."""
     z, r = np.asarray(z), np.asarray(r)
     ce = chunk_elems(z.dtype.itemsize)
     assert r_b % ce == 0 and r.shape[-1] % ce == 0
-    rows = np.concatenate([z[..., :r_b], r, z[..., r_b:]], axis=-1)
+    width = routing_first_width(z.shape[-1], r.shape[-1], page_size, ce)
+    pad = np.zeros(z.shape[:-1] + (width - z.shape[-1] - r.shape[-1],), dtype=z.dtype)
+    rows = np.concatenate([z[..., :r_b], r, z[..., r_b:], pad], axis=-1)
     return pack_pages(rows, block_table, page_size, num_phys_pages)
 
 
-def split_routing_first(rows, r_b, r_q):
-    """Rows [..., rV + rq] in routing-first order -> (z [..., rV], r [..., rq])."""
+def split_routing_first(rows, r_b, r_q, r_v):
+    """Rows [..., width] in routing-first order -> (z [..., rV], r [..., rq])
+    (any unused chunk past rV + rq is dropped)."""
     rows = np.asarray(rows)
-    z = np.concatenate([rows[..., :r_b], rows[..., r_b + r_q:]], axis=-1)
+    z = np.concatenate([rows[..., :r_b], rows[..., r_b + r_q:r_v + r_q]], axis=-1)
     return z, rows[..., r_b:r_b + r_q]

@@ -121,7 +121,8 @@ class DecodeProblem:
             rnd = lambda *shape: random_pool(shape, st, gen, dev)
             pool = lambda w: random_pool((Hkv, self.num_phys, w // ce, S, ce), cst, gen, dev)
             if rf:
-                self.z_pages, self.r_pages = pool(wl.r_v + wl.r_q), None
+                self.z_pages = pool(layout.routing_first_width(wl.r_v, wl.r_q, S, ce))
+                self.r_pages = None
             else:
                 self.z_pages, self.r_pages = pool(wl.r_v), pool(wl.r_q)
             self.k_pages = pool(dh)
@@ -226,7 +227,8 @@ class DecodeProblem:
 
         k = row(self.k_pages)
         if self.r_pages is None:  # routing-first: one pool
-            z, r = layout.split_routing_first(row(self.z_pages), self.wl.r_b, self.wl.r_q)
+            z, r = layout.split_routing_first(row(self.z_pages), self.wl.r_b, self.wl.r_q,
+                                              self.wl.r_v)
             return np.ascontiguousarray(z), np.ascontiguousarray(r), k
         return row(self.z_pages), row(self.r_pages), k
 
@@ -319,7 +321,7 @@ class PrefillProblem:
             return torch.zeros((Hkv, self.num_phys, w // ce, S, ce), dtype=tdt, device=device)
 
         if self.page_layout == api.LAYOUT_ROUTING_FIRST:
-            self.z_pages, self.r_pages = pool(wl.r_v + wl.r_q), None
+            self.z_pages, self.r_pages = pool(layout.routing_first_width(wl.r_v, wl.r_q, S, ce)), None
         else:
             self.z_pages, self.r_pages = pool(wl.r_v), pool(wl.r_q)
         self.k_pages = pool(dh)
@@ -340,7 +342,7 @@ class PrefillProblem:
         out = {"k": logical(self.k_pages)}
         if self.r_pages is None:  # routing-first: one pool
             out["z"], out["r"] = layout.split_routing_first(logical(self.z_pages), self.wl.r_b,
-                                                            self.wl.r_q)
+                                                            self.wl.r_q, self.wl.r_v)
         else:
             out["z"], out["r"] = logical(self.z_pages), logical(self.r_pages)
         return out

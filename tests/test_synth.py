@@ -72,25 +72,35 @@ def test_pack_unpack_roundtrip_both_storages():
 def test_routing_first_pages_hold_routing_dims_first():
     """Routing-first pool: chunk order z[:r_b], r, z[r_b:] within each page; the
     scoring chunks of a token are the first (r_b + r_q) / CE of its page; the
-    split recovers both caches."""
-    bt = synth.block_table(2, 3, shuffle_seed=4)
+    split recovers both caches.  Pages are whole 128-byte lines: 4-token pages
+    with an odd chunk count carry one unused chunk."""
     rng = np.random.default_rng(5)
-    for dt, rv, rb, rq in ((np.uint8, 96, 16, 16), (np.uint16, 64, 64, 32), (np.float32, 32, 16, 8)):
-        z = rng.integers(0, 200, size=(2, 2, 40, rv)).astype(dt)
-        r = rng.integers(0, 200, size=(2, 2, 40, rq)).astype(dt)
-        pool = layout.pack_routing_first(z, r, rb, bt, 16, 6)
-        ce = 16 // np.dtype(dt).itemsize
-        assert pool.shape == (2, 6, (rv + rq) // ce, 16, ce)
-        rows = layout.unpack_pages(pool, bt, 16, 40)
-        zz, rr = layout.split_routing_first(rows, rb, rq)
-        np.testing.assert_array_equal(zz, z)
-        np.testing.assert_array_equal(rr, r)
-        # token 17 of sequence 1, KV head 1: its page and slot, chunk by chunk
-        phys, slot = bt[1, 17 // 16], 17 % 16
-        page = pool[1, phys, :, slot, :].reshape(-1)
-        np.testing.assert_array_equal(page[:rb], z[1, 1, 17, :rb])
-        np.testing.assert_array_equal(page[rb:rb + rq], r[1, 1, 17])
-        np.testing.assert_array_equal(page[rb + rq:], z[1, 1, 17, rb:])
+    for S in (16, 4):
+        bt = synth.block_table(2, 40 // S + 1, shuffle_seed=4)
+        for dt, rv, rb, rq in ((np.uint8, 96, 16, 16), (np.uint16, 64, 64, 32), (np.float32, 32, 16, 8),
+                               (np.uint16, 96, 16, 16)):
+            z = rng.integers(0, 200, size=(2, 2, 40, rv)).astype(dt)
+            r = rng.integers(0, 200, size=(2, 2, 40, rq)).astype(dt)
+            n_phys = 2 * bt.shape[1]
+            pool = layout.pack_routing_first(z, r, rb, bt, S, n_phys)
+            ce = 16 // np.dtype(dt).itemsize
+            chunks = (rv + rq) // ce
+            if S == 4 and chunks % 2:
+                chunks += 1  # 64-byte chunk rows: an even count fills whole lines
+            assert pool.shape == (2, n_phys, chunks, S, ce)
+            assert (chunks * S * 16) % 128 == 0
+            assert layout.routing_first_width(rv, rq, S, ce) == chunks * ce
+            rows = layout.unpack_pages(pool, bt, S, 40)
+            zz, rr = layout.split_routing_first(rows, rb, rq, rv)
+            np.testing.assert_array_equal(zz, z)
+            np.testing.assert_array_equal(rr, r)
+            # token 17 of sequence 1, KV head 1: its page and slot, chunk by chunk
+            phys, slot = bt[1, 17 // S], 17 % S
+            page = pool[1, phys, :, slot, :].reshape(-1)
+            np.testing.assert_array_equal(page[:rb], z[1, 1, 17, :rb])
+            np.testing.assert_array_equal(page[rb:rb + rq], r[1, 1, 17])
+            np.testing.assert_array_equal(page[rb + rq:rv + rq], z[1, 1, 17, rb:])
+            assert not page[rv + rq:].any()  # the unused chunk
 
 
 def test_workload_shapes():
