@@ -17,6 +17,12 @@ CASES = (  # (workload, batch, ctx, seq_lens, top_k): the second is smaller
     ("llama8b-ctx32k", 8, 16384, [16384, 9000, 100, 16384, 5000, 33, 1, 12000], 128),
     ("llama8b-ctx32k", 3, 4096, [4096, 1000, 77], 16),
 )
+# rotary positions (the RoPE kernels' split plan), and E4M3 routing-first pages
+# of whole lines
+CASES_ROPE = (
+    ("llama8b-ctx32k-b16r16-page4-rope", 4, 8192, [8192, 5000, 63, 8191], None),
+    ("llama8b-ctx32k-b16r16-page4-fp8", 2, 4096, [4096, 999], None),
+)
 
 
 def _static_step(prob):
@@ -33,13 +39,14 @@ def _clear(prob):
     prob.y.fill_(0)
 
 
-def test_static_step_matches_the_workspace_step_twice():
-    for name, batch, ctx, seq_lens, top_k in CASES:
+@pytest.mark.parametrize("cases", [CASES, CASES_ROPE], ids=["separate-pools", "rope-routing-first"])
+def test_static_step_matches_the_workspace_step_twice(cases):
+    for name, batch, ctx, seq_lens, top_k in cases:
         print(f"static step {name}: batch={batch} ctx={ctx} top_k={top_k}", flush=True)
         wl = workload(name)
         inp = synth.decode_inputs(wl, batch=batch, ctx=ctx, seq_lens=seq_lens)
         prob = DecodeProblem(wl, inp, top_k=top_k)
-        assert api.workspace_bytes(prob.dims, top_k) <= api.static_scratch_bytes()
+        assert api.workspace_bytes(prob.dims, prob.top_k) <= api.static_scratch_bytes()
         prob.decode_step()
         want = prob.outputs()
         _clear(prob)
