@@ -129,7 +129,7 @@ void attend_split_kernel(
   // else [head][dims] (float32)
   __shared__ __align__(16) uint4 qa_lds[kMfma ? QG * NQC * 4 : 1];
   __shared__ __align__(16) float q_lds[kMfma ? 1 : G][kMfma ? 4 : kHeadDim];
-  __shared__ float w_lds[ROPE ? kHeadDim / 2 : 1];  // RoPE inverse frequencies
+  __shared__ double w_lds[ROPE ? kHeadDim / 2 : 1];  // RoPE frequencies, turns per position
   __shared__ float p_lds[NW][G][kWave];
   __shared__ float m_lds[NW][G];
   __shared__ float l_lds[NW][G];
@@ -202,7 +202,8 @@ void attend_split_kernel(
     } else if constexpr (ROPE) {  // float32 queries, and the rotation's frequencies
       for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x)
         q_lds[i / kHeadDim][i % kHeadDim] = to_f32(qg[i]);
-      for (int i = threadIdx.x; i < kHeadDim / 2; i += blockDim.x) w_lds[i] = a.rope[i];
+      for (int i = threadIdx.x; i < kHeadDim / 2; i += blockDim.x)
+        w_lds[i] = (double)a.rope[i] * 0.15915494309189535;  // 1 / (2 pi)
     } else {
       constexpr int QW = G * kHeadDim * (int)sizeof(T) / 4;  // 32-bit words
       constexpr int QL = (QW + 255) / 256;
@@ -349,7 +350,7 @@ void attend_split_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = -INFINITY;
       if (valid) {
-        const int pos = page[i] * a.page_size + slot;  // the token's position in its sequence
+        const double pos = (double)(page[i] * a.page_size + slot);  // the token's position
         constexpr int HALF = NKC / 2;
         float dot[G];
 #pragma unroll
@@ -363,7 +364,7 @@ void attend_split_kernel(
           for (int e = 0; e < CE; ++e) {
             const int d = c * CE + e;
             float sn, cs;
-            rope_sincos(pos, w_lds[d], sn, cs);
+            rope_sincos_turns(pos, w_lds[d], sn, cs);
             const float xr = x[e] * cs - y[e] * sn;
             const float yr = x[e] * sn + y[e] * cs;
 #pragma unroll

@@ -134,6 +134,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // is taken in double precision (exact for positions below 2^24 and float32
 // frequencies), reduced to a fraction of a turn, and evaluated by the
 // hardware sine and cosine, which take turns (v_sin_f32 / v_cos_f32).
+// The same from a frequency given in turns per position (w / (2 pi), double):
+// one product and its fraction per angle.
+__device__ __forceinline__ void rope_sincos_turns(double pos, double wt, float &sn, float &cs) {
+  const float f = (float)__builtin_amdgcn_fract(pos * wt);  // (pos, wt >= 0)
+  sn = __builtin_amdgcn_sinf(f);
+  cs = __builtin_amdgcn_cosf(f);
+}
 __device__ __forceinline__ void rope_sincos(int pos, float w, float &sn, float &cs) {
   const double turns = (double)pos * (double)w * 0.15915494309189535;  // 1 / (2 pi)
   const float f = (float)(turns - floor(turns));

@@ -415,10 +415,10 @@ void route_rope_kernel(
     for (int mt = 0; mt < 4; ++mt) {
       // the tile's base angles t0 w_l, exact, one frequency per lane
       {
-        const double turns = (double)(pos0 + mt * 16) * wt;
-        const float f = (float)(turns - floor(turns));
-        ang[wave][0][lane] = __builtin_amdgcn_cosf(f);
-        ang[wave][1][lane] = __builtin_amdgcn_sinf(f);
+        float sn, cs;
+        rope_sincos_turns((double)(pos0 + mt * 16), wt, sn, cs);
+        ang[wave][0][lane] = cs;
+        ang[wave][1][lane] = sn;
       }
       rb16x8 av[KS];
       const bool tv = (tmask >> mt) & 1u;
