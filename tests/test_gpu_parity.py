@@ -472,6 +472,14 @@ def test_rope_long_split_plans(batch, ctx, top_k):
     run_case(wl, batch=batch, ctx=ctx, seq_lens=lens, top_k=top_k)
 
 
+@pytest.mark.parametrize("page_size", [8, 16, 64])
+def test_rope_page_sizes(page_size):
+    """RoPE routing and attention at the other page sizes (pages per 64-token
+    step 8, 4 and 1/2), ragged lengths."""
+    wl = workload("llama8b-ctx32k-rope").with_(page_size=page_size)
+    run_case(wl, batch=2, ctx=4096, seq_lens=[4096, 1500], top_k=4096 // page_size // 8)
+
+
 def test_rope_long_positions():
     """Positions up to 131071: rotation angles of the highest frequency reach
     about 1.3e5 radians, where the turn count has to be reduced exactly."""
