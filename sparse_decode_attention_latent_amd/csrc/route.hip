@@ -102,8 +102,6 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int chunk = work - bg * a.chunks_per_bg;
   const int b = bg / a.n_kv, g = bg - b * a.n_kv;
 
-  const int L = clamp_len(seq_lens[b], a.cap);
-  const int NP = (L + a.page_size - 1) >> a.log2_page;
   const int p_begin = chunk * a.pages_per_wg;
   const int p_end = min(a.max_pages, p_begin + a.pages_per_wg);
   const int ppi = kWave >> a.log2_page;  // pages per wave step
@@ -119,47 +117,73 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   const int64_t page_z_bytes = (int64_t)a.geom.z_page_chunks * a.page_size * 16;
   const int64_t page_r_bytes = (int64_t)a.geom.r_page_chunks * a.page_size * 16;
 
+  // The lane's block-table entry (every entry of the row is in bounds), the
+  // sequence length and the projected queries are requested together; the
+  // page loads are issued as soon as they arrive, and the queries are staged
+  // in LDS while the pages are in flight.  A step then costs two dependent
+  // round trips, not the three of staging the queries first.  (Measured:
+  // qwen32b-shaped scoring 48.2 -> 46.8 us, llama8b-shaped 59.6 -> 59.1 us;
+  // converting the queries before issuing the page loads saves the 8-head
+  // kernel 8 registers, five instead of four wavefronts per SIMD, but measured
+  // 48.0 us.)
+  const int step = wave;
+  const int p = p_begin + step * ppi + (lane >> a.log2_page);
+  const bool in_range = step < n_steps && p < p_end;
+  const int phys = in_range ? bt[p] : -1;
+  const int L = clamp_len(seq_lens[b], a.cap);
+  const int NP = (L + a.page_size - 1) >> a.log2_page;
+  constexpr int QN = MF ? QG * NST * 4 : 1;  // staged query entries
+  constexpr int QI = (QN + 255) / 256;       // per thread (256 threads)
+  float4 qv_in[QI];
   if constexpr (MF) {
-    for (int i = threadIdx.x; i < QG * NST * 4; i += blockDim.x) {
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int i = u * 256 + threadIdx.x;
       const int hq = i & 3, st = (i >> 2) % NST, qd = i / (NST * 4);
-      const float4 v = *reinterpret_cast<const float4 *>(qp + (qd * 4 + hq) * W + st * 4);
+      qv_in[u] = i < QN ? *reinterpret_cast<const float4 *>(qp + (qd * 4 + hq) * W + st * 4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const int tok = p * a.page_size + slot;
+  const bool valid = in_range && p < NP && tok < L && phys >= 0 && phys < a.num_phys;
+  // matrix-core path: every lane joins the matrix instructions; one without a
+  // valid token scores zeros and is masked
+  uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
+  if constexpr (MF) {
+#pragma unroll
+    for (int c = 0; c < NZ; ++c) cz[c] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int c = 0; c < NR; ++c) cr[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) {
+      const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
+      const int64_t roff =
+          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
+#pragma unroll
+      for (int c = 0; c < NZ; ++c)
+        cz[c] = load_page_chunk<STREAM>(zpool, zoff + (int64_t)c * a.page_size * 16);
+#pragma unroll
+      for (int c = 0; c < NR; ++c)
+        cr[c] = load_page_chunk<STREAM>(rpool, roff + (int64_t)c * a.page_size * 16);
+    }
+    // the queries (arrived with the block-table entry) into LDS while the
+    // pages are in flight
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int i = u * 256 + threadIdx.x;
+      const float4 v = qv_in[u];
       const uint32_t h01 = f32x2_to_bf16x2(v.x, v.y), h23 = f32x2_to_bf16x2(v.z, v.w);
       const uint32_t l01 = f32x2_to_bf16x2(v.x - __uint_as_float(h01 << 16),
                                            v.y - __uint_as_float(h01 & 0xffff0000u));
       const uint32_t l23 = f32x2_to_bf16x2(v.z - __uint_as_float(h23 << 16),
                                            v.w - __uint_as_float(h23 & 0xffff0000u));
-      qf[i] = make_uint4(h01, h23, l01, l23);
+      if (i < QN) qf[i] = make_uint4(h01, h23, l01, l23);
     }
     __syncthreads();
   }
 
-  if (const int step = wave; step < n_steps) {
-    const int p = p_begin + step * ppi + (lane >> a.log2_page);
-    const bool in_range = p < p_end;
-    const int tok = p * a.page_size + slot;
-    int phys = -1;
-    if (in_range && p < NP) phys = bt[p];
-    const bool valid = in_range && p < NP && tok < L && phys >= 0 && phys < a.num_phys;
+  if (step < n_steps) {
     float best = -INFINITY;
     if constexpr (MF) {
-      // every lane joins the matrix instructions; one without a valid token
-      // scores zeros and is masked
-      uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
-#pragma unroll
-      for (int c = 0; c < NZ; ++c) cz[c] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-      for (int c = 0; c < NR; ++c) cr[c] = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) {
-        const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
-        const int64_t roff =
-            (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
-#pragma unroll
-        for (int c = 0; c < NZ; ++c)
-          cz[c] = load_page_chunk<STREAM>(zpool, zoff + (int64_t)c * a.page_size * 16);
-#pragma unroll
-        for (int c = 0; c < NR; ++c)
-          cr[c] = load_page_chunk<STREAM>(rpool, roff + (int64_t)c * a.page_size * 16);
-      }
       route_f4 sc[QG];
 #pragma unroll
       for (int qd = 0; qd < QG; ++qd) sc[qd] = route_f4{0.f, 0.f, 0.f, 0.f};
@@ -200,7 +224,6 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
       const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
       const int64_t roff =
           (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
-      uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
 #pragma unroll
       for (int c = 0; c < NZ; ++c) {
         const int64_t o = zoff + (int64_t)c * a.page_size * 16;
