@@ -293,8 +293,15 @@ int32_t basiskv_pack_output_matrix(const basiskv_dims *dims, const void *M_plain
 /* A whole decode step of one layer in one call, with the same results as
  *   basiskv_compress_prefill(k_new, v_new, start_pos, n_tokens = 1),
  *   basiskv_route_pages, basiskv_sparse_attend, basiskv_reconstruct
- * in that order (the compression and the query projection share one launch;
- * five launches in all, stream-ordered, no host synchronisation).
+ * in that order, bit for bit.  Five launches, stream-ordered, no host
+ * synchronisation: the query projection; the scoring; the selection;
+ * attention; reconstruction.  Where the scan is long (routing reads of 160 MiB
+ * or more over the pool's capacity, batch * n_kv_heads * max_pages_per_seq *
+ * page_size tokens) the scoring launch's first workgroups compress the new
+ * tokens and score them while the rest scan the other tokens, and the
+ * selection first folds each new token's score into its page's (page_scores
+ * then holds the full scores); otherwise, and with rotary positions, the
+ * compression shares the projection's launch.
  *   k_new, v_new [batch][n_kv_heads][head_dim]: the step's new token of every
  *     sequence, written at position start_pos[b] (device int32 [batch]);
  *     seq_lens must already count it.

@@ -85,7 +85,9 @@ size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 //                launch elects the workgroup that merges a row's splits;
 //                zero after allocation, and every call leaves them zero
 //   [C, C + U)   (bf16 decode step) u as the reconstruction's A operand
-//   [C + U, ..)  scratch: the projected queries during routing, then the
+//   [C + U, +N)  (decode step) the new token's score per (sequence, KV head),
+//                from the scoring launch to the selection launch
+//   [C + U + N, ..)  scratch: the projected queries during routing, then the
 //                attention splits' partial records (stream order keeps the
 //                two uses apart)
 size_t counter_bytes(const basiskv_dims &d) {  // one per (sequence, query subgroup)
@@ -108,13 +110,22 @@ size_t partial_bytes(const basiskv_dims &d, int32_t top_k) {
   return align_up((size_t)d.batch * d.n_q_heads * ns * (d.r_v + 2) * sizeof(float));
 }
 
-size_t scratch_offset(const basiskv_dims &d) { return counter_bytes(d) + utile_bytes(d); }
+size_t newtok_bytes(const basiskv_dims &d) {
+  return align_up((size_t)d.batch * d.n_kv_heads * sizeof(float));
+}
+
+size_t scratch_offset(const basiskv_dims &d) {
+  return counter_bytes(d) + utile_bytes(d) + newtok_bytes(d);
+}
 
 int32_t *attend_counters(void *ws) { return static_cast<int32_t *>(ws); }
 uint16_t *u_tiles(void *ws, const basiskv_dims &d) {
   return bkv_host::act_bf16(d)
              ? reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + counter_bytes(d))
              : nullptr;
+}
+float *newtok_scores(void *ws, const basiskv_dims &d) {
+  return reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes(d) + utile_bytes(d));
 }
 float *scratch_area(void *ws, const basiskv_dims &d) {
   return reinterpret_cast<float *>(static_cast<char *>(ws) + scratch_offset(d));
@@ -218,7 +229,9 @@ int32_t basiskv_select_pages(const basiskv_dims *d, const float *page_scores,
   if (st) return st;
   if (!page_scores || !seq_lens || !sel) return BASISKV_ERR_NULL;
   if (top_k < 1) return BASISKV_ERR_SHAPE;
-  return launched(bkv_host::launch_select(*d, page_scores, seq_lens, top_k, sel, as_stream(stream)));
+  // (the scores are only read: nothing is folded in without new-token scores)
+  return launched(bkv_host::launch_select(*d, const_cast<float *>(page_scores), seq_lens, top_k,
+                                          sel, as_stream(stream)));
 }
 
 int32_t basiskv_score_pages_rope(const basiskv_dims *d, const void *q, const void *P,
@@ -315,6 +328,21 @@ int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_ne
   return BASISKV_OK;
 }
 
+// Whether the decode step compresses its new tokens inside the scoring
+// launch.  There the compression (a chain of dependent memory round trips,
+// longer under the scan's load, in a register budget kept to the scan's)
+// is hidden only behind a long scan.  Measured per step against compressing
+// in the projection's launch: with routing reads of 200 MB and more
+// (llama8b- and qwen32b-shaped layers at 32K context, bf16 or E4M3 pages)
+// 0.5-2 us shorter; with 150 MB or less (4K context, the 4-token-page
+// routers) 1-4 us longer, the compression outlasting the scan.
+constexpr double kBesideScanMinBytes = 160.0 * (1 << 20);
+bool compress_beside_scan(const basiskv_dims &d) {
+  const double bytes = (double)d.batch * d.n_kv_heads * d.max_pages_per_seq * d.page_size *
+                       (d.r_b + d.r_q) * (bkv_host::cache_fp8(d) ? 1 : bkv_host::act_bf16(d) ? 2 : 4);
+  return bytes >= kBesideScanMinBytes;
+}
+
 // The launches of a decode step, after check_decode_step.
 int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_new,
                            const void *v_new, const int32_t *start_pos, const void *A,
@@ -323,17 +351,25 @@ int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_n
                            int32_t *sel, float *u, void *y, void *ws, hipStream_t s) {
   float *scr = scratch_area(ws, *d);
   bool unsupported = false;
-  // (a0) + (a1) in one launch, which also clears the attention's merge
-  // counters; then (a2), (a3), (a4), (a5)
   const int n_counters = (int)(counter_bytes(*d) / sizeof(int32_t));
+  const bool rope = has_rope(c);
+  const bool beside = !rope && compress_beside_scan(*d);
+  // (a1) in one launch, which also clears the attention's merge counters;
+  // with a long scan the new tokens' compression (a0) runs inside the scoring
+  // launch (a2), beside the scan, and the selection (a3) folds their scores
+  // in; otherwise (and with rotary positions) it shares the first launch.
+  // Then (a4), (a5).
   if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr,
-                                     attend_counters(ws), n_counters, s) != hipSuccess)
+                                     attend_counters(ws), n_counters, s, !beside) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
-  hipError_t e = has_rope(c)
-                     ? bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, s, &unsupported)
-                     : bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported);
+  bkv_host::StepTokens tokens{k_new, v_new, A, P, E, start_pos, newtok_scores(ws, *d)};
+  hipError_t e = rope ? bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, s, &unsupported)
+                      : bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported,
+                                               beside ? &tokens : nullptr);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
-  if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s) != hipSuccess)
+  if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s,
+                              beside ? start_pos : nullptr,
+                              beside ? tokens.new_scores : nullptr) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
   uint16_t *ut = u_tiles(ws, *d);  // attention also leaves u as the reconstruction's operand
   e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scr, attend_counters(ws), ut, s,

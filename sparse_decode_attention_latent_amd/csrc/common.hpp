@@ -353,15 +353,25 @@ inline void *residual_pool(const basiskv_dims &d, const basiskv_cache &c) {
 
 hipError_t launch_project(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                           float *q_proj, hipStream_t s);
+// A decode step's new tokens (one per sequence), compressed and scored inside
+// the scoring launch; the selection launch then folds new_scores into the
+// page scores (launch_select's new_pos / new_scores).
+struct StepTokens {
+  const void *k_new, *v_new, *A, *P, *E;
+  const int32_t *start_pos;
+  float *new_scores;  // [batch * n_kv_heads]
+};
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
-                        float *scores, hipStream_t s, bool *unsupported);
+                        float *scores, hipStream_t s, bool *unsupported,
+                        const StepTokens *step = nullptr);
 bool score_rope_supported(const basiskv_dims &d);
 hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                              const basiskv_cache &c, float *scores, hipStream_t s,
                              bool *unsupported);
 bool attend_supported(const basiskv_dims &d, bool rope);
-hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
-                         int32_t top_k, int32_t *sel, hipStream_t s);
+hipError_t launch_select(const basiskv_dims &d, float *scores, const int32_t *seq_lens,
+                         int32_t top_k, int32_t *sel, hipStream_t s,
+                         const int32_t *new_pos = nullptr, const float *new_scores = nullptr);
 int attend_splits(const basiskv_dims &d, int32_t top_k);
 int attend_group_split(const basiskv_dims &d);
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,
@@ -379,7 +389,7 @@ hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void
                                 const void *v_new, const int32_t *start_pos, const void *A,
                                 const void *P, const void *Q, const void *E,
                                 const basiskv_cache &c, float *q_proj, int32_t *counters,
-                                int n_counters, hipStream_t s);
+                                int n_counters, hipStream_t s, bool with_append = true);
 hipError_t launch_compress(const basiskv_dims &d, const void *k, const void *v,
                            const int32_t *start_pos, int32_t n_tokens, const void *A,
                            const void *P, const void *E, const basiskv_cache &c, hipStream_t s);

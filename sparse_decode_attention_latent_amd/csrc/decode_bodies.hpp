@@ -54,7 +54,11 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 // Compression of token `row` (= b * n_tokens + t) for KV head g, by a
 // workgroup of 256 threads.  T: input and factor elements; C: cache elements
 // (T itself, or E4M3 codes beside bf16 inputs: then the Key is rounded too).
-template <typename T, typename C>
+// LOWREG: each phase requests its own factor chunks, four at a time, when it
+// starts, instead of all of them up front -- the same arithmetic in the same
+// order (identical results) in far fewer registers, for a body that runs
+// inside another launch whose register budget it must not raise.
+template <typename T, typename C, bool LOWREG = false>
 __device__ __forceinline__ void append_body(
     const T *__restrict__ kin, const T *__restrict__ vin, const int32_t *__restrict__ start_pos,
     const T *__restrict__ A, const T *__restrict__ P, const T *__restrict__ E,
@@ -87,19 +91,62 @@ __device__ __forceinline__ void append_body(
   const T *Ag = A + (int64_t)g * DH * a.rv;
   const T *Pg = P + (int64_t)g * a.rb * DH;
   const T *Eg = E + (int64_t)g * DH * a.rq;
-  uint4 fa[MAXL], fp[MAXL], fe[MAXL];
+  constexpr int NF = LOWREG ? 1 : MAXL;  // prefetched chunks per factor
+  uint4 fa[NF], fp[NF], fe[NF];
+  if constexpr (!LOWREG) {
 #pragma unroll
-  for (int l = 0; l < MAXL; ++l) {
-    const int d = s1 * L1 + l;
-    if (c1 < C1 && l < L1 && d < DH)
-      fa[l] = *reinterpret_cast<const uint4 *>(Ag + (int64_t)d * a.rv + c1 * CE);
-    const int j = s2 * L2 + l;
-    if (c2 < C2 && l < L2 && j < a.rb)
-      fp[l] = *reinterpret_cast<const uint4 *>(Pg + (int64_t)j * DH + c2 * CE);
-    const int d3 = s3 * L3 + l;
-    if (c3 < C3 && l < L3 && d3 < DH)
-      fe[l] = *reinterpret_cast<const uint4 *>(Eg + (int64_t)d3 * a.rq + c3 * CE);
+    for (int l = 0; l < MAXL; ++l) {
+      const int d = s1 * L1 + l;
+      if (c1 < C1 && l < L1 && d < DH)
+        fa[l] = *reinterpret_cast<const uint4 *>(Ag + (int64_t)d * a.rv + c1 * CE);
+      const int j = s2 * L2 + l;
+      if (c2 < C2 && l < L2 && j < a.rb)
+        fp[l] = *reinterpret_cast<const uint4 *>(Pg + (int64_t)j * DH + c2 * CE);
+      const int d3 = s3 * L3 + l;
+      if (c3 < C3 && l < L3 && d3 < DH)
+        fe[l] = *reinterpret_cast<const uint4 *>(Eg + (int64_t)d3 * a.rq + c3 * CE);
+    }
   }
+  // acc[e] += w(l) * row l of a factor, l in order; rows come from the
+  // prefetched chunks or (LOWREG) four at a time from memory
+  auto phase = [&](float (&acc)[CE], const uint4 *pre, bool on, int n_rows, int lim, int first,
+                   const T *base, int64_t stride, int col, const float *wv) {
+    if constexpr (!LOWREG) {
+#pragma unroll
+      for (int l = 0; l < MAXL; ++l) {
+        const int r = first + l;
+        if (on && l < n_rows && r < lim) {
+          float x[CE];
+          unpack_chunk<T>(pre[l], x);
+          const float w = wv[r];
+#pragma unroll
+          for (int e = 0; e < CE; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int l0 = 0; l0 < MAXL; l0 += 4) {
+        uint4 ch[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int l = l0 + u, r = first + l;
+          if (on && l < n_rows && r < lim)
+            ch[u] = *reinterpret_cast<const uint4 *>(base + (int64_t)r * stride + col * CE);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int l = l0 + u, r = first + l;
+          if (on && l < n_rows && r < lim) {
+            float x[CE];
+            unpack_chunk<T>(ch[u], x);
+            const float w = wv[r];
+#pragma unroll
+            for (int e = 0; e < CE; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+          }
+        }
+      }
+    }
+  };
   // the destination slot, looked up while the factors are in flight
   const int pos = start_pos[b] + t;
   const bool pos_ok = pos >= 0 && pos < a.cap;
@@ -116,19 +163,7 @@ __device__ __forceinline__ void append_body(
   // ---- z = v A_g; z_s = round(z) ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (c1 < C1) {
-#pragma unroll
-    for (int l = 0; l < MAXL; ++l) {
-      const int d = s1 * L1 + l;
-      if (l < L1 && d < DH) {
-        float x[CE];
-        unpack_chunk<T>(fa[l], x);
-        const float vd = v_s[d];
-#pragma unroll
-        for (int e = 0; e < CE; ++e) acc[e] = fmaf(vd, x[e], acc[e]);
-      }
-    }
-  }
+  phase(acc, fa, c1 < C1, L1, DH, s1 * L1, Ag, a.rv, c1, v_s);
   slice_sums<CE>(acc, P1, c1, C1, red);
   __syncthreads();
   if (tid < a.rv) {
@@ -142,19 +177,7 @@ __device__ __forceinline__ void append_body(
   // ---- x = k - z_s[:r_b] P_g ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (c2 < C2) {
-#pragma unroll
-    for (int l = 0; l < MAXL; ++l) {
-      const int j = s2 * L2 + l;
-      if (l < L2 && j < a.rb) {
-        float x[CE];
-        unpack_chunk<T>(fp[l], x);
-        const float zj = zf[j];
-#pragma unroll
-        for (int e = 0; e < CE; ++e) acc[e] = fmaf(zj, x[e], acc[e]);
-      }
-    }
-  }
+  phase(acc, fp, c2 < C2, L2, a.rb, s2 * L2, Pg, DH, c2, zf);
   slice_sums<CE>(acc, P2, c2, C2, red);
   __syncthreads();
   if (tid < DH) x_s[tid] = k_s[tid] - (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
@@ -163,19 +186,7 @@ __device__ __forceinline__ void append_body(
   // ---- r = x E_g; r_s = round(r) ----
 #pragma unroll
   for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (c3 < C3) {
-#pragma unroll
-    for (int l = 0; l < MAXL; ++l) {
-      const int d = s3 * L3 + l;
-      if (l < L3 && d < DH) {
-        float x[CE];
-        unpack_chunk<T>(fe[l], x);
-        const float xd = x_s[d];
-#pragma unroll
-        for (int e = 0; e < CE; ++e) acc[e] = fmaf(xd, x[e], acc[e]);
-      }
-    }
-  }
+  phase(acc, fe, c3 < C3, L3, DH, s3 * L3, Eg, a.rq, c3, x_s);
   slice_sums<CE>(acc, P3, c3, C3, red);
   __syncthreads();
   if (tid < a.rq)
@@ -212,30 +223,38 @@ __device__ __forceinline__ void append_body(
 }
 
 // ---------------------------------------------------------------------------
-// (a1) q_proj[b][h] = [P_g q_bh, Q_g q_bh]   (float32, exact widening of inputs)
-// One output per thread (outputs xblk * NT ... of KV head g of sequence b, NT
-// = the workgroup size, 128 or 256); its whole factor row (head_dim elements)
-// is requested before the queries are staged, so the two loads overlap.
+// (a1) q_proj[b][h] = [P_g q_bh, Q_g q_bh]   (float32; bf16 products are exact)
+// Rows j of [P_g; Q_g] (head_dim elements each) lie 16 lanes to a row, 8 dims
+// per lane, so a load instruction reads whole rows (256 or 512 contiguous
+// bytes each) rather than one 16-byte piece of 64 different rows.  A
+// workgroup of NT threads takes the NT / 16 rows of row block xblk of KV
+// head g for sequence b; its factor loads are in flight while the group's
+// queries are staged in LDS.  Each lane forms its 8-dim partial dot for every
+// head of the group, the row's 16 lanes sum them (DPP), and lane h of the row
+// stores head h's output.
 // ---------------------------------------------------------------------------
 template <typename T, int NT>
 __device__ __forceinline__ void project_body(const T *__restrict__ q, const T *__restrict__ P,
                                              const T *__restrict__ Q, float *__restrict__ q_proj,
                                              int n_q, int n_kv, int rb, int rq, int xblk, int g,
                                              int b) {
+  constexpr int RPW = NT / 16;                    // rows per workgroup
+  constexpr int NL = 8 * (int)sizeof(T) / 16;     // 16-byte loads per lane: 1 (bf16), 2 (float32)
   constexpr int CE = Elem<T>::CE;
-  constexpr int NC = kHeadDim / CE;
   __shared__ __align__(16) float qs[16][kHeadDim];
   const int G = n_q / n_kv;
   const int w = rb + rq;
-  const int o = xblk * NT + threadIdx.x;
-  const bool active = o < G * w;
-  const int h = active ? o / w : 0, j = active ? o % w : 0;
-  const T *row = j < rb ? P + ((int64_t)g * rb + j) * kHeadDim
-                        : Q + ((int64_t)g * rq + (j - rb)) * kHeadDim;
-  uint4 c[NC];
-  if (active) {  // the factor row is in flight while the queries are staged
+  const int c = threadIdx.x & 15;  // dims 8 c .. 8 c + 7
+  const int j = xblk * RPW + (threadIdx.x >> 4);
+  const bool active = j < w;
+  uint4 raw[NL];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) c[i] = reinterpret_cast<const uint4 *>(row)[i];
+  for (int l = 0; l < NL; ++l) raw[l] = make_uint4(0u, 0u, 0u, 0u);
+  if (active) {  // the factor row's 8 dims are in flight while the queries are staged
+    const T *row = j < rb ? P + ((int64_t)g * rb + j) * kHeadDim
+                          : Q + ((int64_t)g * rq + (j - rb)) * kHeadDim;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) raw[l] = reinterpret_cast<const uint4 *>(row + 8 * c)[l];
   }
   {  // the group's queries: G * head_dim elements (G <= 16), one batch of loads
     constexpr int QL = 16 * kHeadDim / NT;
@@ -253,16 +272,47 @@ __device__ __forceinline__ void project_body(const T *__restrict__ q, const T *_
     }
   }
   __syncthreads();
-  if (!active) return;
-  float acc = 0.f;
+  float x[8];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    float x[CE];
-    unpack_chunk<T>(c[i], x);
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc = fmaf(x[e], qs[h][i * CE + e], acc);
+  for (int l = 0; l < NL; ++l) unpack_chunk<T>(raw[l], x + l * CE);
+  // every lane takes part (inactive rows hold zeros): the sums read whole rows of lanes
+  float mine = 0.f;
+  for (int h = 0; h < G; ++h) {
+    const float4 q0 = *reinterpret_cast<const float4 *>(&qs[h][8 * c]);
+    const float4 q1 = *reinterpret_cast<const float4 *>(&qs[h][8 * c + 4]);
+    float part = x[0] * q0.x;
+    part = fmaf(x[1], q0.y, part);
+    part = fmaf(x[2], q0.z, part);
+    part = fmaf(x[3], q0.w, part);
+    part = fmaf(x[4], q1.x, part);
+    part = fmaf(x[5], q1.y, part);
+    part = fmaf(x[6], q1.z, part);
+    part = fmaf(x[7], q1.w, part);
+    part += dpp_move<0xB1>(part);   // lanes c ^ 1
+    part += dpp_move<0x4E>(part);   // lanes c ^ 2
+    part += dpp_move<0x141>(part);  // the other quad of the half-row
+    part += dpp_move<0x140>(part);  // the other half of the row
+    if (c == h) mine = part;
   }
-  q_proj[((int64_t)b * n_q + g * G + h) * w + j] = acc;
+  if (active && c < G) q_proj[((int64_t)b * n_q + g * G + c) * w + j] = mine;
 }
 
 }  // namespace bkv
+
+namespace bkv_host {
+// The decode step's append: one new token per sequence.
+inline bkv::AppendArgs step_append_args(const basiskv_dims &d) {
+  bkv::AppendArgs a;
+  a.n_tokens = 1;
+  a.n_kv = d.n_kv_heads;
+  a.rv = d.r_v;
+  a.rb = d.r_b;
+  a.rq = d.r_q;
+  a.max_pages = d.max_pages_per_seq;
+  a.num_phys = d.num_phys_pages;
+  a.page_size = d.page_size;
+  a.cap = d.max_pages_per_seq * d.page_size;
+  a.geom = pool_geom(d);
+  return a;
+}
+}  // namespace bkv_host

@@ -10,7 +10,7 @@ namespace bkv {
 
 // ---------------------------------------------------------------------------
 // (a1) query projection launch; the body is in decode_bodies.hpp.
-// grid (ceil(G * (r_b + r_q) / 128), n_kv, batch), 128 threads.
+// grid (ceil((r_b + r_q) / 8), n_kv, batch), 128 threads.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(128) void project_queries_kernel(
@@ -24,18 +24,34 @@ __global__ __launch_bounds__(128) void project_queries_kernel(
 // ---------------------------------------------------------------------------
 // Standalone selection: grid (n_kv, batch), 64 * NWV threads.  With a recent
 // window of `recent` tokens the candidates are the pages before the window.
+// With new_scores (a decode step whose scoring left each sequence's new token,
+// at new_pos[b], to the compression workgroups) that token's score is first
+// folded into its page's score, max(page, token), which is also written back.
 template <int KPT, int NWV>
 __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k,
-    int recent) {
+    int recent, const int32_t *__restrict__ new_pos, const float *__restrict__ new_scores) {
   const int g = blockIdx.x, b = blockIdx.y;
   // the whole row is requested before the sequence length arrives
-  const float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
+  float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
   const int base = (threadIdx.x >> 6) * 64 * KPT + (threadIdx.x & 63);
   float v[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) v[j] = base + 64 * j < max_pages ? row[base + 64 * j] : 0.f;
+  if (new_scores) {
+    const int pos = new_pos[b];
+    const float ns = new_scores[(int64_t)b * n_kv + g];
+    const int np = pos >= 0 && pos < cap ? pos / page_size : -1;
+    if (np >= 0 && ns != -INFINITY) {  // (-inf: the token does not count)
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (base + 64 * j == np) {
+          v[j] = fmaxf(v[j], ns);
+          row[np] = v[j];
+        }
+    }
+  }
   const int L = clamp_len(seq_lens[b], cap);
   const int NP = recent > 0 ? max(0, L - recent) / page_size : (L + page_size - 1) / page_size;
   int32_t *out = sel + ((int64_t)b * n_kv + g) * k;
@@ -67,10 +83,29 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // few loads per lane their longer latency is not hidden.
 // ---------------------------------------------------------------------------
 
+// The decode step's new tokens compressed inside the scoring launch (n_append
+// > 0): the first app_padded workgroups of the grid each compress the new
+// token of one (sequence, KV head) -- with the low-register body, so that the
+// launch keeps the scan's register budget -- and then score that token with
+// the scan's own arithmetic into new_scores; the scan leaves the token at
+// start_pos[b] out of its page's score, and the selection launch takes the
+// maximum of the two.  Max is exact, so the page scores are those of scoring
+// after the compression, while the compression's chain of round trips runs
+// beside the scan instead of before it.
+struct DeferArgs {
+  const void *k_new, *v_new, *A, *P, *E;  // new tokens and factors (activation type)
+  const int32_t *start_pos;               // the new token's position per sequence
+  void *zpool, *rpool, *kpool;            // the pools it is written to
+  float *new_scores;                      // [batch * n_kv] the new token's score (-inf: none)
+  AppendArgs ap;
+  int n_append, app_padded;  // batch * n_kv workgroups, padded to a multiple of the XCD count
+};
+
 struct ScoreArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap;
   int pages_per_wg, chunks_per_bg, total, padded;
   PoolGeom geom;  // chunk positions of the latent and residual pages
+  DeferArgs df;   // df.n_append = 0: scoring only
 };
 
 typedef short route_s4 __attribute__((ext_vector_type(4)));
@@ -86,7 +121,7 @@ typedef float route_f4 __attribute__((ext_vector_type(4)));
 // float32.  The query operands are staged in LDS once per workgroup.
 template <typename T, int G, int NZ, int NR, bool STREAM, bool MF>
 __global__ __launch_bounds__(256) void route_scan_kernel(
-    const float *__restrict__ q_proj, const T *__restrict__ zpool, const T *__restrict__ rpool,
+    const float *__restrict__ q_proj, const T *zpool, const T *rpool,  // (written by compression)
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     float *__restrict__ scores, ScoreArgs a) {
   constexpr int CE = Elem<T>::CE;
@@ -96,11 +131,32 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   static_assert(!MF || (G % 4 == 0 && sizeof(T) <= 2), "matrix-core logits: bf16/E4M3, G % 4 == 0");
   // [quad][step][head in quad]: {hi 4 x bf16, lo 4 x bf16}
   __shared__ __align__(16) uint4 qf[MF ? QG * NST * 4 : 1];
-  const int work = xcd_work_index(a.padded);
-  if (work >= a.total) return;
-  const int bg = work / a.chunks_per_bg;
-  const int chunk = work - bg * a.chunks_per_bg;
+  using TA = typename std::conditional<sizeof(T) == 1, uint16_t, T>::type;  // activations
+  // compression workgroups first (app_padded of them, a multiple of the XCD
+  // count, so the scan's workgroups keep their XCD placement)
+  int bid = blockIdx.x;
+  const bool compress = bid < a.df.app_padded;  // (workgroup-uniform)
+  if (compress && bid >= a.df.n_append) return;
+  int bg, chunk = 0;
+  if (compress) {
+    bg = bid;  // b * n_kv + g
+  } else {
+    bid -= a.df.app_padded;
+    const int per_xcd = a.padded / kXcds;
+    const int work = (bid % kXcds) * per_xcd + bid / kXcds;
+    if (work >= a.total) return;
+    bg = work / a.chunks_per_bg;
+    chunk = work - bg * a.chunks_per_bg;
+  }
   const int b = bg / a.n_kv, g = bg - b * a.n_kv;
+  if (compress) {
+    append_body<TA, T, true>(
+        static_cast<const TA *>(a.df.k_new), static_cast<const TA *>(a.df.v_new), a.df.start_pos,
+        static_cast<const TA *>(a.df.A), static_cast<const TA *>(a.df.P),
+        static_cast<const TA *>(a.df.E), static_cast<T *>(a.df.zpool),
+        static_cast<T *>(a.df.rpool), static_cast<T *>(a.df.kpool), block_table, a.df.ap, g, b);
+    __syncthreads();  // the token's codes are stored, and visible to this workgroup
+  }
 
   const int p_begin = chunk * a.pages_per_wg;
   const int p_end = min(a.max_pages, p_begin + a.pages_per_wg);
@@ -127,8 +183,16 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   // kernel 8 registers, five instead of four wavefronts per SIMD, but measured
   // 48.0 us.)
   const int step = wave;
-  const int p = p_begin + step * ppi + (lane >> a.log2_page);
-  const bool in_range = step < n_steps && p < p_end;
+  int p = p_begin + step * ppi + (lane >> a.log2_page);
+  bool in_range = step < n_steps && p < p_end;
+  int slot_t = slot;  // the lane's token slot in its page
+  const int newpos = a.df.n_append > 0 ? a.df.start_pos[b] : -1;
+  if (compress) {  // one token: the new one, in thread 0
+    const bool pos_ok = newpos >= 0 && newpos < a.cap;
+    p = pos_ok ? newpos >> a.log2_page : 0;
+    slot_t = newpos & (a.page_size - 1);
+    in_range = pos_ok && threadIdx.x == 0;
+  }
   const int phys = in_range ? bt[p] : -1;
   const int L = clamp_len(seq_lens[b], a.cap);
   const int NP = (L + a.page_size - 1) >> a.log2_page;
@@ -144,8 +208,10 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  const int tok = p * a.page_size + slot;
-  const bool valid = in_range && p < NP && tok < L && phys >= 0 && phys < a.num_phys;
+  const int tok = p * a.page_size + slot_t;
+  // (the scan leaves the new token to the compression workgroups)
+  const bool valid = in_range && p < NP && tok < L && phys >= 0 && phys < a.num_phys &&
+                     (compress || tok != newpos);
   // matrix-core path: every lane joins the matrix instructions; one without a
   // valid token scores zeros and is masked
   uint4 cz[NZ > 0 ? NZ : 1], cr[NR > 0 ? NR : 1];  // (a width may be 0)
@@ -155,9 +221,9 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 #pragma unroll
     for (int c = 0; c < NR; ++c) cr[c] = make_uint4(0u, 0u, 0u, 0u);
     if (valid) {
-      const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
+      const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot_t * 16;
       const int64_t roff =
-          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
+          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot_t) * 16;
 #pragma unroll
       for (int c = 0; c < NZ; ++c)
         cz[c] = load_page_chunk<STREAM>(zpool, zoff + (int64_t)c * a.page_size * 16);
@@ -181,7 +247,7 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
     __syncthreads();
   }
 
-  if (step < n_steps) {
+  if (compress ? wave == 0 : step < n_steps) {
     float best = -INFINITY;
     if constexpr (MF) {
       route_f4 sc[QG];
@@ -221,9 +287,9 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
         for (int h = 0; h < G; ++h) best = fmaxf(best, sc[h / 4][h % 4]);
       }
     } else if (valid) {
-      const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot * 16;
+      const int64_t zoff = (zhead + phys) * page_z_bytes + (int64_t)slot_t * 16;
       const int64_t roff =
-          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot) * 16;
+          (zhead + phys) * page_r_bytes + ((int64_t)a.geom.r_first * a.page_size + slot_t) * 16;
 #pragma unroll
       for (int c = 0; c < NZ; ++c) {
         const int64_t o = zoff + (int64_t)c * a.page_size * 16;
@@ -258,6 +324,10 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) best = fmaxf(best, acc[h]);
+    }
+    if (compress) {  // thread 0's token alone
+      if (threadIdx.x == 0) a.df.new_scores[bg] = best;  // (-inf when it does not count)
+      return;
     }
     best = group_max(best, a.page_size);
     if (in_range && slot == 0) out[p] = (p < NP) ? best : -INFINITY;
@@ -549,9 +619,8 @@ void route_rope_kernel(
 template <typename T>
 hipError_t project_t(const basiskv_dims &d, const void *q, const void *P, const void *Q,
                      float *q_proj, hipStream_t s) {
-  const int G = d.n_q_heads / d.n_kv_heads;
-  const int outs = G * (d.r_b + d.r_q);
-  hipLaunchKernelGGL(project_queries_kernel<T>, dim3((outs + 127) / 128, d.n_kv_heads, d.batch),
+  const int row_blocks = (d.r_b + d.r_q + 7) / 8;  // 8 rows per 128-thread workgroup
+  hipLaunchKernelGGL(project_queries_kernel<T>, dim3(row_blocks, d.n_kv_heads, d.batch),
                      dim3(128), 0, s,
                      (const T *)q, (const T *)P, (const T *)Q, q_proj, d.n_q_heads, d.n_kv_heads,
                      d.r_b, d.r_q);
@@ -683,7 +752,7 @@ hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P
     return hipSuccess;
   }
   *unsupported = false;
-  ScoreArgs a;
+  ScoreArgs a{};
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -712,14 +781,29 @@ hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P
 }
 
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
-                        float *scores, hipStream_t s, bool *unsupported) {
+                        float *scores, hipStream_t s, bool *unsupported, const StepTokens *step) {
   const void *fn = find_score(d);
   if (!fn) {
     *unsupported = true;
     return hipSuccess;
   }
   *unsupported = false;
-  ScoreArgs a;
+  ScoreArgs a{};
+  if (step) {  // the step's new tokens compressed and scored in this launch
+    a.df.k_new = step->k_new;
+    a.df.v_new = step->v_new;
+    a.df.A = step->A;
+    a.df.P = step->P;
+    a.df.E = step->E;
+    a.df.start_pos = step->start_pos;
+    a.df.zpool = c.z_pages;
+    a.df.rpool = residual_pool(d, c);
+    a.df.kpool = c.k_pages;
+    a.df.new_scores = step->new_scores;
+    a.df.ap = step_append_args(d);
+    a.df.n_append = d.batch * d.n_kv_heads;
+    a.df.app_padded = (a.df.n_append + kXcds - 1) / kXcds * kXcds;
+  }
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -737,7 +821,7 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   void *rpool = residual_pool(d, c);
   void *args[] = {(void *)&q_proj, (void *)&c.z_pages, (void *)&rpool,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&scores, (void *)&a};
-  return hipLaunchKernel(fn, dim3(a.padded), dim3(256), args, 0, s);
+  return hipLaunchKernel(fn, dim3(a.df.app_padded + a.padded), dim3(256), args, 0, s);
 }
 
 #ifndef BKV_SELECT_SMALL_WAVES
@@ -745,26 +829,27 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
 #endif
 constexpr int kSelectSmallWaves = BKV_SELECT_SMALL_WAVES;  // wavefronts per row up to 1024 pages
 
-hipError_t launch_select(const basiskv_dims &d, const float *scores, const int32_t *seq_lens,
-                         int32_t top_k, int32_t *sel, hipStream_t s) {
+hipError_t launch_select(const basiskv_dims &d, float *scores, const int32_t *seq_lens,
+                         int32_t top_k, int32_t *sel, hipStream_t s, const int32_t *new_pos,
+                         const float *new_scores) {
   const int mp = d.max_pages_per_seq, cap = d.max_pages_per_seq * d.page_size;
   const dim3 grid(d.n_kv_heads, d.batch);
   if (mp <= 1024)
     hipLaunchKernelGGL((topk_select_kernel<16 / kSelectSmallWaves, kSelectSmallWaves>), grid,
                        dim3(64 * kSelectSmallWaves), 0, s, scores, seq_lens, sel, d.n_kv_heads, mp,
-                       d.page_size, cap, top_k, d.recent_tokens);
+                       d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
   else if (mp <= 4096)
     hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
   else if (mp <= 8192)
     hipLaunchKernelGGL((topk_select_kernel<8, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
   else if (mp <= 16384)
     hipLaunchKernelGGL((topk_select_kernel<16, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
   else
     hipLaunchKernelGGL((topk_select_kernel<32, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
   return hipGetLastError();
 }
 

@@ -1,7 +1,9 @@
 // One launch for the start of a decode step: the new token's compression
 // (a0) and the routing projection of the queries (a1) are independent, so
 // their workgroups share one grid (the first n_kv * batch workgroups
-// compress, the rest project).  The first workgroup also zeroes the counters
+// compress, the rest project).  Without with_append only the projection runs
+// here (the compression then runs inside the scoring launch; rotary-position
+// steps keep it here).  The first workgroup also zeroes the counters
 // with which the step's attention launch elects its merging workgroups (they
 // are left at zero by every call; clearing them here makes the step
 // independent of what an earlier call left in the workspace).  Bodies in
@@ -38,6 +40,20 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(
   }
 }
 
+// The start of a decode step whose compression runs inside the scoring
+// launch: the query projection alone (8 rows of [P; Q] per 128-thread
+// workgroup, as basiskv_project_queries), and the first workgroup zeroes the
+// attention's merge counters.
+template <typename T>
+__global__ __launch_bounds__(128) void step_project_kernel(
+    const T *__restrict__ q, const T *__restrict__ P, const T *__restrict__ Q,
+    float *__restrict__ q_proj, int n_q, int n_kv, int rb, int rq, int32_t *__restrict__ counters,
+    int n_counters) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < n_counters; i += blockDim.x) counters[i] = 0;
+  project_body<T, 128>(q, P, Q, q_proj, n_q, n_kv, rb, rq, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 }  // namespace bkv
 
 namespace bkv_host {
@@ -47,23 +63,14 @@ template <typename T, typename C>
 static hipError_t prologue_t(const basiskv_dims &d, const void *q, const void *k_new,
                              const void *v_new, const int32_t *start_pos, const void *A,
                              const void *P, const void *Q, const void *E, const basiskv_cache &c,
-                             float *q_proj, int32_t *counters, int n_counters, hipStream_t s) {
+                             float *q_proj, int32_t *counters, int n_counters, hipStream_t s,
+                             bool with_append) {
   PrologueArgs a;
   a.counters = counters;
   a.n_counters = n_counters;
-  a.ap.n_tokens = 1;
-  a.ap.n_kv = d.n_kv_heads;
-  a.ap.rv = d.r_v;
-  a.ap.rb = d.r_b;
-  a.ap.rq = d.r_q;
-  a.ap.max_pages = d.max_pages_per_seq;
-  a.ap.num_phys = d.num_phys_pages;
-  a.ap.page_size = d.page_size;
-  a.ap.cap = d.max_pages_per_seq * d.page_size;
-  a.ap.geom = pool_geom(d);
-  a.n_append = d.n_kv_heads * d.batch;
-  const int G = d.n_q_heads / d.n_kv_heads;
-  a.proj_x = (G * (d.r_b + d.r_q) + 255) / 256;
+  a.ap = step_append_args(d);
+  a.n_append = with_append ? d.n_kv_heads * d.batch : 0;
+  a.proj_x = (d.r_b + d.r_q + 15) / 16;  // 16 rows per 256-thread workgroup
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
   a.rb = d.r_b;
@@ -80,15 +87,27 @@ hipError_t launch_step_prologue(const basiskv_dims &d, const void *q, const void
                                 const void *v_new, const int32_t *start_pos, const void *A,
                                 const void *P, const void *Q, const void *E,
                                 const basiskv_cache &c, float *q_proj, int32_t *counters,
-                                int n_counters, hipStream_t s) {
+                                int n_counters, hipStream_t s, bool with_append) {
+  if (!with_append) {
+    const dim3 grid((d.r_b + d.r_q + 7) / 8, d.n_kv_heads, d.batch);
+    if (act_bf16(d))
+      hipLaunchKernelGGL(step_project_kernel<uint16_t>, grid, dim3(128), 0, s, (const uint16_t *)q,
+                         (const uint16_t *)P, (const uint16_t *)Q, q_proj, d.n_q_heads,
+                         d.n_kv_heads, d.r_b, d.r_q, counters, n_counters);
+    else
+      hipLaunchKernelGGL(step_project_kernel<float>, grid, dim3(128), 0, s, (const float *)q,
+                         (const float *)P, (const float *)Q, q_proj, d.n_q_heads, d.n_kv_heads,
+                         d.r_b, d.r_q, counters, n_counters);
+    return hipGetLastError();
+  }
   if (cache_fp8(d))
     return prologue_t<uint16_t, uint8_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
-                                         counters, n_counters, s);
+                                         counters, n_counters, s, with_append);
   return act_bf16(d)
              ? prologue_t<uint16_t, uint16_t>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
-                                              counters, n_counters, s)
+                                              counters, n_counters, s, with_append)
              : prologue_t<float, float>(d, q, k_new, v_new, start_pos, A, P, Q, E, c, q_proj,
-                                        counters, n_counters, s);
+                                        counters, n_counters, s, with_append);
 }
 
 }  // namespace bkv_host

@@ -561,6 +561,49 @@ def test_combined_calls_equal_the_separate_calls(wl_index):
     compare_step(wl, inp, prob, got, range(4))
 
 
+@pytest.mark.parametrize("name", ["llama8b-ctx32k", "qwen32b-ctx32k", "llama8b-ctx32k-fp8"])
+def test_step_new_token_scored_beside_the_scan(name):
+    """With a long scan (8 sequences of 32K-token capacity: 200 MB of routing
+    reads and more) the one-call step compresses and scores each sequence's
+    new token in workgroups of its own inside the scoring launch, the scan
+    leaves that token out, and the selection folds the token's score into
+    its page's.  With the new tokens scaled up (8x, either sign) some of them
+    hold their page's and their row's highest score: page scores, selection,
+    u and y are still bit-identical to the separate calls (which append first
+    and scan every token), and such a page is selected.  Ragged lengths: new
+    tokens that open a page, fill one, or are a sequence's only token."""
+    wl = workload(name)
+    S = wl.page_size
+    lens = [32768, 32768 - S + 1, 4096, S + 1, 1, 20000, S - 1, 2 * S]
+    inp = synth.decode_inputs(wl, batch=8, ctx=32768, seq_lens=lens)
+    decided = 0
+    for sign in (8.0, -8.0):
+        prob = DecodeProblem(wl, inp, top_k=16)
+        prob.k_new.mul_(sign)
+        prob.v_new.mul_(sign)
+        _say(f"new token x{sign} {name}: seq_lens={lens}")
+        prob.decode_step()
+        got = prob.outputs()
+        for t in (prob.page_scores, prob.u):
+            t.fill_(float("nan"))
+        prob.sel.fill_(-7)
+        prob.y.fill_(0)
+        prob.step_unfused(append=True)  # the same token appended again, then scanned with the rest
+        base = prob.outputs()
+        for key in ("scores", "sel", "u", "y"):
+            np.testing.assert_array_equal(got[key], base[key], err_msg=f"x{sign} {key}")
+        for b, L in enumerate(lens):
+            npg = (L - 1) // wl.page_size  # the new token's page
+            NP = -(-L // wl.page_size)
+            for g in range(wl.n_kv_heads):
+                row = got["scores"][b, g, :NP]
+                if row[npg] == row.max():
+                    decided += 1
+                    assert npg in set(got["sel"][b, g].tolist()), (b, g)
+    _say(f"  rows whose top page score is the new token's page: {decided}")
+    assert decided > 0
+
+
 def test_repeated_steps_reuse_the_workspace_bit_exact():
     """Steps that merge several attention splits (the merge counters return to
     zero after every call) give identical bits call after call."""
