@@ -75,6 +75,13 @@ def parse():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 64 MiB read + 64 MiB write elementwise kernel (torch.neg) "
                          "five times, the reference for HBM counter scaling")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run of this script "
+                         "(markdown to stdout): per-kernel durations, and the library's "
+                         "kernels split by pass in dispatch order")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="COUNTER_DIR",
+                    help="summarise rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 runs of this script, "
+                         "one directory per workload named mfma_<workload> (markdown to stdout)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE; --calibration-copy) into "
@@ -147,6 +154,94 @@ def pmc_summary(fetch_dir, write_dir, workload_name):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        sys.exit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _kernel_name(name):
+    """A kernel's demangled name without its parameter list."""
+    name = name.strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                return name[:i]
+    return name
+
+
+def trace_summary(trace_dir):
+    """Markdown summary of one rocprofv3 kernel trace of this script: rocprofv3's
+    own per-kernel statistics, then the library's kernels (bkv::) split by pass
+    in dispatch order.  Passes: the one-call steps (up to the first separate
+    compression call, append_kernel, which only the stage pass launches), the
+    stage pass (separate calls), and what follows it (cold steps after each
+    cache-flushing read, whose reduction kernel opens that pass; the prefill and
+    the decode sequence of the prefill + decode workload)."""
+    lines = []
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines += ["| kernel | calls | avg µs | min µs | max µs | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _kernel_name(r["Name"])
+        name = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f} |")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [_kernel_name(r["Kernel_Name"]) for r in trace]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    s1 = next((i for i, n in enumerate(names) if "append_kernel" in n), len(names))
+    s2 = next((i for i in range(s1, len(names)) if "reduce_kernel" in names[i]
+               or "compress_kernel" in names[i]), len(names))
+    lines += ["", "The library's kernels split by pass (dispatch order in the trace):", "",
+              "| kernel | pass | calls | avg µs |", "|---|---|---|---|"]
+    for label, lo, hi in (("one-call steps", 0, s1), ("stage pass", s1, s2),
+                          ("after the stage pass", s2, len(names))):
+        acc = {}
+        for n, d in zip(names[lo:hi], durs[lo:hi]):
+            if n.startswith("bkv::"):
+                acc.setdefault(n, []).append(d)
+        for n, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| `{n}` | {label} | {len(v)} | {sum(v) / len(v):.2f} |")
+    print("\n".join(lines))
+
+
+def mfma_summary(dirs):
+    """Markdown table of MfmaUtil and MfmaFlopsBF16 per dispatch of every
+    matrix-issuing kernel, one counter directory per workload."""
+    lines = ["| workload | kernel | dispatches | MfmaUtil % | MFMA GFLOP per dispatch |",
+             "|---|---|---|---|---|"]
+    for d in dirs:
+        wl = os.path.basename(os.path.normpath(d))
+        wl = wl[len("mfma_"):] if wl.startswith("mfma_") else wl
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = (_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        kernels = sorted({k for k, c in acc if k.startswith("bkv::")})
+        rows = []
+        for k in kernels:
+            util = acc.get((k, "MfmaUtil"), [0.0])
+            flops = acc.get((k, "MfmaFlopsBF16"), [0.0])
+            if max(flops) <= 0:
+                continue
+            rows.append((sum(util) / len(util), k, len(util), sum(flops) / len(flops) / 1e9))
+        for u, k, n, g in sorted(rows, reverse=True):
+            lines.append(f"| {wl} | `{k}` | {n} | {u:.2f} | {g:.3f} |")
+    print("\n".join(lines))
 
 
 def kernel_source_sha():
@@ -411,6 +506,12 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

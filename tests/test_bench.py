@@ -59,3 +59,63 @@ def test_byte_model_e4m3_pages_and_short_rows():
     full = traffic.attend_bytes(_c2(), lens)
     assert traffic.attend_bytes(_c2(), short) < full
     assert full - traffic.attend_bytes(_c2(), short) >= (4096 - 100) * 8 * 192 * 2 * 0.99
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(",".join(header) + "\n")
+        for r in rows:
+            f.write(",".join(f'"{v}"' for v in r) + "\n")
+
+
+def test_trace_summary_splits_passes_in_dispatch_order(tmp_path):
+    # a one-call step (scan, attention), then the stage pass (opened by the
+    # separate compression call), then a cold step opened by the flush's sum
+    d = tmp_path / "kt"
+    seq = [("bkv::route_scan_kernel<unsigned short, 4>(int*, int)", 10),
+           ("bkv::attend_split_kernel<unsigned short>(float*)", 4),
+           ("bkv::append_kernel<unsigned short>(int)", 2),
+           ("bkv::route_scan_kernel<unsigned short, 4>(int*, int)", 8),
+           ("at::native::reduce_kernel<512, 1>(float)", 30),
+           ("bkv::route_scan_kernel<unsigned short, 4>(int*, int)", 12)]
+    t, rows = 0, []
+    for name, us in seq:
+        rows.append((name, t, t + us * 1000))
+        t += us * 1000 + 500
+    _write_csv(str(d / "h" / "1" / "run_kernel_trace.csv"),
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    stats = {}
+    for name, us in seq:
+        stats.setdefault(name, []).append(us * 1000)
+    _write_csv(str(d / "h" / "1" / "run_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"],
+               [(n, len(v), sum(v), sum(v) / len(v), min(v), max(v)) for n, v in stats.items()])
+    r = subprocess.run([sys.executable, os.path.join(REPO, "bench.py"), "--trace-summary", str(d)],
+                       capture_output=True, text=True, cwd=REPO, timeout=60)
+    assert r.returncode == 0, r.stderr
+    out = r.stdout
+    assert "| `bkv::route_scan_kernel<unsigned short, 4>` | 3 | 10.00 | 8.00 | 12.00 |" in out
+    assert "| `bkv::route_scan_kernel<unsigned short, 4>` | one-call steps | 1 | 10.00 |" in out
+    assert "| `bkv::route_scan_kernel<unsigned short, 4>` | stage pass | 1 | 8.00 |" in out
+    assert "| `bkv::route_scan_kernel<unsigned short, 4>` | after the stage pass | 1 | 12.00 |" in out
+    assert "| `bkv::append_kernel<unsigned short>` | stage pass | 1 | 2.00 |" in out
+    assert "reduce_kernel<512, 1>` | 1 |" in out  # listed overall, not split by pass
+
+
+def test_mfma_summary_averages_per_dispatch(tmp_path):
+    d = tmp_path / "mfma_llama8b-ctx32k"
+    rows = [("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaUtil", 1.0),
+            ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaUtil", 3.0),
+            ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaFlopsBF16", 2e9),
+            ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaFlopsBF16", 4e9),
+            ("bkv::topk_select_kernel<4, 4>(int)", "MfmaUtil", 0.0),
+            ("bkv::topk_select_kernel<4, 4>(int)", "MfmaFlopsBF16", 0.0)]
+    _write_csv(str(d / "h" / "1" / "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    r = subprocess.run([sys.executable, os.path.join(REPO, "bench.py"), "--mfma-summary", str(d)],
+                       capture_output=True, text=True, cwd=REPO, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert ("| llama8b-ctx32k | `bkv::reconstruct_kernel<unsigned short, 1, true>` | 2 | 2.00 | 3.000 |"
+            in r.stdout)
+    assert "topk_select" not in r.stdout  # no matrix instructions: not listed
