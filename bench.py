@@ -170,8 +170,10 @@ def _csv_rows(d, suffix):
 
 
 def _kernel_name(name):
-    """A kernel's demangled name without its parameter list."""
+    """A kernel's demangled name without its return type and parameter list."""
     name = name.strip()
+    if name.startswith("void "):
+        name = name[len("void "):]
     if name.endswith(")"):
         depth = 0
         for i in range(len(name) - 1, -1, -1):

@@ -105,7 +105,7 @@ def test_trace_summary_splits_passes_in_dispatch_order(tmp_path):
 
 def test_mfma_summary_averages_per_dispatch(tmp_path):
     d = tmp_path / "mfma_llama8b-ctx32k"
-    rows = [("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaUtil", 1.0),
+    rows = [("void bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaUtil", 1.0),
             ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaUtil", 3.0),
             ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaFlopsBF16", 2e9),
             ("bkv::reconstruct_kernel<unsigned short, 1, true>(float)", "MfmaFlopsBF16", 4e9),
