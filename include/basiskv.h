@@ -301,7 +301,15 @@ int32_t basiskv_pack_output_matrix(const basiskv_dims *dims, const void *M_plain
  * tokens and score them while the rest scan the other tokens, and the
  * selection first folds each new token's score into its page's (page_scores
  * then holds the full scores); otherwise, and with rotary positions, the
- * compression shares the projection's launch.
+ * compression shares the projection's launch.  With such a long scan over
+ * pages of 8 or more tokens, bf16 or E4M3 pages, groups of a multiple of 4
+ * query heads and a routing width of at least 8 cached 16-byte chunks, the
+ * projection moves into the scoring launch as well (four launches): its
+ * workgroups come first in the grid, mark each block of projected rows done
+ * with the step's epoch, and the scanning workgroups wait for those marks
+ * before reading the projected queries.  The epoch is a word in the
+ * workspace that the selection launch advances, so the call may be captured
+ * in a graph and replayed.
  *   k_new, v_new [batch][n_kv_heads][head_dim]: the step's new token of every
  *     sequence, written at position start_pos[b] (device int32 [batch]);
  *     seq_lens must already count it.

@@ -87,7 +87,13 @@ size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 //   [C, C + U)   (bf16 decode step) u as the reconstruction's A operand
 //   [C + U, +N)  (decode step) the new token's score per (sequence, KV head),
 //                from the scoring launch to the selection launch
-//   [C + U + N, ..)  scratch: the projected queries during routing, then the
+//   [.., +T)     (bf16 / E4M3 decode step, groups of a multiple of 4 heads)
+//                the epoch word of the last step that projected its queries
+//                inside the scoring launch (advanced by the step's selection
+//                launch), then per (sequence, KV head, block of 16 projection
+//                rows) the epoch that last projected it; zero after
+//                allocation, which no step's epoch is
+//   [C + U + N + T, ..)  scratch: the projected queries during routing, then the
 //                attention splits' partial records (stream order keeps the
 //                two uses apart)
 size_t counter_bytes(const basiskv_dims &d) {  // one per (sequence, query subgroup)
@@ -114,8 +120,21 @@ size_t newtok_bytes(const basiskv_dims &d) {
   return align_up((size_t)d.batch * d.n_kv_heads * sizeof(float));
 }
 
+// (decode step with the projection inside the scoring launch) the done-tags
+// of the projection's row blocks; sized wherever the scan may take the
+// projection in (bf16 activations, groups of a multiple of 4 heads), so that
+// the workspace does not depend on the page format
+constexpr size_t kEpochBytes = 256;  // the epoch word, alone in its 256 bytes
+size_t qtag_bytes(const basiskv_dims &d) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  return bkv_host::act_bf16(d) && G % 4 == 0
+             ? kEpochBytes + align_up((size_t)d.batch * d.n_kv_heads *
+                                      ((d.r_b + d.r_q + 15) / 16) * sizeof(uint32_t))
+             : 0;
+}
+
 size_t scratch_offset(const basiskv_dims &d) {
-  return counter_bytes(d) + utile_bytes(d) + newtok_bytes(d);
+  return counter_bytes(d) + utile_bytes(d) + newtok_bytes(d) + qtag_bytes(d);
 }
 
 int32_t *attend_counters(void *ws) { return static_cast<int32_t *>(ws); }
@@ -126,6 +145,13 @@ uint16_t *u_tiles(void *ws, const basiskv_dims &d) {
 }
 float *newtok_scores(void *ws, const basiskv_dims &d) {
   return reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes(d) + utile_bytes(d));
+}
+uint32_t *epoch_word(void *ws, const basiskv_dims &d) {
+  return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + counter_bytes(d) + utile_bytes(d) +
+                                      newtok_bytes(d));
+}
+uint32_t *qtag_area(void *ws, const basiskv_dims &d) {
+  return epoch_word(ws, d) + kEpochBytes / sizeof(uint32_t);
 }
 float *scratch_area(void *ws, const basiskv_dims &d) {
   return reinterpret_cast<float *>(static_cast<char *>(ws) + scratch_offset(d));
@@ -354,22 +380,31 @@ int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_n
   const int n_counters = (int)(counter_bytes(*d) / sizeof(int32_t));
   const bool rope = has_rope(c);
   const bool beside = !rope && compress_beside_scan(*d);
+  // with a long scan on the matrix-core logits, the query projection (a1)
+  // runs inside the scoring launch too (it also clears the attention's merge
+  // counters there)
+  const bool project_beside = beside && bkv_host::score_projects(*d);
   // (a1) in one launch, which also clears the attention's merge counters;
   // with a long scan the new tokens' compression (a0) runs inside the scoring
   // launch (a2), beside the scan, and the selection (a3) folds their scores
   // in; otherwise (and with rotary positions) it shares the first launch.
   // Then (a4), (a5).
-  if (bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr,
+  if (!project_beside &&
+      bkv_host::launch_step_prologue(*d, q, k_new, v_new, start_pos, A, P, Q, E, *c, scr,
                                      attend_counters(ws), n_counters, s, !beside) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
-  bkv_host::StepTokens tokens{k_new, v_new, A, P, E, start_pos, newtok_scores(ws, *d)};
+  bkv_host::StepTokens tokens{k_new,     v_new, A, P, E, start_pos, newtok_scores(ws, *d), q, Q,
+                              project_beside ? qtag_area(ws, *d) : nullptr,
+                              project_beside ? epoch_word(ws, *d) : nullptr,
+                              attend_counters(ws), n_counters};
   hipError_t e = rope ? bkv_host::launch_score_rope(*d, q, P, Q, *c, page_scores, s, &unsupported)
                       : bkv_host::launch_score(*d, scr, *c, page_scores, s, &unsupported,
                                                beside ? &tokens : nullptr);
   if (e != hipSuccess || unsupported) return BASISKV_ERR_LAUNCH;
   if (bkv_host::launch_select(*d, page_scores, c->seq_lens, top_k, sel, s,
                               beside ? start_pos : nullptr,
-                              beside ? tokens.new_scores : nullptr) != hipSuccess)
+                              beside ? tokens.new_scores : nullptr,
+                              project_beside ? epoch_word(ws, *d) : nullptr) != hipSuccess)
     return BASISKV_ERR_LAUNCH;
   uint16_t *ut = u_tiles(ws, *d);  // attention also leaves u as the reconstruction's operand
   e = bkv_host::launch_attend(*d, q, *c, sel, top_k, scale, u, scr, attend_counters(ws), ut, s,

@@ -242,6 +242,12 @@ __device__ __forceinline__ void store_coherent(float *p, float v) {
 __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent_u32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
@@ -360,7 +366,16 @@ struct StepTokens {
   const void *k_new, *v_new, *A, *P, *E;
   const int32_t *start_pos;
   float *new_scores;  // [batch * n_kv_heads]
+  // the query projection in the same launch (qtags null: projected before it)
+  const void *q, *Q;
+  uint32_t *qtags;    // [batch][n_kv_heads][row blocks] the step that last completed each
+  uint32_t *epoch;    // the last step's tag (this step's is one more; the selection advances it)
+  int32_t *counters;  // the attention's merge counters, zeroed there
+  int n_counters;
 };
+// Whether the scoring launch can take the query projection in (matrix-core
+// logits: bf16 or E4M3 pages, groups of a multiple of 4 heads).
+bool score_projects(const basiskv_dims &d);
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
                         float *scores, hipStream_t s, bool *unsupported,
                         const StepTokens *step = nullptr);
@@ -371,7 +386,8 @@ hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P
 bool attend_supported(const basiskv_dims &d, bool rope);
 hipError_t launch_select(const basiskv_dims &d, float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s,
-                         const int32_t *new_pos = nullptr, const float *new_scores = nullptr);
+                         const int32_t *new_pos = nullptr, const float *new_scores = nullptr,
+                         uint32_t *epoch = nullptr);
 int attend_splits(const basiskv_dims &d, int32_t top_k);
 int attend_group_split(const basiskv_dims &d);
 hipError_t launch_attend(const basiskv_dims &d, const void *q, const basiskv_cache &c,

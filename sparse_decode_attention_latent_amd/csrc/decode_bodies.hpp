@@ -231,13 +231,17 @@ __device__ __forceinline__ void append_body(
 // head g for sequence b; its factor loads are in flight while the group's
 // queries are staged in LDS.  Each lane forms its 8-dim partial dot for every
 // head of the group, the row's 16 lanes sum them (DPP), and lane h of the row
-// stores head h's output.
+// stores head h's output.  TAG (the projection inside the scoring launch):
+// the outputs are written through to the agent's coherence point, and once
+// every one of them has been acknowledged thread 0 writes `tag` to *done the
+// same way, so a reader on any XCD that sees the tag (reading as
+// load_coherent does) reads this block's values, not older ones.
 // ---------------------------------------------------------------------------
-template <typename T, int NT>
+template <typename T, int NT, bool TAG = false>
 __device__ __forceinline__ void project_body(const T *__restrict__ q, const T *__restrict__ P,
                                              const T *__restrict__ Q, float *__restrict__ q_proj,
                                              int n_q, int n_kv, int rb, int rq, int xblk, int g,
-                                             int b) {
+                                             int b, uint32_t *done = nullptr, uint32_t tag = 0) {
   constexpr int RPW = NT / 16;                    // rows per workgroup
   constexpr int NL = 8 * (int)sizeof(T) / 16;     // 16-byte loads per lane: 1 (bf16), 2 (float32)
   constexpr int CE = Elem<T>::CE;
@@ -294,7 +298,18 @@ __device__ __forceinline__ void project_body(const T *__restrict__ q, const T *_
     part += dpp_move<0x140>(part);  // the other half of the row
     if (c == h) mine = part;
   }
-  if (active && c < G) q_proj[((int64_t)b * n_q + g * G + c) * w + j] = mine;
+  if (active && c < G) {
+    const int64_t o = ((int64_t)b * n_q + g * G + c) * w + j;
+    if constexpr (TAG)
+      store_coherent(q_proj + o, mine);
+    else
+      q_proj[o] = mine;
+  }
+  if constexpr (TAG) {
+    wait_stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent_u32(done, tag);
+  }
 }
 
 }  // namespace bkv

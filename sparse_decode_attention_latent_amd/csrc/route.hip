@@ -31,8 +31,13 @@ template <int KPT, int NWV>
 __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
     float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     int32_t *__restrict__ sel, int n_kv, int max_pages, int page_size, int cap, int k,
-    int recent, const int32_t *__restrict__ new_pos, const float *__restrict__ new_scores) {
+    int recent, const int32_t *__restrict__ new_pos, const float *__restrict__ new_scores,
+    uint32_t *__restrict__ epoch) {
   const int g = blockIdx.x, b = blockIdx.y;
+  // (decode step with the projection inside the scoring launch) the scan is
+  // over: the next step's scoring launch takes the next epoch
+  if (epoch && g == 0 && b == 0 && threadIdx.x == 0)
+    store_coherent_u32(epoch, load_coherent_u32(epoch) + 1);
   // the whole row is requested before the sequence length arrives
   float *row = scores + ((int64_t)b * n_kv + g) * max_pages;
   const int base = (threadIdx.x >> 6) * 64 * KPT + (threadIdx.x & 63);
@@ -92,6 +97,24 @@ __global__ __launch_bounds__(64 * NWV) void topk_select_kernel(
 // maximum of the two.  Max is exact, so the page scores are those of scoring
 // after the compression, while the compression's chain of round trips runs
 // beside the scan instead of before it.
+//
+// The query projection inside the scoring launch as well (n_proj > 0, the
+// matrix-core logits only): the grid's first proj_padded workgroups each
+// project 16 rows of [P_g; Q_g] for one (sequence, KV head) with the
+// arithmetic of the separate projection (the same values, bit for bit, at the
+// same place) and then mark the row block done with the step's epoch
+// (project_body's TAG form).  Every other workgroup requests the done-tags of
+// the row blocks its queries come from where it would have requested the
+// projected queries; once its page loads are issued it checks them, waits
+// (sleeps, re-reading the stale tags) until all carry this step's epoch, and
+// only then reads the values.  The projection workgroups come first in the
+// grid and wait for nothing, so they run and finish whatever the others do;
+// the wait is bounded all the same (kTagWaitRounds).  The first of them also
+// zeroes the attention's merge counters, as the projection's own launch does.
+// The step's epoch is one more than the device word epoch, which the step's
+// selection launch then advances: no two launches of a stream share an
+// epoch, graph replays included, and a zero-filled workspace starts both at
+// zero.
 struct DeferArgs {
   const void *k_new, *v_new, *A, *P, *E;  // new tokens and factors (activation type)
   const int32_t *start_pos;               // the new token's position per sequence
@@ -99,7 +122,15 @@ struct DeferArgs {
   float *new_scores;                      // [batch * n_kv] the new token's score (-inf: none)
   AppendArgs ap;
   int n_append, app_padded;  // batch * n_kv workgroups, padded to a multiple of the XCD count
+  const void *q, *Q;         // raw queries and residual factor (activation type)
+  uint32_t *qtags;           // done-tags per (sequence, KV head, row block) (null: projected before)
+  float *q_proj_out;         // where the projection writes: the launch's q_proj
+  const uint32_t *epoch;     // the last step's tag: this launch's is one more
+  int n_proj, proj_padded, proj_x;  // projection workgroups (padded as above); row blocks per KV head
+  int32_t *counters;         // the attention's merge counters
+  int n_counters;
 };
+constexpr int kTagWaitRounds = 1 << 16;  // rounds of a 1 us sleep and a read (over 0.1 s)
 
 struct ScoreArgs {
   int n_q, n_kv, max_pages, num_phys, page_size, log2_page, cap;
@@ -119,7 +150,7 @@ typedef float route_f4 __attribute__((ext_vector_type(4)));
 // projected queries enter as two bf16 terms, hi = bf16(q) and lo = bf16(q -
 // hi) (about 16 significant bits); every product is exact and the sums are
 // float32.  The query operands are staged in LDS once per workgroup.
-template <typename T, int G, int NZ, int NR, bool STREAM, bool MF>
+template <typename T, int G, int NZ, int NR, bool STREAM, bool MF, bool PROJ = false>
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const float *__restrict__ q_proj, const T *zpool, const T *rpool,  // (written by compression)
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
@@ -132,9 +163,25 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   // [quad][step][head in quad]: {hi 4 x bf16, lo 4 x bf16}
   __shared__ __align__(16) uint4 qf[MF ? QG * NST * 4 : 1];
   using TA = typename std::conditional<sizeof(T) == 1, uint16_t, T>::type;  // activations
-  // compression workgroups first (app_padded of them, a multiple of the XCD
-  // count, so the scan's workgroups keep their XCD placement)
+  // projection workgroups first, then compression workgroups (proj_padded and
+  // app_padded of them, multiples of the XCD count, so the scan's workgroups
+  // keep their XCD placement)
   int bid = blockIdx.x;
+  static_assert(!PROJ || MF, "the projection inside the launch goes with the matrix-core logits");
+  if (PROJ && bid < a.df.proj_padded) {  // (workgroup-uniform)
+    if (bid < a.df.n_proj) {
+      if (bid == 0)
+        for (int i = threadIdx.x; i < a.df.n_counters; i += blockDim.x) a.df.counters[i] = 0;
+      const int xblk = bid % a.df.proj_x, rest = bid / a.df.proj_x;
+      const uint32_t tag = load_coherent_u32(a.df.epoch) + 1;
+      project_body<TA, 256, true>(static_cast<const TA *>(a.df.q), static_cast<const TA *>(a.df.P),
+                                  static_cast<const TA *>(a.df.Q), a.df.q_proj_out,
+                                  a.n_q, a.n_kv, W - NR * CE, NR * CE, xblk, rest % a.n_kv,
+                                  rest / a.n_kv, a.df.qtags + bid, tag);
+    }
+    return;
+  }
+  if constexpr (PROJ) bid -= a.df.proj_padded;
   const bool compress = bid < a.df.app_padded;  // (workgroup-uniform)
   if (compress && bid >= a.df.n_append) return;
   int bg, chunk = 0;
@@ -199,13 +246,25 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
   constexpr int QN = MF ? QG * NST * 4 : 1;  // staged query entries
   constexpr int QI = (QN + 255) / 256;       // per thread (256 threads)
   float4 qv_in[QI];
+  uint32_t qt[PROJ ? QI : 1];  // done-tags of the entries' row blocks (projection in this launch)
+  constexpr bool tagged = PROJ;
+  const uint32_t *tags = tagged ? a.df.qtags + (int64_t)bg * a.df.proj_x : nullptr;
+  auto q_index = [&](int i) {  // staged entry i: 4 dims of one head's projected query
+    const int hq = i & 3, st = (i >> 2) % NST, qd = i / (NST * 4);
+    return (qd * 4 + hq) * W + st * 4;
+  };
+  auto q_block = [&](int i) { return ((i >> 2) % NST) / 4; };  // its row block (16 rows)
+  uint32_t expect = 0;  // this launch's epoch
+  if constexpr (tagged) expect = load_coherent_u32(a.df.epoch) + 1;
   if constexpr (MF) {
 #pragma unroll
     for (int u = 0; u < QI; ++u) {
       const int i = u * 256 + threadIdx.x;
-      const int hq = i & 3, st = (i >> 2) % NST, qd = i / (NST * 4);
-      qv_in[u] = i < QN ? *reinterpret_cast<const float4 *>(qp + (qd * 4 + hq) * W + st * 4)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (tagged)
+        qt[u] = i < QN ? load_coherent_u32(tags + q_block(i)) : 0u;
+      else
+        qv_in[u] = i < QN ? *reinterpret_cast<const float4 *>(qp + q_index(i))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   const int tok = p * a.page_size + slot_t;
@@ -230,6 +289,32 @@ __global__ __launch_bounds__(256) void route_scan_kernel(
 #pragma unroll
       for (int c = 0; c < NR; ++c)
         cr[c] = load_page_chunk<STREAM>(rpool, roff + (int64_t)c * a.page_size * 16);
+    }
+    if constexpr (tagged) {  // this step's projected queries: their row blocks done, then the values
+      auto stale = [&]() {
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < QI; ++u) any |= u * 256 + (int)threadIdx.x < QN && qt[u] != expect;
+        return any;
+      };
+      if (__syncthreads_or(stale())) {
+        for (int round = 0; round < kTagWaitRounds; ++round) {
+          __builtin_amdgcn_s_sleep(40);
+#pragma unroll
+          for (int u = 0; u < QI; ++u) {
+            const int i = u * 256 + threadIdx.x;
+            if (i < QN && qt[u] != expect) qt[u] = load_coherent_u32(tags + q_block(i));
+          }
+          if (!__syncthreads_or(stale())) break;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QI; ++u) {
+        const int i = u * 256 + threadIdx.x;
+        const float *src = qp + (i < QN ? q_index(i) : 0);
+        qv_in[u] = make_float4(load_coherent(src), load_coherent(src + 1), load_coherent(src + 2),
+                               load_coherent(src + 3));
+      }
     }
     // the queries (arrived with the block-table entry) into LDS while the
     // pages are in flight
@@ -635,6 +720,7 @@ constexpr int kStreamMinChunks = BKV_STREAM_MIN_CHUNKS;  // chunk loads per lane
 struct ScoreVariant {
   int dtype, G, rb, rq;
   const void *fn, *fn_nt;  // ordinary loads; non-temporal loads (null: not built)
+  const void *fn_proj;     // non-temporal, matrix-core logits, projection inside (null: not built)
 };
 
 #ifndef BKV_ROUTE_MFMA_MIN_G
@@ -646,6 +732,16 @@ constexpr bool route_mfma() {
   return sizeof(T) <= 2 && G % 4 == 0 && G >= BKV_ROUTE_MFMA_MIN_G;
 }
 
+// the decode step's scan with the query projection inside: built where the
+// non-temporal, matrix-core scan is
+template <typename T, int G, int NZ, int NR>
+const void *score_proj_kernel() {
+  if constexpr (route_mfma<T, G>() && NZ + NR >= kStreamMinChunks)
+    return reinterpret_cast<const void *>(&route_scan_kernel<T, G, NZ, NR, true, true, true>);
+  else
+    return nullptr;
+}
+
 #define BKV_SCORE(T, DT, G, RB, RQ)                                                                  \
   {DT, G, RB, RQ,                                                                                     \
    reinterpret_cast<const void *>(&route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE,   \
@@ -655,7 +751,8 @@ constexpr bool route_mfma() {
              &route_scan_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE,                         \
                                 (((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks),                    \
                                 route_mfma<T, G>()>)                                                  \
-       : nullptr}
+       : nullptr,                                                                                     \
+   score_proj_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE>()}
 
 #define BKV_SCORE_G(T, DT, RB, RQ) \
   BKV_SCORE(T, DT, 1, RB, RQ), BKV_SCORE(T, DT, 2, RB, RQ), BKV_SCORE(T, DT, 4, RB, RQ), \
@@ -727,6 +824,14 @@ static const void *find_score(const basiskv_dims &d) {
 
 bool score_supported(const basiskv_dims &d) { return find_score(d) != nullptr; }
 
+static const void *find_score_proj(const basiskv_dims &d) {
+  const int G = d.n_q_heads / d.n_kv_heads;
+  for (const auto &v : kScoreVariants)
+    if (v.dtype == d.dtype && v.G == G && v.rb == d.r_b && v.rq == d.r_q)
+      return d.page_size >= 8 ? v.fn_proj : nullptr;
+  return nullptr;
+}
+
 static const void *find_score_rope(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   for (const auto &v : kScoreRopeVariants)
@@ -782,13 +887,26 @@ hipError_t launch_score_rope(const basiskv_dims &d, const void *q, const void *P
 
 hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basiskv_cache &c,
                         float *scores, hipStream_t s, bool *unsupported, const StepTokens *step) {
-  const void *fn = find_score(d);
+  const void *fn = step && step->qtags ? find_score_proj(d) : find_score(d);
   if (!fn) {
     *unsupported = true;
     return hipSuccess;
   }
   *unsupported = false;
   ScoreArgs a{};
+  if (step && step->qtags) {  // the query projection in this launch too
+    a.df.q = step->q;
+    a.df.Q = step->Q;
+    a.df.P = step->P;
+    a.df.qtags = step->qtags;
+    a.df.q_proj_out = const_cast<float *>(q_proj);  // (the caller's scratch)
+    a.df.epoch = step->epoch;
+    a.df.proj_x = (d.r_b + d.r_q + 15) / 16;  // 16 rows per 256-thread workgroup
+    a.df.n_proj = a.df.proj_x * d.n_kv_heads * d.batch;
+    a.df.proj_padded = (a.df.n_proj + kXcds - 1) / kXcds * kXcds;
+    a.df.counters = step->counters;
+    a.df.n_counters = step->n_counters;
+  }
   if (step) {  // the step's new tokens compressed and scored in this launch
     a.df.k_new = step->k_new;
     a.df.v_new = step->v_new;
@@ -821,8 +939,11 @@ hipError_t launch_score(const basiskv_dims &d, const float *q_proj, const basisk
   void *rpool = residual_pool(d, c);
   void *args[] = {(void *)&q_proj, (void *)&c.z_pages, (void *)&rpool,
                   (void *)&c.block_table, (void *)&c.seq_lens, (void *)&scores, (void *)&a};
-  return hipLaunchKernel(fn, dim3(a.df.app_padded + a.padded), dim3(256), args, 0, s);
+  return hipLaunchKernel(fn, dim3(a.df.proj_padded + a.df.app_padded + a.padded), dim3(256), args,
+                         0, s);
 }
+
+bool score_projects(const basiskv_dims &d) { return find_score_proj(d) != nullptr; }
 
 #ifndef BKV_SELECT_SMALL_WAVES
 #define BKV_SELECT_SMALL_WAVES 4
@@ -831,25 +952,25 @@ constexpr int kSelectSmallWaves = BKV_SELECT_SMALL_WAVES;  // wavefronts per row
 
 hipError_t launch_select(const basiskv_dims &d, float *scores, const int32_t *seq_lens,
                          int32_t top_k, int32_t *sel, hipStream_t s, const int32_t *new_pos,
-                         const float *new_scores) {
+                         const float *new_scores, uint32_t *epoch) {
   const int mp = d.max_pages_per_seq, cap = d.max_pages_per_seq * d.page_size;
   const dim3 grid(d.n_kv_heads, d.batch);
   if (mp <= 1024)
     hipLaunchKernelGGL((topk_select_kernel<16 / kSelectSmallWaves, kSelectSmallWaves>), grid,
                        dim3(64 * kSelectSmallWaves), 0, s, scores, seq_lens, sel, d.n_kv_heads, mp,
-                       d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
+                       d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores, epoch);
   else if (mp <= 4096)
     hipLaunchKernelGGL((topk_select_kernel<16, 4>), grid, dim3(256), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores, epoch);
   else if (mp <= 8192)
     hipLaunchKernelGGL((topk_select_kernel<8, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores, epoch);
   else if (mp <= 16384)
     hipLaunchKernelGGL((topk_select_kernel<16, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores, epoch);
   else
     hipLaunchKernelGGL((topk_select_kernel<32, 16>), grid, dim3(1024), 0, s, scores, seq_lens, sel,
-                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores);
+                       d.n_kv_heads, mp, d.page_size, cap, top_k, d.recent_tokens, new_pos, new_scores, epoch);
   return hipGetLastError();
 }
 

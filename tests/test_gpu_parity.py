@@ -621,6 +621,73 @@ def test_repeated_steps_reuse_the_workspace_bit_exact():
     compare_step(wl, inp, prob, outs[-1], range(3))
 
 
+def _new_queries(prob, seed):
+    """Seeded N(0, 1) queries of the problem's shape, written into prob.q."""
+    gen = torch.Generator().manual_seed(seed)
+    prob.q.copy_(torch.randn(tuple(prob.q.shape), generator=gen).to(prob.q.dtype))
+
+
+def _separate_calls(prob):
+    """The same step as the library's separate calls, after the one-call step
+    (its new token appended again at the same position), as host arrays."""
+    for t in (prob.page_scores, prob.u):
+        t.fill_(float("nan"))
+    prob.sel.fill_(-7)
+    prob.y.fill_(0)
+    prob.step(append=True)
+    return prob.outputs()
+
+
+@pytest.mark.parametrize("name", ["llama8b-ctx32k", "qwen32b-ctx32k"])
+def test_decode_steps_with_new_queries_every_call(name):
+    """One-call steps where the scoring launch projects the queries itself
+    (long scans): three calls in a row, each with new queries, each
+    bit-identical to the separate calls on the same queries -- a call that
+    scored with an earlier call's projected queries would differ."""
+    wl = workload(name)
+    _say(f"decode_step, new queries per call, {name}: batch={wl.batch} ctx={wl.ctx}")
+    inp = synth.decode_inputs(wl)
+    prob = DecodeProblem(wl, inp)
+    for i in range(3):
+        _new_queries(prob, 100 + i)
+        prob.decode_step()
+        got = prob.outputs()
+        base = _separate_calls(prob)
+        for key in ("scores", "sel", "u", "y"):
+            np.testing.assert_array_equal(got[key], base[key], err_msg=f"call {i}: {key}")
+
+
+def test_decode_step_graph_replays_with_new_queries():
+    """The one-call step captured once in a HIP graph and replayed with new
+    queries each time (eager work and synchronisations between replays): every
+    replay bit-identical to the separate calls on its queries.  The step's
+    epoch lives in device memory, so replays never take an earlier replay's
+    projected queries for their own."""
+    wl = workload("llama8b-ctx32k")
+    _say(f"decode_step graph replays: batch={wl.batch} ctx={wl.ctx}")
+    inp = synth.decode_inputs(wl)
+    prob = DecodeProblem(wl, inp)
+    prob.decode_step()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            prob.decode_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(3):
+        _new_queries(prob, 200 + i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = prob.outputs()
+        base = _separate_calls(prob)
+        for key in ("scores", "sel", "u", "y"):
+            np.testing.assert_array_equal(got[key], base[key], err_msg=f"replay {i}: {key}")
+
+
 @pytest.mark.parametrize("page_size,ctx", [(8, 100000), (4, 80000), (4, 131072)])
 def test_long_rows_selection(page_size, ctx):
     """Rows of 12500, 20000 and 32768 pages (the largest max_pages_per_seq the
