@@ -657,13 +657,14 @@ def test_decode_steps_with_new_queries_every_call(name):
             np.testing.assert_array_equal(got[key], base[key], err_msg=f"call {i}: {key}")
 
 
-def test_decode_step_graph_replays_with_new_queries():
+@pytest.mark.parametrize("name", ["llama8b-ctx32k", "qwen32b-ctx32k"])
+def test_decode_step_graph_replays_with_new_queries(name):
     """The one-call step captured once in a HIP graph and replayed with new
     queries each time (eager work and synchronisations between replays): every
     replay bit-identical to the separate calls on its queries.  The step's
     epoch lives in device memory, so replays never take an earlier replay's
-    projected queries for their own."""
-    wl = workload("llama8b-ctx32k")
+    projected queries for their own (4- and 8-head groups)."""
+    wl = workload(name)
     _say(f"decode_step graph replays: batch={wl.batch} ctx={wl.ctx}")
     inp = synth.decode_inputs(wl)
     prob = DecodeProblem(wl, inp)
