@@ -638,7 +638,7 @@ def _separate_calls(prob):
     return prob.outputs()
 
 
-@pytest.mark.parametrize("name", ["llama8b-ctx32k", "qwen32b-ctx32k"])
+@pytest.mark.parametrize("name", ["llama8b-ctx32k", "qwen32b-ctx32k", "llama8b-ctx32k-fp8"])
 def test_decode_steps_with_new_queries_every_call(name):
     """One-call steps where the scoring launch projects the queries itself
     (long scans): three calls in a row, each with new queries, each
