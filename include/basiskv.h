@@ -156,10 +156,14 @@ const char *basiskv_status_string(int32_t status);
  * basiskv_decode_step need for these dims and top_k; one buffer of this size
  * serves all three.  0 if dims are invalid.
  * The workspace is device memory owned by the caller.  It must be zero-filled
- * once after allocation: it holds small integer counters with which the
- * workgroups of the attention launch elect the one that merges a (sequence,
- * KV head) row's splits, and every call leaves them at zero again.  Calls
- * that share one workspace must not run concurrently. */
+ * after allocation, and again before it serves calls of other dims: it holds
+ * small integer counters with which the workgroups of the attention launch
+ * elect the one that merges a (sequence, KV head) row's splits (every call
+ * leaves them at zero again), and for basiskv_decode_step the epoch of its
+ * last step and the marks with which that step's projection workgroups
+ * told the scanning ones their queries were ready (both carried from call to
+ * call; a step recognises only marks of its own epoch).  Calls that share one
+ * workspace must not run concurrently. */
 size_t basiskv_workspace_bytes(const basiskv_dims *dims, int32_t top_k);
 
 /* (a0) Compress new tokens into the cache -- BasisKV abstract (Value kept
@@ -341,9 +345,11 @@ size_t basiskv_static_scratch_bytes(void);
  * and ERR_LAUNCH if the device address cannot be obtained; all other
  * arguments and checks as for basiskv_decode_step.  Every call on one GPU
  * shares that GPU's array and finds what the previous call left in it (the
- * step zeroes what must start at zero itself): calls that overlap on one GPU
- * -- on different streams, or from different host threads -- race and must
- * not be made. */
+ * step zeroes what must start at zero itself; when its dims differ from the
+ * previous call's on that GPU it first zeroes, with a small fill kernel on
+ * `stream`, the epoch and marks that steps carry from call to call): calls
+ * that overlap on one GPU -- on different streams, or from different host
+ * threads -- race and must not be made. */
 int32_t basiskv_decode_step_static(const basiskv_dims *dims, const void *q, const void *k_new,
                                    const void *v_new, const int32_t *start_pos, const void *A,
                                    const void *P, const void *Q, const void *E, const void *M,

@@ -174,7 +174,22 @@ std::mutex g_scratch_mutex;
 void *g_scratch_ptr[kMaxDevices];  // per device, looked up on first use
 
 // Device address of `scratch` on the current device (looked up once per device).
-int32_t static_scratch(void **out) {
+basiskv_dims g_scratch_dims[kMaxDevices];  // per device, the dims of the last step on it
+bool g_scratch_used[kMaxDevices];
+
+// Zeroes n 32-bit words (a fill kernel, not a memset: the step may be
+// captured in a graph).
+__global__ void zero_words_kernel(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// The scratch of the current device.  When the step's dims differ from the
+// last step run on it, the words that a step carries over to the next (the
+// projection's epoch and done-tags, at a place that depends on the dims) are
+// zeroed first on the step's stream, so that nothing an earlier step of other
+// dims left there can pass for this step's.
+int32_t static_scratch(void **out, const basiskv_dims &d, hipStream_t s) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BASISKV_ERR_LAUNCH;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
@@ -184,6 +199,15 @@ int32_t static_scratch(void **out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  if (!g_scratch_used[dev] || memcmp(&g_scratch_dims[dev], &d, sizeof d) != 0) {
+    const size_t words = qtag_bytes(d) / sizeof(uint32_t);
+    if (words > 0) {
+      hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, s, epoch_word(*out, d), words);
+      if (hipGetLastError() != hipSuccess) return BASISKV_ERR_LAUNCH;
+    }
+    g_scratch_dims[dev] = d;
+    g_scratch_used[dev] = true;
+  }
   return BASISKV_OK;
 }
 
@@ -445,7 +469,7 @@ int32_t basiskv_decode_step_static(const basiskv_dims *d, const void *q, const v
                                  page_scores, sel, u, y, stand_in, kStaticScratchBytes);
   if (st) return st;
   void *ws = nullptr;
-  if ((st = static_scratch(&ws))) return st;
+  if ((st = static_scratch(&ws, *d, as_stream(stream)))) return st;
   return launch_decode_step(d, q, k_new, v_new, start_pos, A, P, Q, E, M, c, top_k, scale,
                             page_scores, sel, u, y, ws, as_stream(stream));
 }

@@ -24,6 +24,15 @@ CASES_ROPE = (
     ("llama8b-ctx32k-b16r16-page4-fp8", 2, 4096, [4096, 999], None),
 )
 
+# long scans with the projection inside the scoring launch, one after the
+# other with other dims (the epoch and marks sit elsewhere in the scratch),
+# then the first dims again
+CASES_PROJ = (
+    ("llama8b-ctx32k", 4, 32768, [32768, 20000, 4097, 31000], 128),
+    ("llama8b-ctx32k", 8, 16384, [16384, 9000, 100, 16384, 5000, 33, 1, 12000], 128),
+    ("llama8b-ctx32k", 4, 32768, [32768, 20000, 4097, 31000], 128),
+)
+
 
 def _static_step(prob):
     api.decode_step_static(prob.dims, prob.q, prob.k_new, prob.v_new, prob.start_pos,
@@ -39,7 +48,8 @@ def _clear(prob):
     prob.y.fill_(0)
 
 
-@pytest.mark.parametrize("cases", [CASES, CASES_ROPE], ids=["separate-pools", "rope-routing-first"])
+@pytest.mark.parametrize("cases", [CASES, CASES_ROPE, CASES_PROJ],
+                         ids=["separate-pools", "rope-routing-first", "projection-inside"])
 def test_static_step_matches_the_workspace_step_twice(cases):
     for name, batch, ctx, seq_lens, top_k in cases:
         print(f"static step {name}: batch={batch} ctx={ctx} top_k={top_k}", flush=True)
