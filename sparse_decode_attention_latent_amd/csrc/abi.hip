@@ -385,12 +385,20 @@ int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_ne
 // in the projection's launch: with routing reads of 200 MB and more
 // (llama8b- and qwen32b-shaped layers at 32K context, bf16 or E4M3 pages)
 // 0.5-2 us shorter; with 150 MB or less (4K context, the 4-token-page
-// routers) 1-4 us longer, the compression outlasting the scan.
+// routers) 1-4 us longer while the projection kept a launch of its own, the
+// compression outlasting the scan.
 constexpr double kBesideScanMinBytes = 160.0 * (1 << 20);
 bool compress_beside_scan(const basiskv_dims &d) {
   const double bytes = (double)d.batch * d.n_kv_heads * d.max_pages_per_seq * d.page_size *
                        (d.r_b + d.r_q) * (bkv_host::cache_fp8(d) ? 1 : bkv_host::act_bf16(d) ? 2 : 4);
-  return bytes >= kBesideScanMinBytes;
+  if (bytes >= kBesideScanMinBytes) return true;
+  // a shorter scan takes both in where the query projection can come too (the
+  // step then has no launch before the scan) over bf16 pages at least 32
+  // routing dims wide.  Measured against the separate launch: 4K-context
+  // llama8b-shaped layer 57.8 -> 55.6 us, the adopted router 68.8 -> 67.3 us,
+  // R32 69.5 -> 67.2 us; narrower scans (B16: +0.8 us) and E4M3 pages (no
+  // change) keep the launch.
+  return bkv_host::score_projects(d) && !bkv_host::cache_fp8(d) && d.r_b + d.r_q >= 32;
 }
 
 // The launches of a decode step, after check_decode_step.

@@ -150,8 +150,19 @@ typedef float route_f4 __attribute__((ext_vector_type(4)));
 // projected queries enter as two bf16 terms, hi = bf16(q) and lo = bf16(q -
 // hi) (about 16 significant bits); every product is exact and the sums are
 // float32.  The query operands are staged in LDS once per workgroup.
+// Wavefronts per SIMD asked of the compiler: the projection-inside form of a
+// narrow 4-head scan (up to 6 chunk loads per lane) carries more scalar state
+// than fits eight wavefronts' share of the scalar registers, and is held to the
+// eight its plain form runs (its few extra scalars then live in vector-register
+// lanes); no request otherwise.
+template <int G, int NZ, int NR, bool PROJ>
+constexpr int route_waves_per_eu() {
+  return PROJ && G == 4 && NZ + NR <= 6 ? 8 : 1;
+}
 template <typename T, int G, int NZ, int NR, bool STREAM, bool MF, bool PROJ = false>
-__global__ __launch_bounds__(256) void route_scan_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(route_waves_per_eu<G, NZ, NR, PROJ>())))
+void route_scan_kernel(
     const float *__restrict__ q_proj, const T *zpool, const T *rpool,  // (written by compression)
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     float *__restrict__ scores, ScoreArgs a) {
@@ -720,7 +731,9 @@ constexpr int kStreamMinChunks = BKV_STREAM_MIN_CHUNKS;  // chunk loads per lane
 struct ScoreVariant {
   int dtype, G, rb, rq;
   const void *fn, *fn_nt;  // ordinary loads; non-temporal loads (null: not built)
-  const void *fn_proj;     // non-temporal, matrix-core logits, projection inside (null: not built)
+  // matrix-core logits with the projection inside (null: not built): ordinary
+  // and non-temporal loads
+  const void *fn_proj, *fn_nt_proj;
 };
 
 #ifndef BKV_ROUTE_MFMA_MIN_G
@@ -733,11 +746,11 @@ constexpr bool route_mfma() {
 }
 
 // the decode step's scan with the query projection inside: built where the
-// non-temporal, matrix-core scan is
-template <typename T, int G, int NZ, int NR>
+// scan takes the matrix-core logits, with the loads the plain scan uses
+template <typename T, int G, int NZ, int NR, bool STREAM>
 const void *score_proj_kernel() {
-  if constexpr (route_mfma<T, G>() && NZ + NR >= kStreamMinChunks)
-    return reinterpret_cast<const void *>(&route_scan_kernel<T, G, NZ, NR, true, true, true>);
+  if constexpr (route_mfma<T, G>() && (!STREAM || NZ + NR >= kStreamMinChunks))
+    return reinterpret_cast<const void *>(&route_scan_kernel<T, G, NZ, NR, STREAM, true, true>);
   else
     return nullptr;
 }
@@ -752,7 +765,8 @@ const void *score_proj_kernel() {
                                 (((RB) + (RQ)) / Elem<T>::CE >= kStreamMinChunks),                    \
                                 route_mfma<T, G>()>)                                                  \
        : nullptr,                                                                                     \
-   score_proj_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE>()}
+   score_proj_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE, false>(),                         \
+   score_proj_kernel<T, G, (RB) / Elem<T>::CE, (RQ) / Elem<T>::CE, true>()}
 
 #define BKV_SCORE_G(T, DT, RB, RQ) \
   BKV_SCORE(T, DT, 1, RB, RQ), BKV_SCORE(T, DT, 2, RB, RQ), BKV_SCORE(T, DT, 4, RB, RQ), \
@@ -828,7 +842,7 @@ static const void *find_score_proj(const basiskv_dims &d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   for (const auto &v : kScoreVariants)
     if (v.dtype == d.dtype && v.G == G && v.rb == d.r_b && v.rq == d.r_q)
-      return d.page_size >= 8 ? v.fn_proj : nullptr;
+      return v.fn_nt && d.page_size >= 8 ? v.fn_nt_proj : v.fn_proj;  // as find_score
   return nullptr;
 }
 
