@@ -306,10 +306,10 @@ int32_t basiskv_pack_output_matrix(const basiskv_dims *dims, const void *M_plain
  * selection first folds each new token's score into its page's (page_scores
  * then holds the full scores); otherwise, and with rotary positions, the
  * compression shares the projection's launch.  Where the scoring launch can
- * take the projection in too (bf16 or E4M3 pages, groups of a multiple of 4
- * query heads), it does so with such a long scan, and also with a shorter one
- * over bf16 pages at least 32 routing dims wide, which then takes the
- * compression in as well (four launches): the projection's
+ * take the projection in too (bf16 pages, groups of a multiple of 4 query
+ * heads), it does so with such a long scan, and also with a shorter one
+ * of 64 MiB or more over bf16 pages at least 32 routing dims wide, which then
+ * takes the compression in as well (four launches): the projection's
  * workgroups come first in the grid, mark each block of projected rows done
  * with the step's epoch, and the scanning workgroups wait for those marks
  * before reading the projected queries.  The epoch is a word in the

@@ -388,17 +388,29 @@ int32_t check_decode_step(const basiskv_dims *d, const void *q, const void *k_ne
 // routers) 1-4 us longer while the projection kept a launch of its own, the
 // compression outlasting the scan.
 constexpr double kBesideScanMinBytes = 160.0 * (1 << 20);
+constexpr double kBesideProjMinBytes = 64.0 * (1 << 20);
+
+// Whether the step's scoring launch takes the query projection in (its scan
+// then waits on the projection's marks): bf16 pages on the matrix-core logits.
+// E4M3 pages keep the projection's own launch: with it inside, their scans
+// measured 1-4.6 us longer (context sweep, 32K-96K, batch 8), none shorter.
+bool projects_beside_scan(const basiskv_dims &d) {
+  return bkv_host::score_projects(d) && !bkv_host::cache_fp8(d);
+}
 bool compress_beside_scan(const basiskv_dims &d) {
   const double bytes = (double)d.batch * d.n_kv_heads * d.max_pages_per_seq * d.page_size *
                        (d.r_b + d.r_q) * (bkv_host::cache_fp8(d) ? 1 : bkv_host::act_bf16(d) ? 2 : 4);
   if (bytes >= kBesideScanMinBytes) return true;
-  // a shorter scan takes both in where the query projection can come too (the
-  // step then has no launch before the scan) over bf16 pages at least 32
-  // routing dims wide.  Measured against the separate launch: 4K-context
-  // llama8b-shaped layer 57.8 -> 55.6 us, the adopted router 68.8 -> 67.3 us,
-  // R32 69.5 -> 67.2 us; narrower scans (B16: +0.8 us) and E4M3 pages (no
-  // change) keep the launch.
-  return bkv_host::score_projects(d) && !bkv_host::cache_fp8(d) && d.r_b + d.r_q >= 32;
+  // a shorter scan of 64 MiB or more takes both in where the query projection
+  // can come too (the step then has no launch before the scan) over bf16
+  // pages at least 32 routing dims wide.  Measured against the separate
+  // launch: 4K-context llama8b-shaped layer 58.3 -> 55.5 us, the adopted
+  // router 68.3 -> 66.6 us, R32 69.4 -> 67.0 us, batch-1 llama8b-shaped steps
+  // at 64K and 96K context (101 and 151 MB) 2 us shorter; narrower scans (B16:
+  // +0.8 us), E4M3 pages (no change) and scans under 64 MiB (batch 1 at 24K
+  // and 32K context: 1.5-3 us longer, nearly every scanning workgroup waiting
+  // on the projection) keep the launch.
+  return bytes >= kBesideProjMinBytes && projects_beside_scan(d) && d.r_b + d.r_q >= 32;
 }
 
 // The launches of a decode step, after check_decode_step.
@@ -415,7 +427,7 @@ int32_t launch_decode_step(const basiskv_dims *d, const void *q, const void *k_n
   // with a long scan on the matrix-core logits, the query projection (a1)
   // runs inside the scoring launch too (it also clears the attention's merge
   // counters there)
-  const bool project_beside = beside && bkv_host::score_projects(*d);
+  const bool project_beside = beside && projects_beside_scan(*d);
   // (a1) in one launch, which also clears the attention's merge counters;
   // with a long scan the new tokens' compression (a0) runs inside the scoring
   // launch (a2), beside the scan, and the selection (a3) folds their scores
